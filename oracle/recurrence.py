@@ -1,0 +1,99 @@
+"""Token-by-token fp64 gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Follows Systolic Linear Attention (paperpeel 2611.06828), section 2.1,
+Eq. (2): per token, decay the state by the diagonal gate F_t, take the
+prediction error u_t = v_t - (F_t S_{t-1})^T k_t, write S_t = F_t S_{t-1} +
+beta_t k_t u_t^T, and read out o_t = S_t^T q_t after the update.
+
+Two independent implementations of the same definition:
+
+* :func:`recurrence_c` calls ``liboracle.so`` (``gdr_oracle.c``), threaded over
+  (batch, value head).  Used at large sizes.
+* :func:`recurrence_np` is a numpy loop over tokens, vectorised over
+  (batch, value head).  Used at small sizes and as the C code's twin.
+
+Argument conventions (both functions):
+  q, k       [B, T, H_k, d_k]  float32 (bf16 inputs are decoded to fp32 exactly)
+  v          [B, T, H_v, d_v]
+  beta       [B, T, H_v]  ([B, T, H_k] when beta_per_key_head)
+  log_alpha  [B, T, H_k, G]  natural-log decay, channel i uses group i // (d_k // G)
+  h0         [B, H_v, d_k, d_v] or None (zero state)
+Returns (o [B, T, H_v, d_v], hT [B, H_v, d_k, d_v]) in float64.
+Value head h_v reads key head h_v // (H_v // H_k) (contiguous value-head groups,
+section 2.4.1 of the same paper).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        f = lib.oracle_gdr_recurrence
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int] * 8 + [ctypes.c_void_p] * 8 + [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        _LIB = lib
+    return _LIB
+
+
+def _shapes(q, v, log_alpha):
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    G = log_alpha.shape[3]
+    return B, T, Hk, Hv, dk, dv, G
+
+
+def recurrence_c(q, k, v, beta, log_alpha, h0=None, beta_per_key_head=False,
+                 units=None, nthreads=None):
+    """fp64 token recurrence in C.  ``units`` optionally lists b * H_v + h_v
+    indices to evaluate; the rows of ``o``/``hT`` of other units stay zero."""
+    B, T, Hk, Hv, dk, dv, G = _shapes(q, v, log_alpha)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    q, k, v, beta, log_alpha = f32(q), f32(k), f32(v), f32(beta), f32(log_alpha)
+    h0a = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    o = np.zeros((B, T, Hv, dv), np.float64)
+    hT = np.zeros((B, Hv, dk, dv), np.float64)
+    ua = None if units is None else np.ascontiguousarray(units, dtype=np.int32)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    p = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = _lib().oracle_gdr_recurrence(
+        B, T, Hk, Hv, dk, dv, G, int(bool(beta_per_key_head)),
+        p(q), p(k), p(v), p(beta), p(log_alpha), p(h0a), p(o), p(hT),
+        p(ua), 0 if ua is None else len(ua), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_gdr_recurrence rejected the problem")
+    return o, hT
+
+
+def recurrence_np(q, k, v, beta, log_alpha, h0=None, beta_per_key_head=False):
+    """fp64 token recurrence in numpy (small sizes)."""
+    B, T, Hk, Hv, dk, dv, G = _shapes(q, v, log_alpha)
+    R = Hv // Hk
+    key_of = np.arange(Hv) // R
+    q = np.asarray(q, np.float64)[:, :, key_of]          # [B, T, Hv, dk]
+    k = np.asarray(k, np.float64)[:, :, key_of]
+    v = np.asarray(v, np.float64)
+    la = np.asarray(log_alpha, np.float64)[:, :, key_of]  # [B, T, Hv, G]
+    la = np.repeat(la, dk // G, axis=3)                   # [B, T, Hv, dk]
+    beta = np.asarray(beta, np.float64)
+    if beta_per_key_head:
+        beta = beta[:, :, key_of]
+    S = np.zeros((B, Hv, dk, dv)) if h0 is None else np.array(h0, np.float64)
+    o = np.zeros((B, T, Hv, dv))
+    for t in range(T):
+        S = np.exp(la[:, t])[..., None] * S                           # F_t S_{t-1}
+        u = v[:, t] - np.einsum("bhij,bhi->bhj", S, k[:, t])          # v_t - (F_t S)^T k_t
+        S = S + beta[:, t, :, None, None] * k[:, t, :, :, None] * u[:, :, None, :]
+        o[:, t] = np.einsum("bhij,bhi->bhj", S, q[:, t])               # S_t^T q_t
+    return o, S
