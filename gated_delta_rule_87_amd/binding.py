@@ -1,0 +1,230 @@
+"""ctypes binding of libgdr.so with the C ABI's names (include/gdr.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if libgdr.so is missing or a tensor is not on
+the GPU, the call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
+GDR_F32, GDR_BF16 = 0, 1
+GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
+
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_prepare", "gdr_chunk_scan",
+           "gdr_recurrent_step", "gdr_status_string", "gdr_last_error")
+
+
+class GdrProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "B", "T", "H_k", "H_v", "d_k", "d_v", "chunk", "gate_groups", "beta_per_key_head",
+        "in_dtype", "out_dtype", "solve", "neumann_order", "neumann_residual_steps")]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libgdr.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_87_amd._build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(GdrProblem)
+        vp = ctypes.c_void_p
+        lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+        lib.gdr_chunk_fwd_workspace_size.argtypes = [P]
+        lib.gdr_chunk_fwd.restype = ctypes.c_int
+        lib.gdr_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_scan.restype = ctypes.c_int
+        lib.gdr_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_prepare.restype = ctypes.c_int
+        lib.gdr_chunk_prepare.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_recurrent_step.restype = ctypes.c_int
+        lib.gdr_recurrent_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_status_string.restype = ctypes.c_char_p
+        lib.gdr_status_string.argtypes = [ctypes.c_int]
+        lib.gdr_last_error.restype = ctypes.c_char_p
+        lib.gdr_last_error.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def status_string(status):
+    return load().gdr_status_string(int(status)).decode()
+
+
+def last_error():
+    return load().gdr_last_error().decode()
+
+
+def _check(status):
+    if status != GDR_OK:
+        raise GdrError(status, last_error())
+
+
+_DT = {torch.float32: GDR_F32, torch.bfloat16: GDR_BF16}
+
+
+def make_problem(q, v, log_alpha, beta, *, chunk=64, solve="exact", neumann_order=4,
+                 neumann_residual_steps=1, out_dtype=torch.float32):
+    """A gdr_problem from tensor shapes (q [B,T,H_k,d_k], v [B,T,H_v,d_v],
+    log_alpha [B,T,H_k,G], beta [B,T,H_v] or [B,T,H_k])."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if q.dtype not in _DT or out_dtype not in _DT:
+        raise TypeError(f"dtypes must be float32 or bfloat16, got {q.dtype} / {out_dtype}")
+    if beta.shape[2] not in (Hk, Hv):
+        raise ValueError(f"beta has {beta.shape[2]} heads; expected H_v={Hv} or H_k={Hk}")
+    p = GdrProblem()
+    p.B, p.T, p.H_k, p.H_v, p.d_k, p.d_v = B, T, Hk, Hv, dk, dv
+    p.chunk = chunk
+    p.gate_groups = log_alpha.shape[3]
+    p.beta_per_key_head = int(beta.shape[2] == Hk and Hk != Hv)
+    p.in_dtype = _DT[q.dtype]
+    p.out_dtype = _DT[out_dtype]
+    p.solve = {"exact": GDR_SOLVE_EXACT, "neumann": GDR_SOLVE_NEUMANN}[solve]
+    p.neumann_order = neumann_order
+    p.neumann_residual_steps = neumann_residual_steps
+    return p
+
+
+def _ptr(t, name, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_inputs(q, k, v, beta, log_alpha):
+    dt = q.dtype
+    B, T, Hk, dk = q.shape
+    _ptr(q, "q", dt)
+    _ptr(k, "k", dt, q.shape)
+    if v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise ValueError(f"v has shape {tuple(v.shape)}; expected [B, T, H_v, d_v] with B={B}, T={T}")
+    _ptr(v, "v", dt)
+    if beta.dim() != 3 or beta.shape[:2] != q.shape[:2]:
+        raise ValueError(f"beta has shape {tuple(beta.shape)}; expected [B, T, H]")
+    _ptr(beta, "beta", dt)
+    if log_alpha.dim() != 4 or log_alpha.shape[:3] != q.shape[:3]:
+        raise ValueError(f"log_alpha has shape {tuple(log_alpha.shape)}; expected [B, T, H_k, G]")
+    _ptr(log_alpha, "log_alpha", dt)
+
+
+def gdr_chunk_fwd_workspace_size(problem):
+    return int(load().gdr_chunk_fwd_workspace_size(ctypes.byref(problem)))
+
+
+def _chunk_call(entry, q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order, neumann_residual_steps,
+                out_dtype, o, hT, return_final_state, workspace, stream):
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, chunk=chunk, solve=solve, neumann_order=neumann_order,
+                     neumann_residual_steps=neumann_residual_steps, out_dtype=out_dtype)
+    dev = q.device
+    if o is None:
+        o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=dev)
+    state_shape = (p.B, p.H_v, p.d_k, p.d_v)
+    if hT is None and return_final_state:
+        hT = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    ws_bytes = gdr_chunk_fwd_workspace_size(p)
+    if ws_bytes == 0 and p.B * p.T > 0:
+        _check(getattr(lib, entry)(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None))
+    if workspace is None:
+        if entry == "gdr_chunk_scan":
+            raise ValueError("gdr_chunk_scan needs the workspace gdr_chunk_prepare filled")
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(getattr(lib, entry)(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"),
+        _ptr(log_alpha, "log_alpha"), _ptr(h0, "h0", torch.float32, state_shape),
+        _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _ptr(hT, "hT", torch.float32, state_shape),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, hT
+
+
+def gdr_chunk_fwd(q, k, v, beta, log_alpha, h0=None, *, chunk=64, solve="exact", neumann_order=4,
+                  neumann_residual_steps=1, out_dtype=torch.float32, o=None, hT=None,
+                  return_final_state=True, workspace=None, stream=None):
+    """Chunkwise forward.  Returns (o [B,T,H_v,d_v], hT [B,H_v,d_k,d_v] fp32 or None).
+
+    ``workspace`` (a GPU tensor) may be passed to avoid an allocation; on
+    return it holds A_c and L_c (see gdr_chunk_fwd_workspace_size)."""
+    return _chunk_call("gdr_chunk_fwd", q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order,
+                       neumann_residual_steps, out_dtype, o, hT, return_final_state, workspace, stream)
+
+
+def gdr_chunk_scan(q, k, v, beta, log_alpha, h0=None, *, workspace, chunk=64, solve="exact", neumann_order=4,
+                   neumann_residual_steps=1, out_dtype=torch.float32, o=None, hT=None,
+                   return_final_state=True, stream=None):
+    """State scan and output over a workspace filled by gdr_chunk_prepare."""
+    return _chunk_call("gdr_chunk_scan", q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order,
+                       neumann_residual_steps, out_dtype, o, hT, return_final_state, workspace, stream)
+
+
+def gdr_chunk_prepare(q, k, beta, log_alpha, *, chunk=64, solve="exact", neumann_order=4,
+                      neumann_residual_steps=1, H_v=None, workspace=None, stream=None):
+    """Per-chunk matrices only.  Returns (A [B,H_beta,N_c,C,C], L [B,H_k,N_c,C,C]) fp32,
+    views into ``workspace`` (allocated if not given; a float32 GPU tensor)."""
+    lib = load()
+    B, T, Hk, dk = q.shape
+    Hv = beta.shape[2] if H_v is None else H_v
+    fake_v = torch.empty((B, T, Hv, 16), dtype=q.dtype, device=q.device)
+    _check_inputs(q, k, fake_v, beta, log_alpha)
+    p = make_problem(q, fake_v, log_alpha, beta, chunk=chunk, solve=solve, neumann_order=neumann_order,
+                     neumann_residual_steps=neumann_residual_steps)
+    ws_bytes = gdr_chunk_fwd_workspace_size(p)
+    nc = (T + chunk - 1) // chunk
+    Hb = Hk if p.beta_per_key_head else Hv
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device=q.device)
+    _check(lib.gdr_chunk_prepare(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(beta, "beta"),
+                                 _ptr(log_alpha, "log_alpha"), _ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    ws = workspace.view(torch.float32) if workspace.dtype != torch.float32 else workspace
+    nA = B * Hb * nc * chunk * chunk
+    A = ws[:nA].view(B, Hb, nc, chunk, chunk)
+    L = ws[nA:nA + B * Hk * nc * chunk * chunk].view(B, Hk, nc, chunk, chunk)
+    return A, L
+
+
+def gdr_recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None, stream=None):
+    """Token recurrence over q.shape[1] tokens; ``state`` (fp32 [B,H_v,d_k,d_v])
+    is updated in place.  Returns o [B,T,H_v,d_v]."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, out_dtype=out_dtype)
+    if o is None:
+        o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=q.device)
+    _check(lib.gdr_recurrent_step(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
+        _ptr(state, "state", torch.float32, (p.B, p.H_v, p.d_k, p.d_v)),
+        _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _stream(stream)))
+    return o

@@ -1,0 +1,199 @@
+// Device helpers shared by the gfx950 kernels: MFMA wrappers and operand
+// fragments.
+//
+// MFMA tiles are 16x16 with a 32-deep contraction block.  For one wave64:
+//   A operand (16 x 32): lane l holds row l%16, contraction indices
+//                        8*(l/16) .. 8*(l/16)+7
+//   B operand (32 x 16): lane l holds column l%16, the same 8 indices
+//   D (16 x 16, fp32):   lane l holds column l%16, rows 4*(l/16) .. +3
+// Any consistent assignment of contraction indices gives the same product,
+// so the fp32 path (v_mfma_f32_16x16x4_f32, four indices per instruction)
+// reuses the layout: instruction s takes index 8*(l/16)+s from every lane,
+// and eight instructions cover the block.
+//
+// Precision.  An operand is a fragment of one of three kinds:
+//   Plain  - eight bf16 values (round-to-nearest-even of the fp32 value);
+//   Split  - hi = bf16(x), lo = bf16(x - hi): ~16 significant bits;
+//   F32    - eight fp32 values for the fp32 MFMA.
+// A product of two Split fragments costs three bf16 MFMAs (lo*hi, hi*lo,
+// hi*hi; lo*lo is below fp32 accumulation noise), Split x Plain two, and
+// Plain x Plain one.  Which operands must be Split is a numerical decision
+// made per product in the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
+
+// Loads of one input element as fp32 (bf16 decodes exactly).
+__device__ __forceinline__ float ldf(const float *p) { return *p; }
+__device__ __forceinline__ float ldf(const bf16 *p) { return static_cast<float>(*p); }
+
+// Eight consecutive inputs as fp32.
+__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void ld8(const bf16 *p, float (&x)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
+}
+
+__device__ __forceinline__ void st(float *p, float x) { *p = x; }
+__device__ __forceinline__ void st(bf16 *p, float x) { *p = to_bf16(x); }
+
+// ----------------------------------------------------------------- fragments
+struct FragP {            // plain bf16
+  bf16x8 h;
+};
+struct FragS {            // split bf16 hi + lo
+  bf16x8 h, l;
+};
+struct FragF {            // fp32
+  float v[8];
+};
+
+template <class F> __device__ __forceinline__ F make_frag(const float (&x)[8]);
+
+template <> __device__ __forceinline__ FragP make_frag<FragP>(const float (&x)[8]) {
+  FragP f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.h[e] = to_bf16(x[e]);
+  return f;
+}
+template <> __device__ __forceinline__ FragS make_frag<FragS>(const float (&x)[8]) {
+  FragS f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = to_bf16(x[e]);
+    f.h[e] = h;
+    f.l[e] = to_bf16(x[e] - static_cast<float>(h));
+  }
+  return f;
+}
+template <> __device__ __forceinline__ FragF make_frag<FragF>(const float (&x)[8]) {
+  FragF f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = x[e];
+  return f;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4 &c, const FragP &a, const FragP &b) {
+  c = mfma_bf16(a.h, b.h, c);
+}
+__device__ __forceinline__ void mma(f32x4 &c, const FragP &a, const FragS &b) {
+  c = mfma_bf16(a.h, b.l, c);
+  c = mfma_bf16(a.h, b.h, c);
+}
+__device__ __forceinline__ void mma(f32x4 &c, const FragS &a, const FragP &b) {
+  c = mfma_bf16(a.l, b.h, c);
+  c = mfma_bf16(a.h, b.h, c);
+}
+__device__ __forceinline__ void mma(f32x4 &c, const FragS &a, const FragS &b) {
+  c = mfma_bf16(a.l, b.h, c);
+  c = mfma_bf16(a.h, b.l, c);
+  c = mfma_bf16(a.h, b.h, c);
+}
+__device__ __forceinline__ void mma(f32x4 &c, const FragF &a, const FragF &b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = mfma_f32(a.v[s], b.v[s], c);
+}
+
+// Precision policies.  Each kernel names, per operand, whether it needs the
+// Split kind; the fp32 policy maps every kind to FragF.
+struct PrecBF16 {
+  using Plain = FragP;
+  using Split = FragS;
+  static constexpr bool kF32 = false;
+};
+struct PrecF32 {
+  using Plain = FragF;
+  using Split = FragF;
+  static constexpr bool kF32 = true;
+};
+
+// LDS storage of an operand that is read back as B fragments: element (n, k)
+// of an N x K operand (column n of the B matrix, contraction index k) lives at
+// n * ld + k, so a fragment is eight consecutive values.  bf16 policy: hi and
+// lo planes; fp32 policy: one fp32 plane (same bytes).
+template <class P> struct OperandLds;
+
+template <> struct OperandLds<PrecBF16> {
+  bf16 *hi;
+  bf16 *lo;
+  int ld;
+  static constexpr int kBytesPerElem = 4;
+  __device__ __forceinline__ void init(void *base, int n_rows, int ld_) {
+    hi = reinterpret_cast<bf16 *>(base);
+    lo = hi + n_rows * ld_;
+    ld = ld_;
+  }
+  __device__ __forceinline__ void put(int n, int k, float x) {
+    const bf16 h = to_bf16(x);
+    hi[n * ld + k] = h;
+    lo[n * ld + k] = to_bf16(x - static_cast<float>(h));
+  }
+  // four consecutive k for one n (D-layout rows of one column)
+  __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
+    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 h, l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = to_bf16(x[r]);
+      l[r] = to_bf16(x[r] - static_cast<float>(h[r]));
+    }
+    *reinterpret_cast<bf16x4 *>(hi + n * ld + k) = h;
+    *reinterpret_cast<bf16x4 *>(lo + n * ld + k) = l;
+  }
+  __device__ __forceinline__ FragS get(int n, int k) const {
+    FragS f;
+    f.h = *reinterpret_cast<const bf16x8 *>(hi + n * ld + k);
+    f.l = *reinterpret_cast<const bf16x8 *>(lo + n * ld + k);
+    return f;
+  }
+};
+
+template <> struct OperandLds<PrecF32> {
+  float *v;
+  int ld;
+  static constexpr int kBytesPerElem = 4;
+  __device__ __forceinline__ void init(void *base, int /*n_rows*/, int ld_) {
+    v = reinterpret_cast<float *>(base);
+    ld = ld_;
+  }
+  __device__ __forceinline__ void put(int n, int k, float x) { v[n * ld + k] = x; }
+  __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
+    *reinterpret_cast<f32x4 *>(v + n * ld + k) = x;
+  }
+  __device__ __forceinline__ FragF get(int n, int k) const {
+    FragF f;
+    const float4 a = *reinterpret_cast<const float4 *>(v + n * ld + k);
+    const float4 b = *reinterpret_cast<const float4 *>(v + n * ld + k + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+};
+
+}  // namespace gdr

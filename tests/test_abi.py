@@ -1,0 +1,153 @@
+"""The C ABI on the host (no GPU): libgdr.so loads, exports every entry point
+include/gdr.h declares, sizes its workspace, and rejects every malformed call
+with its documented status before anything is launched.
+
+Every call here fails validation; none is a well-formed problem with real
+device pointers, so nothing reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_87_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gb.LIB_PATH), reason="libgdr.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    lib = gb.load()
+    names = declared_functions()
+    assert set(names) == set(gb.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings():
+    assert gb.status_string(gb.GDR_OK) == "GDR_OK"
+    assert gb.status_string(gb.GDR_ERR_INVALID_ARG) == "GDR_ERR_INVALID_ARG"
+    assert gb.status_string(gb.GDR_ERR_UNSUPPORTED) == "GDR_ERR_UNSUPPORTED"
+    assert gb.status_string(gb.GDR_ERR_WORKSPACE) == "GDR_ERR_WORKSPACE"
+    assert gb.status_string(gb.GDR_ERR_HIP) == "GDR_ERR_HIP"
+
+
+def problem(**kw):
+    p = gb.GdrProblem()
+    base = dict(B=2, T=8192, H_k=32, H_v=32, d_k=128, d_v=128, chunk=64, gate_groups=128,
+                beta_per_key_head=0, in_dtype=gb.GDR_BF16, out_dtype=gb.GDR_F32, solve=0,
+                neumann_order=4, neumann_residual_steps=1)
+    base.update(kw)
+    for k_, v_ in base.items():
+        setattr(p, k_, v_)
+    return p
+
+
+def test_workspace_size():
+    lib = gb.load()
+    p = problem()
+    # A per value head and L per key head, fp32 C x C per chunk
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 64 * 64 * 128 * 2 * (32 + 32)
+    p = problem(H_k=8, H_v=32, d_k=256, gate_groups=4, T=100)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 64 * 64 * 2 * 2 * (32 + 8)
+    p = problem(H_k=8, H_v=32, d_k=256, gate_groups=4, T=100, beta_per_key_head=1)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 64 * 64 * 2 * 2 * (8 + 8)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(problem(H_v=30))) == 0
+    assert lib.gdr_chunk_fwd_workspace_size(None) == 0
+
+
+FAKE = 0x10000          # 64 KiB-aligned non-null address, never dereferenced
+MIS = 0x10004           # misaligned
+
+
+def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, la=FAKE, h0=None, o=FAKE, hT=None, ws=FAKE, ws_bytes=None):
+    lib = gb.load()
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    vp = ctypes.c_void_p
+    return lib.gdr_chunk_fwd(None if p is None else ctypes.byref(p), vp(q), vp(k), vp(v), vp(beta), vp(la),
+                             vp(h0), vp(o), vp(hT), vp(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_v=30), gb.GDR_ERR_INVALID_ARG),
+    (dict(H_k=0), gb.GDR_ERR_INVALID_ARG),
+    (dict(B=-1), gb.GDR_ERR_INVALID_ARG),
+    (dict(T=-5), gb.GDR_ERR_INVALID_ARG),
+    (dict(d_v=0), gb.GDR_ERR_INVALID_ARG),
+    (dict(gate_groups=3), gb.GDR_ERR_INVALID_ARG),
+    (dict(gate_groups=0), gb.GDR_ERR_INVALID_ARG),
+    (dict(in_dtype=7), gb.GDR_ERR_INVALID_ARG),
+    (dict(out_dtype=-1), gb.GDR_ERR_INVALID_ARG),
+    (dict(beta_per_key_head=2), gb.GDR_ERR_INVALID_ARG),
+    (dict(chunk=0), gb.GDR_ERR_INVALID_ARG),
+    (dict(solve=5), gb.GDR_ERR_INVALID_ARG),
+    (dict(solve=1, neumann_order=-1), gb.GDR_ERR_INVALID_ARG),
+    (dict(solve=1, neumann_residual_steps=-2), gb.GDR_ERR_INVALID_ARG),
+    (dict(d_k=96, gate_groups=96), gb.GDR_ERR_UNSUPPORTED),
+    (dict(d_v=72), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=48), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=32), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=128, d_k=256, gate_groups=256), gb.GDR_ERR_UNSUPPORTED),
+    (dict(B=1 << 20, T=1 << 20), gb.GDR_ERR_INVALID_ARG),
+])
+def test_invalid_problems(kw, status):
+    assert call_fwd(problem(**kw)) == status
+    assert gb.last_error() != ""
+
+
+def test_null_problem():
+    assert call_fwd(None) == gb.GDR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "beta", "la", "o", "ws"])
+def test_null_pointer(arg):
+    assert call_fwd(problem(), **{arg: 0}) == gb.GDR_ERR_INVALID_ARG
+    assert "NULL" in gb.last_error()
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "beta", "la", "o", "h0", "hT", "ws"])
+def test_misaligned_pointer(arg):
+    assert call_fwd(problem(), **{arg: MIS}) == gb.GDR_ERR_INVALID_ARG
+    assert "aligned" in gb.last_error()
+
+
+def test_workspace_too_small():
+    p = problem()
+    need = gb.load().gdr_chunk_fwd_workspace_size(ctypes.byref(p))
+    assert call_fwd(p, ws_bytes=need - 1) == gb.GDR_ERR_WORKSPACE
+    assert str(need) in gb.last_error()
+
+
+def test_prepare_and_step_validate():
+    lib = gb.load()
+    vp = ctypes.c_void_p
+    p = problem(H_v=30)
+    assert lib.gdr_chunk_prepare(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1 << 40,
+                                 None) == gb.GDR_ERR_INVALID_ARG
+    p = problem()
+    assert lib.gdr_chunk_prepare(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 16,
+                                 None) == gb.GDR_ERR_WORKSPACE
+    # the recurrent path ignores chunk/solve but checks the rest
+    p = problem(chunk=0, solve=9)
+    assert lib.gdr_recurrent_step(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(0),
+                                  vp(FAKE), None) == gb.GDR_ERR_INVALID_ARG
+    assert "state" in gb.last_error()
+    p = problem(d_k=32, gate_groups=32)
+    assert lib.gdr_recurrent_step(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                  vp(FAKE), None) == gb.GDR_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        gb.gdr_chunk_fwd(q, q, q, torch.zeros(1, 64, 1), torch.zeros(1, 64, 1, 1))

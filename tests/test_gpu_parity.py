@@ -1,0 +1,138 @@
+"""GPU path (libgdr.so through the C ABI) against the fp64 CPU oracle.
+
+Statistic: max |x_gpu - x_ref| / rms(x_ref) over all elements, for o and for
+hT separately.  Bar: 1e-2 for bf16 inputs, 1e-4 for fp32 inputs.  The oracle
+for the exact mode is the token recurrence; for the Neumann mode it is the
+fp64 chunk form with the same truncated series (its distance to the exact
+recurrence is reported, not bounded).
+
+Sizes here finish in seconds on the CPU side, span several chunks and
+16-token tiles, and end in a ragged final chunk.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_87_amd import binding as gb
+from gated_delta_rule_87_amd.inputs import Workload
+from gpu_common import TOL, device_inputs, draw, need_gpu, rel_err, run_chunk, to_torch
+from oracle import chunk as och
+from oracle.recurrence import recurrence_c
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "gdn_f32": Workload("gdn_f32", 2, 300, 2, 2, 64, 64, 64, 1, "f32", seed=1),
+    "kda_f32_c128": Workload("kda_f32_c128", 1, 333, 2, 2, 128, 32, 128, 128, "f32", seed=2),
+    "gdn_bf16": Workload("gdn_bf16", 2, 300, 2, 2, 128, 128, 64, 1, "bf16", seed=3),
+    "kda_bf16": Workload("kda_bf16", 1, 517, 2, 2, 128, 64, 64, 128, "bf16", seed=4),
+    "gva_g4_bf16": Workload("gva_g4_bf16", 1, 300, 2, 8, 256, 128, 64, 4, "bf16", seed=5),
+    "kda_c128_strong": Workload("kda_c128_strong", 1, 700, 2, 2, 128, 128, 128, 128, "bf16",
+                                alpha_mu=1.0, alpha_sigma=2.0, seed=6),
+    "dk64_bkh_gva": Workload("dk64_bkh_gva", 2, 190, 2, 4, 64, 48, 64, 8, "bf16", beta_per_key_head=True, seed=7),
+    "dk256_kda_bf16": Workload("dk256_kda_bf16", 1, 200, 1, 1, 256, 64, 64, 256, "bf16", seed=8),
+}
+
+
+def oracle(x, w, h0=None, units=None):
+    return recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], h0, w.beta_per_key_head,
+                        units=units)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)}", flush=True)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_chunk_fwd_small(name):
+    w = SMALL[name]
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    print(f"[case] chunk_fwd {name}", flush=True)
+    o, hT = run_chunk(dev, w)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle(x, w)
+    eo, eh = rel_err(o.cpu().numpy(), o_ref), rel_err(hT.cpu().numpy(), h_ref)
+    print(f"  err o={eo:.3e} hT={eh:.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name", ["gdn_f32", "kda_bf16", "dk64_bkh_gva"])
+def test_chunk_fwd_nonzero_h0(name):
+    w = SMALL[name]
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    rng = np.random.default_rng(11)
+    h0 = rng.standard_normal((w.B, w.H_v, w.d_k, w.d_v)).astype(np.float32)
+    print(f"[case] chunk_fwd h0 {name}", flush=True)
+    o, hT = run_chunk(dev, w, h0=to_torch(h0))
+    o_ref, h_ref = oracle(x, w, h0.astype(np.float64))
+    eo, eh = rel_err(o.cpu().numpy(), o_ref), rel_err(hT.cpu().numpy(), h_ref)
+    print(f"  err o={eo:.3e} hT={eh:.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name,order,res", [("kda_c128_strong", 4, 1), ("kda_bf16", 2, 1), ("kda_f32_c128", 3, 2),
+                                            ("gva_g4_bf16", 1, 0)])
+def test_neumann_small(name, order, res):
+    w = SMALL[name].with_(neumann_order=order, neumann_residual=res)
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    print(f"[case] neumann {name} m={order} r={res}", flush=True)
+    o, hT = run_chunk(dev, w, solve="neumann")
+    o_n, h_n = och.chunk_forward(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], chunk=w.chunk,
+                                 solve="neumann", order=order, residual_steps=res,
+                                 beta_per_key_head=w.beta_per_key_head)
+    o_ref, _ = oracle(x, w)
+    eo, eh = rel_err(o.cpu().numpy(), o_n), rel_err(hT.cpu().numpy(), h_n)
+    print(f"  err vs neumann oracle o={eo:.3e} hT={eh:.3e}; neumann oracle vs exact recurrence "
+          f"{rel_err(o_n, o_ref):.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong"])
+@pytest.mark.parametrize("solve", ["exact", "neumann"])
+def test_prepare_matrices(name, solve):
+    """A_c and L_c of every chunk against the fp64 chunk quantities."""
+    w = SMALL[name]
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    print(f"[case] prepare {name} {solve}", flush=True)
+    A, L = gb.gdr_chunk_prepare(dev["q"], dev["k"], dev["beta"], dev["log_alpha"], chunk=w.chunk, solve=solve,
+                                neumann_order=w.neumann_order, neumann_residual_steps=w.neumann_residual,
+                                H_v=w.H_v)
+    A_ref, L_ref = och.chunk_stage_matrices(x["q"], x["k"], x["beta"], x["log_alpha"], w.chunk, solve=solve,
+                                            order=w.neumann_order, residual_steps=w.neumann_residual,
+                                            beta_per_key_head=w.beta_per_key_head)
+    A, L = A.cpu().numpy(), L.cpu().numpy()
+    tol = 1e-5 if w.dtype == "f32" else 1e-4
+    ea = np.max(np.abs(A - A_ref)) / np.max(np.abs(A_ref))
+    el = np.max(np.abs(L - L_ref)) / np.max(np.abs(L_ref))
+    print(f"  err A={ea:.3e} L={el:.3e}", flush=True)
+    assert ea <= tol and el <= tol
+
+
+RECUR = {
+    "f32_g1": Workload("f32_g1", 2, 37, 2, 2, 64, 32, 64, 1, "f32", seed=21),
+    "bf16_kda": Workload("bf16_kda", 1, 50, 2, 4, 128, 64, 64, 128, "bf16", seed=22),
+    "bf16_g4_dk256": Workload("bf16_g4_dk256", 1, 20, 1, 2, 256, 128, 64, 4, "bf16", seed=23),
+    "bf16_bkh": Workload("bf16_bkh", 2, 9, 2, 4, 64, 16, 64, 64, "bf16", beta_per_key_head=True, seed=24),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RECUR))
+def test_recurrent_step(name):
+    w = RECUR[name]
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    rng = np.random.default_rng(5)
+    s0 = rng.standard_normal((w.B, w.H_v, w.d_k, w.d_v)).astype(np.float32)
+    state = to_torch(s0)
+    print(f"[case] recurrent {name}", flush=True)
+    o = gb.gdr_recurrent_step(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], state)
+    o_ref, h_ref = oracle(x, w, s0.astype(np.float64))
+    eo, eh = rel_err(o.cpu().numpy(), o_ref), rel_err(state.cpu().numpy(), h_ref)
+    print(f"  err o={eo:.3e} state={eh:.3e}", flush=True)
+    assert eo <= 1e-5 and eh <= 1e-5
