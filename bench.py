@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Chunkwise gated delta-rule forward on one MI355X: throughput, roofline,
+and the fp64 CPU oracle timed beside it.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--solve exact|neumann]
+    python bench.py --copy-calibration BYTES      # plain copy, for rocprofv3 --pmc scaling
+
+One step is one full forward over the workload's synthetic batch, inputs
+already resident in HBM: the chunk-prep kernel then the scan/output kernel
+(exactly the launches of gdr_chunk_fwd, issued as gdr_chunk_prepare +
+gdr_chunk_scan so that HIP events on the launch stream time each kernel).
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec and MFMA TFLOP/s (% of peak) for chunkwise gated-delta fwd, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA peaks
+KERNEL_SOURCES = {
+    "prep": ["gated_delta_rule_87_amd/csrc/prep.hip", "gated_delta_rule_87_amd/csrc/common.hpp"],
+    "scan": ["gated_delta_rule_87_amd/csrc/scan.hip", "gated_delta_rule_87_amd/csrc/common.hpp"],
+}
+
+
+def source_sha(kernel):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_model(w):
+    """Algorithmic FLOPs and bytes per kernel ("Roofline")."""
+    C, dk, dv = w.chunk, w.d_k, w.d_v
+    R = w.H_v // w.H_k
+    token_heads = w.B * w.T * w.H_v
+    es = 2 if w.dtype == "bf16" else 4
+    flops_prep = token_heads * (2.0 * C * dk / R + C * C / 3.0)
+    flops_scan = token_heads * ((C + 1.0) * (dk + 2.0 * dv) + 6.0 * dk * dv)
+    bt = w.B * w.T
+    key_side = es * bt * (2 * w.H_k * dk + w.H_k * w.G + w.H_beta)   # q, k, log_alpha, beta
+    bytes_prep = key_side
+    bytes_scan = key_side + es * bt * w.H_v * dv + 4 * bt * w.H_v * dv + 4 * w.B * w.H_v * dk * dv
+    return {"prep": (flops_prep, bytes_prep), "scan": (flops_scan, bytes_scan)}
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    e = data.get(f"{kernel}:{workload}")
+    if not e or e.get("source_sha") != source_sha(kernel):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, o_gpu, target_s=10.0):
+    """The fp64 oracle on a bounded sample of (batch, value head) units over the
+    full sequence, on this host's cores; also the GPU's error on that sample."""
+    import numpy as np
+    from oracle.recurrence import recurrence_c   # test infrastructure: baseline leg only
+
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    units_all = w.B * w.H_v
+    # calibrate: one unit over a short prefix
+    Tc = min(w.T, 256)
+    sl = lambda a: np.ascontiguousarray(a[:1, :Tc])
+    t = time.perf_counter()
+    recurrence_c(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["log_alpha"]),
+                 beta_per_key_head=w.beta_per_key_head, units=[0], nthreads=1)
+    per_token_head = (time.perf_counter() - t) / Tc
+    n_units = int(target_s * threads / max(per_token_head * w.T, 1e-9))
+    n_units = max(1, min(units_all, (n_units // threads) * threads or threads))
+    rng = np.random.default_rng(12345)
+    units = sorted(rng.choice(units_all, size=n_units, replace=False).tolist())
+    t = time.perf_counter()
+    o_ref, _ = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"],
+                            beta_per_key_head=w.beta_per_key_head, units=units, nthreads=threads)
+    dt = time.perf_counter() - t
+    tokens_equiv = n_units * w.T / w.H_v          # whole-job tokens (all heads) the sample is worth
+    err = None
+    if o_gpu is not None:
+        num, den = 0.0, 0.0
+        for u in units:
+            b, h = divmod(u, w.H_v)
+            ref = o_ref[b, :, h]
+            num = max(num, float(np.max(np.abs(o_gpu[b, :, h] - ref))))
+            den += float(np.sum(ref ** 2))
+        err = num / (den / (n_units * w.T * w.d_v)) ** 0.5
+    return {
+        "value": tokens_equiv / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": f"{n_units} of {units_all} (batch, value head) units x all {w.T} tokens, "
+                  f"fp64 token recurrence in C, {dt:.1f} s",
+    }, err
+
+
+def copy_calibration(nbytes, steps):
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / steps
+    print(json.dumps({"copy_bytes": n * 4, "steps": steps, "ms_per_copy": dt * 1e3,
+                      "GBs_read_plus_write": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index (default: per-channel-gate KDA)")
+    ap.add_argument("--solve", default=None, choices=["exact", "neumann"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (batch, head) unit is independent; see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
+
+    import numpy as np
+    import torch
+
+    from gated_delta_rule_87_amd import binding as gb
+    from gated_delta_rule_87_amd.inputs import WORKLOADS, decoded, make_inputs
+
+    w = WORKLOADS[args.config]
+    solve = args.solve or w.solves[0]
+    print(f"[bench] workload {w.name}: {w.description}; solve={solve}", file=sys.stderr, flush=True)
+    raw = make_inputs(w)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    q, k, v, beta, la = (dev(raw[n]) for n in ("q", "k", "v", "beta", "log_alpha"))
+    p = gb.make_problem(q, v, la, beta, chunk=w.chunk, solve=solve, neumann_order=w.neumann_order,
+                        neumann_residual_steps=w.neumann_residual)
+    ws = torch.empty(gb.gdr_chunk_fwd_workspace_size(p) // 4, dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, w.T, w.H_v, w.d_v), dtype=torch.float32, device="cuda")
+    hT = torch.empty((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    kw = dict(chunk=w.chunk, solve=solve, neumann_order=w.neumann_order,
+              neumann_residual_steps=w.neumann_residual)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        gb.gdr_chunk_prepare(q, k, beta, la, H_v=w.H_v, workspace=ws, **kw)
+        if evs:
+            evs[1].record()
+        gb.gdr_chunk_scan(q, k, v, beta, la, None, workspace=ws, o=o, hT=hT, **kw)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed / args.steps * 1e3
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    tokens = w.B * w.T
+    model = work_model(w)
+    flops_total = model["prep"][0] + model["scan"][0]
+    tflops = flops_total / (ms_step * 1e-3) / 1e12
+    dtype = "bf16" if w.dtype == "bf16" else "f32"
+
+    dom = "scan" if scan_ms >= prep_ms else "prep"
+    dom_ms = scan_ms if dom == "scan" else prep_ms
+    f_dom, b_dom = model[dom]
+    path_bytes = model["scan"][1]
+    hbm_bound = path_bytes / (HBM_PEAK_GBS * 1e9) >= flops_total / (MFMA_PEAK_TFS[dtype] * 1e12)
+    if hbm_bound:
+        achieved = b_dom / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = f_dom / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFS[dtype], "unit": "TFLOP/s",
+                "frac": achieved / MFMA_PEAK_TFS[dtype]}
+    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(dom, w.name)
+
+    result = {
+        "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H_k": w.H_k, "H_v": w.H_v, "d_k": w.d_k,
+                   "d_v": w.d_v, "chunk": w.chunk, "gate_groups": w.G, "solve": solve,
+                   "in_dtype": w.dtype, "out_dtype": "f32", "parallelism": "single-gpu"},
+        "tflops_useful": tflops, "mfma_frac_useful": tflops / MFMA_PEAK_TFS[dtype],
+        "kernel_ms": {"prep": prep_ms, "scan": scan_ms},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        o_np = o.cpu().numpy()
+        cb, err = cpu_baseline(w, decoded(raw), o_np)
+        result["cpu_baseline"] = cb
+        result["parity_sample_max_err_over_rms"] = err
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

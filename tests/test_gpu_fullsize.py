@@ -1,0 +1,182 @@
+"""Every workload at its full size, through gdr_chunk_fwd exactly as bench.py
+launches it, against the fp64 oracle on sampled (batch, value head) units
+over the whole sequence.  Plus GPU-side invariants: determinism, resume from
+hT, grouped value heads == replicated heads, extreme decay, empty input.
+
+Statistic per sample: max |o_gpu - o_ref| / rms(o_ref) over the sampled
+units (and the same for hT); bar 1e-2 (bf16 inputs) / 1e-4 (fp32 inputs).
+The Neumann run of the strong-decay workload is held to the bar against the
+fp64 chunk form with the same truncated series; its distance to the exact
+recurrence is printed (the pages bound it for trained layers only).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_87_amd import binding as gb
+from gated_delta_rule_87_amd.inputs import WORKLOADS, Workload
+from gpu_common import TOL, device_inputs, draw, need_gpu, rel_err, run_chunk, to_torch
+from oracle import chunk as och
+from oracle.recurrence import recurrence_c
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def sample_units(w, n=3):
+    total = w.B * w.H_v
+    return sorted({0, total // 2, total - 1} if n == 3 else set(range(min(n, total))))
+
+
+def unit_err(o, o_ref, w, units):
+    got = np.concatenate([o[u // w.H_v, :, u % w.H_v] for u in units])
+    ref = np.concatenate([o_ref[u // w.H_v, :, u % w.H_v] for u in units])
+    return rel_err(got, ref)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_workload_exact(cfg):
+    w = WORKLOADS[cfg]
+    print(f"\n[case] full-size exact {w.name}", flush=True)
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    o, hT = run_chunk(dev, w)
+    o, hT = o.cpu().numpy(), hT.cpu().numpy()
+    units = list(range(w.B * w.H_v)) if cfg == 0 else sample_units(w)
+    o_ref, h_ref = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"],
+                                beta_per_key_head=w.beta_per_key_head, units=units)
+    eo = unit_err(o, o_ref, w, units)
+    eh = rel_err(np.stack([hT[u // w.H_v, u % w.H_v] for u in units]),
+                 np.stack([h_ref[u // w.H_v, u % w.H_v] for u in units]))
+    print(f"  {w.name}: units {units} err o={eo:.3e} hT={eh:.3e} (bar {TOL[w.dtype]:g})", flush=True)
+    assert np.all(np.isfinite(o))
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
+
+
+def test_strong_decay_neumann():
+    w = WORKLOADS[4]
+    print(f"\n[case] full-size neumann {w.name} m={w.neumann_order} r={w.neumann_residual}", flush=True)
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    o_n, h_n = run_chunk(dev, w, solve="neumann")
+    o_e, _ = run_chunk(dev, w, solve="exact")
+    o_n, h_n, o_e = o_n.cpu().numpy(), h_n.cpu().numpy(), o_e.cpu().numpy()
+    units = [0, 9]
+    o_ref_n, h_ref_n = och.chunk_forward(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], chunk=w.chunk,
+                                         solve="neumann", order=w.neumann_order,
+                                         residual_steps=w.neumann_residual, units=units)
+    o_ref, _ = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], units=units)
+    e_parity = unit_err(o_n, o_ref_n, w, units)
+    e_vs_oracle = unit_err(o_n, o_ref, w, units)
+    e_vs_exact = rel_err(o_n, o_e)
+    e_oracle_trunc = unit_err(o_ref_n, o_ref, w, units)
+    print(f"  neumann GPU vs fp64 neumann chunk form: {e_parity:.3e}; GPU neumann vs exact recurrence: "
+          f"{e_vs_oracle:.3e}; fp64 neumann vs exact recurrence: {e_oracle_trunc:.3e}; "
+          f"GPU neumann vs GPU exact (all units): {e_vs_exact:.3e}", flush=True)
+    assert np.all(np.isfinite(o_n))
+    assert e_parity <= TOL[w.dtype]
+
+
+SMALL_KDA = Workload("inv_kda", 2, 640, 2, 4, 128, 64, 64, 128, "bf16", seed=31)
+
+
+def test_bitwise_determinism():
+    raw, _ = draw(SMALL_KDA)
+    dev = device_inputs(raw)
+    o1, h1 = run_chunk(dev, SMALL_KDA)
+    o2, h2 = run_chunk(dev, SMALL_KDA)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_resume_from_final_state_is_exact():
+    """Splitting the sequence at a chunk boundary and resuming from hT gives
+    bit-identical results (the state is carried in fp32 either way)."""
+    w = SMALL_KDA
+    raw, _ = draw(w)
+    dev = device_inputs(raw)
+    o, hT = run_chunk(dev, w)
+    cut = 5 * w.chunk
+    first = {n: t[:, :cut].contiguous() for n, t in dev.items()}
+    rest = {n: t[:, cut:].contiguous() for n, t in dev.items()}
+    oa, ha = run_chunk(first, w)
+    ob, hb = run_chunk(rest, w, h0=ha)
+    assert torch.equal(torch.cat([oa, ob], 1), o) and torch.equal(hb, hT)
+
+
+def test_resume_mid_chunk():
+    """Cutting inside a chunk changes the chunking but not the result."""
+    w = SMALL_KDA
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    cut = 5 * w.chunk + 17
+    first = {n: t[:, :cut].contiguous() for n, t in dev.items()}
+    rest = {n: t[:, cut:].contiguous() for n, t in dev.items()}
+    oa, ha = run_chunk(first, w)
+    ob, hb = run_chunk(rest, w, h0=ha)
+    o_ref, h_ref = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"])
+    assert rel_err(torch.cat([oa, ob], 1).cpu().numpy(), o_ref) <= TOL["bf16"]
+    assert rel_err(hb.cpu().numpy(), h_ref) <= TOL["bf16"]
+
+
+def test_gva_equals_replicated_heads():
+    w = Workload("inv_gva", 1, 300, 2, 8, 256, 64, 64, 4, "bf16", seed=32)
+    raw, _ = draw(w)
+    dev = device_inputs(raw)
+    o, hT = run_chunk(dev, w)
+    rep = {n: (t.repeat_interleave(4, dim=2) if n in ("q", "k", "log_alpha") else t) for n, t in dev.items()}
+    o2, h2 = run_chunk(rep, w)
+    assert torch.allclose(o, o2, rtol=0, atol=1e-6 * float(o.abs().max()))
+    assert torch.allclose(hT, h2, rtol=0, atol=1e-6 * float(hT.abs().max()))
+
+
+def test_chunk_sizes_agree():
+    """C = 64 and C = 128 give the same answer within the bar."""
+    w = SMALL_KDA
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    o64, _ = run_chunk(dev, w)
+    o128, _ = run_chunk(dev, w.with_(chunk=128))
+    assert rel_err(o64.cpu().numpy(), o128.cpu().numpy()) <= TOL["bf16"]
+
+
+def test_extreme_decay_is_finite():
+    """log alpha = -1e4 everywhere: each token sees an empty state, so
+    o_t = beta_t (q_t . k_t) v_t; nothing may overflow (no division by decay)."""
+    w = SMALL_KDA
+    raw, x = draw(w)
+    x["log_alpha"] = np.full_like(x["log_alpha"], -1e4)
+    raw["log_alpha"] = np.full_like(raw["log_alpha"], 0xC61C)   # bf16 bits of -9984
+    x["log_alpha"][:] = -9984.0
+    dev = device_inputs(raw)
+    o, hT = run_chunk(dev, w)
+    o = o.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT.cpu().numpy()))
+    o_ref, _ = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"])
+    assert rel_err(o, o_ref) <= TOL["bf16"]
+
+
+def test_empty_sequence_copies_state():
+    w = SMALL_KDA.with_(T=0)
+    dev = {n: to_torch(a) for n, a in draw(SMALL_KDA.with_(T=1))[0].items()}
+    dev = {n: t[:, :0].contiguous() for n, t in dev.items()}
+    h0 = torch.randn(w.B, w.H_v, w.d_k, w.d_v, device="cuda")
+    o, hT = gb.gdr_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], h0, chunk=64)
+    assert o.numel() == 0 and torch.equal(hT, h0)
+    _, hz = gb.gdr_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], None, chunk=64)
+    assert not hz.any()
+
+
+def test_recurrent_matches_chunk():
+    """Decode path and chunk path agree on the same tokens."""
+    w = SMALL_KDA.with_(T=130)
+    raw, _ = draw(w)
+    dev = device_inputs(raw)
+    o_c, h_c = run_chunk(dev, w)
+    state = torch.zeros(w.B, w.H_v, w.d_k, w.d_v, device="cuda")
+    o_r = gb.gdr_recurrent_step(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], state)
+    assert rel_err(o_c.cpu().numpy(), o_r.cpu().numpy()) <= TOL["bf16"]
+    assert rel_err(h_c.cpu().numpy(), state.cpu().numpy()) <= TOL["bf16"]
