@@ -56,6 +56,23 @@ __device__ __forceinline__ void ld8(const bf16 *p, float (&x)[8]) {
 __device__ __forceinline__ void st(float *p, float x) { *p = x; }
 __device__ __forceinline__ void st(bf16 *p, float x) { *p = to_bf16(x); }
 
+// In-chunk prefix sum of one decay column (Lambda_t = sum_{s<=t} log alpha_s,
+// the cumulative log-decay of Systolic Linear Attention, Table 2): loads all
+// C values first (independent loads in flight together), then accumulates.
+// Tokens at or past `valid` read as 0 (identity steps).  Writes out[t * ld].
+template <int C, typename TIn>
+__device__ __forceinline__ void lambda_column(const TIn *src, size_t stride, int valid, float *out, int ld) {
+  float x[C];
+#pragma unroll
+  for (int t = 0; t < C; ++t) x[t] = (t < valid) ? ldf(src + (size_t)t * stride) : 0.f;
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < C; ++t) {
+    acc += x[t];
+    out[t * ld] = acc;
+  }
+}
+
 // ----------------------------------------------------------------- fragments
 struct FragP {            // plain bf16
   bf16x8 h;
@@ -166,6 +183,17 @@ template <> struct OperandLds<PrecBF16> {
     *reinterpret_cast<bf16x4 *>(hi + n * ld + k) = h;
     *reinterpret_cast<bf16x4 *>(lo + n * ld + k) = l;
   }
+  // eight consecutive k for one n
+  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      h[r] = to_bf16(x[r]);
+      l[r] = to_bf16(x[r] - static_cast<float>(h[r]));
+    }
+    *reinterpret_cast<bf16x8 *>(hi + n * ld + k) = h;
+    *reinterpret_cast<bf16x8 *>(lo + n * ld + k) = l;
+  }
   __device__ __forceinline__ FragS get(int n, int k) const {
     FragS f;
     f.h = *reinterpret_cast<const bf16x8 *>(hi + n * ld + k);
@@ -185,6 +213,10 @@ template <> struct OperandLds<PrecF32> {
   __device__ __forceinline__ void put(int n, int k, float x) { v[n * ld + k] = x; }
   __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
     *reinterpret_cast<f32x4 *>(v + n * ld + k) = x;
+  }
+  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
+    *reinterpret_cast<float4 *>(v + n * ld + k) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(v + n * ld + k + 4) = make_float4(x[4], x[5], x[6], x[7]);
   }
   __device__ __forceinline__ FragF get(int n, int k) const {
     FragF f;

@@ -215,13 +215,8 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   const TIn *kp = reinterpret_cast<const TIn *>(a.k);
 
   // Lambda: in-chunk prefix sums of log alpha per decay group (padding: 0).
-  for (int g = tid; g < G; g += blockDim.x) {
-    float acc = 0.f;
-    for (int t = 0; t < C; ++t) {
-      if (t0 + t < T) acc += ldf(la + ((size_t)(b * T + t0 + t) * a.H_k + hk) * G + g);
-      lam[t * G + g] = acc;
-    }
-  }
+  for (int g = tid; g < G; g += blockDim.x)
+    lambda_column<C>(la + ((size_t)(b * T + t0) * a.H_k + hk) * G + g, (size_t)a.H_k * G, T - t0, lam + g, G);
   if (tid < NB) flags[tid] = 0;
   for (int i = tid; i < C * C; i += blockDim.x) gmat[i] = 0.f;
   __syncthreads();
