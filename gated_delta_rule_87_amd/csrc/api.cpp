@@ -72,6 +72,10 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
     }
     if (!(p->chunk == 64 || p->chunk == 128))
       return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: this build supports chunk in {64, 128}", p->chunk);
+    const int beta_heads_per_key = p->beta_per_key_head ? 1 : p->H_v / p->H_k;
+    if (p->chunk * beta_heads_per_key > 1024)
+      return fail(GDR_ERR_UNSUPPORTED, "chunk * (H_v / H_k) = %d: at most 1024 beta values per chunk",
+                  p->chunk * beta_heads_per_key);
     if (!gdr::prep_supported(p->chunk, p->d_k, p->gate_groups) ||
         gdr::scan_choose_bv(p->B, p->H_v, p->chunk, p->d_k, p->d_v, p->gate_groups, p->in_dtype == GDR_BF16) == 0)
       return fail(GDR_ERR_UNSUPPORTED, "chunk=%d d_k=%d G=%d exceeds the 160 KiB LDS budget", p->chunk, p->d_k,

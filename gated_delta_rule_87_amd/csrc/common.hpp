@@ -56,20 +56,57 @@ __device__ __forceinline__ void ld8(const bf16 *p, float (&x)[8]) {
 __device__ __forceinline__ void st(float *p, float x) { *p = x; }
 __device__ __forceinline__ void st(bf16 *p, float x) { *p = to_bf16(x); }
 
-// In-chunk prefix sum of one decay column (Lambda_t = sum_{s<=t} log alpha_s,
-// the cumulative log-decay of Systolic Linear Attention, Table 2): loads all
-// C values first (independent loads in flight together), then accumulates.
-// Tokens at or past `valid` read as 0 (identity steps).  Writes out[t * ld].
-template <int C, typename TIn>
-__device__ __forceinline__ void lambda_column(const TIn *src, size_t stride, int valid, float *out, int ld) {
-  float x[C];
+// --------------------------------------------------------------- raw loads
+// Eight consecutive input elements kept in registers until use.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void store(bf16 *p) const { *reinterpret_cast<uint4 *>(p) = v; }
+  __device__ __forceinline__ void to_float(float (&x)[8]) const {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int t = 0; t < C; ++t) x[t] = (t < valid) ? ldf(src + (size_t)t * stride) : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void store(float *p) const {
+    *reinterpret_cast<float4 *>(p) = a;
+    *reinterpret_cast<float4 *>(p + 4) = b;
+  }
+  __device__ __forceinline__ void to_float(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
+// In-place prefix sum over rows of one column of a row-major LDS matrix
+// (the cumulative log-decay Lambda_t = sum_{s<=t} log alpha_s of Systolic
+// Linear Attention, Table 2), 16 rows at a time so the reads of a block are
+// in flight together.
+template <int C>
+__device__ __forceinline__ void prefix_column(float *col, int ld) {
   float acc = 0.f;
 #pragma unroll
-  for (int t = 0; t < C; ++t) {
-    acc += x[t];
-    out[t * ld] = acc;
+  for (int t0 = 0; t0 < C; t0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = col[(t0 + t) * ld];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      acc += x[t];
+      col[(t0 + t) * ld] = acc;
+    }
   }
 }
 

@@ -32,28 +32,56 @@ namespace gdr {
 
 constexpr float kPivotRange = 64.f;  // exp(64) ~ 6e27 keeps every partial sum finite
 
+// LDS rows of the C x C matrices are padded to C + 4 floats, so the 16 rows a
+// column-strided fragment read touches fall into different banks.
+__host__ __device__ inline int prep_ld(int C) { return C + 4; }
 __host__ __device__ inline int prep_region0_floats(int C, int G) {
-  return (C * G > C * C) ? C * G : C * C;
+  return (C * G > C * prep_ld(C)) ? C * G : C * prep_ld(C);
 }
 __host__ __device__ inline int prep_tmp_floats(int C) {
-  return (C * C / 4 > C * 16) ? C * C / 4 : C * 16;
+  const int merge = C * (C / 2 + 4) / 2, neumann = C * 20;
+  return merge > neumann ? merge : neumann;
 }
 
 size_t prep_lds_bytes(int C, int G) {
   const int nb = C / 16;
-  return sizeof(float) * (size_t)(prep_region0_floats(C, G) + C * C + prep_tmp_floats(C) + C) +
+  return sizeof(float) * (size_t)(prep_region0_floats(C, G) + C * prep_ld(C) + prep_tmp_floats(C) + C) +
          sizeof(int) * (size_t)nb;
 }
 
 // --------------------------------------------------------------- fp32 tiles
-// acc += X[r0 + i, k] * Y[k, c0 + j] over k in [k0, k1) (multiple of 4), with
-// element accessors.  fp32 MFMA: lane l supplies X[i = l%16][k + l/16] and
-// Y[k + l/16][j = l%16].
-template <class FX, class FY>
-__device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, int k0, int k1) {
+// acc += X[i, k] * Y[k, j] for one 16x16 tile over k in [k0, k0 + 16 N)
+// (element accessors; fp32 MFMA, lane l supplies X[i = l%16][k + l/16] and
+// Y[k + l/16][j = l%16]).  The length is a template constant so the loop
+// unrolls and its LDS reads are issued ahead of the MFMAs.
+template <int N, class FX, class FY>
+__device__ __forceinline__ void tile_f32_n(f32x4 &acc, const FX &x, const FY &y, int k0) {
   const int l = lane_id();
   const int i = l & 15, kk = l >> 4;
-  for (int k = k0; k < k1; k += 4) acc = mfma_f32(x(i, k + kk), y(k + kk, i), acc);
+  float xa[4 * N], yb[4 * N];
+#pragma unroll
+  for (int u = 0; u < 4 * N; ++u) {
+    xa[u] = x(i, k0 + 4 * u + kk);
+    yb[u] = y(k0 + 4 * u + kk, i);
+  }
+#pragma unroll
+  for (int u = 0; u < 4 * N; ++u) acc = mfma_f32(xa[u], yb[u], acc);
+}
+
+// Same over [k0, k1), k1 - k0 a multiple of 16 up to 128.
+template <class FX, class FY>
+__device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, int k0, int k1) {
+  switch ((k1 - k0) >> 4) {
+    case 1: tile_f32_n<1>(acc, x, y, k0); break;
+    case 2: tile_f32_n<2>(acc, x, y, k0); break;
+    case 3: tile_f32_n<3>(acc, x, y, k0); break;
+    case 4: tile_f32_n<4>(acc, x, y, k0); break;
+    case 5: tile_f32_n<5>(acc, x, y, k0); break;
+    case 6: tile_f32_n<6>(acc, x, y, k0); break;
+    case 7: tile_f32_n<7>(acc, x, y, k0); break;
+    case 8: tile_f32_n<8>(acc, x, y, k0); break;
+    default: break;
+  }
 }
 
 // ------------------------------------------------------------- exact solve
@@ -63,38 +91,51 @@ __device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, i
 template <int C>
 __device__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
   constexpr int NB = C / 16;
+  constexpr int LD = C + 4;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  for (int i = tid; i < C * C; i += blockDim.x) amat[i] = 0.f;
+  for (int i = tid; i < C * LD; i += blockDim.x) amat[i] = 0.f;
   __syncthreads();
   if (tid < NB * 16) {
     const int base = 16 * (tid >> 4), cc = tid & 15;
-    float x[16];
+    float bl[16], x[16];
+#pragma unroll
+    for (int m = 0; m < 16; m += 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(bet + base + m);
+      bl[m] = v.x; bl[m + 1] = v.y; bl[m + 2] = v.z; bl[m + 3] = v.w;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      float row[16];
+#pragma unroll
+      for (int m = 0; m < 16; m += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(gmat + (base + i) * LD + base + m);
+        row[m] = v.x; row[m + 1] = v.y; row[m + 2] = v.z; row[m + 3] = v.w;
+      }
       float s = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) s -= gmat[(base + i) * C + base + m] * bet[base + m] * x[m];
+      for (int m = 0; m < i; ++m) s -= row[m] * bl[m] * x[m];
       x[i] = s;
-      amat[(base + i) * C + base + cc] = s;
+      amat[(base + i) * LD + base + cc] = s;
     }
   }
   __syncthreads();
   for (int bs = 16; bs < C; bs *= 2) {
     const int tpb = bs / 16;                  // tiles per block side
+    const int XLD = bs + 4;
     const int jobs = (C / (2 * bs)) * tpb * tpb;
-    // X_p = M[bot, top] * A[top, top] -> tmp (pair p at tmp + p * bs * bs)
+    // X_p = M[bot, top] * A[top, top] -> tmp (pair p at tmp + p * bs * XLD)
     for (int job = w; job < jobs; job += blockDim.x / kWave) {
       const int p = job / (tpb * tpb), ti = (job / tpb) % tpb, tj = job % tpb;
       const int top = 2 * bs * p, bot = top + bs;
       const int r0 = bot + 16 * ti, c0 = top + 16 * tj;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       tile_f32(acc,
-               [&](int i, int k) { return gmat[(r0 + i) * C + k] * bet[k]; },
-               [&](int k, int j) { return amat[k * C + c0 + j]; },
+               [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
+               [&](int k, int j) { return amat[k * LD + c0 + j]; },
                c0, top + bs);                 // A[top,top] is lower: rows k >= column
-      float *X = tmp + p * bs * bs;
+      float *X = tmp + p * bs * XLD;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) X[(16 * ti + 4 * (l >> 4) + r) * bs + 16 * tj + (l & 15)] = acc[r];
+      for (int r = 0; r < 4; ++r) X[(16 * ti + 4 * (l >> 4) + r) * XLD + 16 * tj + (l & 15)] = acc[r];
     }
     __syncthreads();
     // A[bot, top] = -A[bot, bot] * X_p
@@ -102,15 +143,15 @@ __device__ void solve_exact(const float *gmat, const float *bet, float *amat, fl
       const int p = job / (tpb * tpb), ti = (job / tpb) % tpb, tj = job % tpb;
       const int top = 2 * bs * p, bot = top + bs;
       const int r0 = bot + 16 * ti;
-      const float *X = tmp + p * bs * bs;
+      const float *X = tmp + p * bs * XLD;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       tile_f32(acc,
-               [&](int i, int k) { return amat[(r0 + i) * C + k]; },
-               [&](int k, int j) { return X[(k - bot) * bs + 16 * tj + j]; },
+               [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
+               [&](int k, int j) { return X[(k - bot) * XLD + 16 * tj + j]; },
                bot, r0 + 16);                 // A[bot,bot] is lower: columns k <= row
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        amat[(r0 + 4 * (l >> 4) + r) * C + top + 16 * tj + (l & 15)] = -acc[r];
+        amat[(r0 + 4 * (l >> 4) + r) * LD + top + 16 * tj + (l & 15)] = -acc[r];
     }
     __syncthreads();
   }
@@ -126,12 +167,14 @@ template <int C>
 __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, float *tmp, int order,
                               int residual) {
   constexpr int NB = C / 16;
+  constexpr int LD = C + 4;
+  constexpr int TLD = 20;                     // tmp rows: one 16-column block, padded
   constexpr int kMaxTiles = (NB + 3) / 4;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int nw = blockDim.x / kWave;
-  for (int i = tid; i < C * C; i += blockDim.x) amat[i] = ((i / C) == (i % C)) ? 1.f : 0.f;
+  for (int i = tid; i < C * LD; i += blockDim.x) amat[i] = ((i / LD) == (i % LD)) ? 1.f : 0.f;
   __syncthreads();
-  auto Mx = [&](int i, int k, int r0) { return gmat[(r0 + i) * C + k] * bet[k]; };
+  auto Mx = [&](int i, int k, int r0) { return gmat[(r0 + i) * LD + k] * bet[k]; };
   for (int it = 0; it < order; ++it) {
     for (int J = 0; J < NB; ++J) {
       f32x4 acc[kMaxTiles];
@@ -140,7 +183,7 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int r0 = 16 * I;
         tile_f32(acc[nt], [&](int i, int k) { return Mx(i, k, r0); },
-                 [&](int k, int j) { return amat[k * C + 16 * J + j]; }, 16 * J, r0 + 16);
+                 [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, r0 + 16);
       }
       __syncthreads();
       nt = 0;
@@ -148,7 +191,7 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          amat[row * C + col] = ((row == col) ? 1.f : 0.f) - acc[nt][r];
+          amat[row * LD + col] = ((row == col) ? 1.f : 0.f) - acc[nt][r];
         }
       }
       __syncthreads();
@@ -156,16 +199,16 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
   }
   for (int it = 0; it < residual; ++it) {
     for (int J = 0; J < NB; ++J) {
-      // Rm[:, J] = I - X[:, J] - (M X)[:, J] -> tmp[row * 16 + col - 16J]
+      // Rm[:, J] = I - X[:, J] - (M X)[:, J] -> tmp[row * TLD + col - 16J]
       for (int I = J + w; I < NB; I += nw) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const int r0 = 16 * I;
         tile_f32(acc, [&](int i, int k) { return Mx(i, k, r0); },
-                 [&](int k, int j) { return amat[k * C + 16 * J + j]; }, 16 * J, r0 + 16);
+                 [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, r0 + 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          tmp[row * 16 + (l & 15)] = ((row == col) ? 1.f : 0.f) - amat[row * C + col] - acc[r];
+          tmp[row * TLD + (l & 15)] = ((row == col) ? 1.f : 0.f) - amat[row * LD + col] - acc[r];
         }
       }
       __syncthreads();
@@ -174,8 +217,8 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
       for (int I = J + w; I < NB; I += nw, ++nt) {
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int r0 = 16 * I;
-        tile_f32(acc[nt], [&](int i, int k) { return amat[(r0 + i) * C + k]; },
-                 [&](int k, int j) { return tmp[k * 16 + j]; }, 16 * J, r0 + 16);
+        tile_f32(acc[nt], [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
+                 [&](int k, int j) { return tmp[k * TLD + j]; }, 16 * J, r0 + 16);
       }
       __syncthreads();
       nt = 0;
@@ -183,7 +226,7 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          amat[row * C + col] += acc[nt][r];
+          amat[row * LD + col] += acc[nt][r];
         }
       }
       __syncthreads();
@@ -192,9 +235,15 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
 }
 
 // ------------------------------------------------------------------ kernel
+// Loads are unconditional (tokens past T read a clamped, valid address and
+// are zeroed where used): a load behind a branch forces an early wait for
+// every memory operation in flight.
 template <typename TIn, class P, int C, int DK>
 __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   constexpr int NB = C / 16;
+  constexpr int NPAIR = NB * (NB + 1) / 2;
+  constexpr int NKV = C * DK / (8 * 256);   // bound on 8-element log-alpha vectors per thread
+  constexpr int KS = DK / 32;
   using Split = typename P::Split;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float *smem = reinterpret_cast<float *>(smem_raw);
@@ -202,27 +251,101 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   const int G = a.G, gs = a.gshift, T = a.T;
   const int t0 = c * C;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int lr = l & 15, lq = l >> 4;
+  const int lgG = __builtin_ctz(DK) - gs;
+  const int Rb = a.H_beta / a.H_k;
 
   float *lam = smem;                                   // [C][G] (Gram phase)
-  float *amat = smem;                                  // [C][C] (solve phase, aliases lam)
-  float *gmat = smem + prep_region0_floats(C, G);      // [C][C]
-  float *tmp = gmat + C * C;
+  float *amat = smem;                                  // [C][C + 4] (solve phase, aliases lam)
+  float *gmat = smem + prep_region0_floats(C, G);      // [C][C + 4]
+  float *tmp = gmat + C * prep_ld(C);
   float *bet = tmp + prep_tmp_floats(C);               // [C]
   int *flags = reinterpret_cast<int *>(bet + C);       // [NB]
 
   const TIn *la = reinterpret_cast<const TIn *>(a.log_alpha);
   const TIn *qp = reinterpret_cast<const TIn *>(a.q);
   const TIn *kp = reinterpret_cast<const TIn *>(a.k);
+  const TIn *bp = reinterpret_cast<const TIn *>(a.beta);
+  const size_t row_stride = (size_t)a.H_k * DK;        // token stride of q, k
+  const size_t la_row = (size_t)a.H_k * G;
+  auto tok = [&](int t) { return (size_t)b * T + min(t0 + t, T - 1); };
 
-  // Lambda: in-chunk prefix sums of log alpha per decay group (padding: 0).
-  for (int g = tid; g < G; g += blockDim.x)
-    lambda_column<C>(la + ((size_t)(b * T + t0) * a.H_k + hk) * G + g, (size_t)a.H_k * G, T - t0, lam + g, G);
+  // ---- all loads of the chunk's key side, issued together
+  Raw8<TIn> lav[NKV];
+  TIn las[NKV];
+  const bool la_vec = G >= 8;
+  if (la_vec) {
+#pragma unroll
+    for (int j = 0; j < NKV; ++j) {
+      const int e = min(8 * (tid + 256 * j), C * G - 8);
+      lav[j].load(la + tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1)));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NKV; ++j) {
+      const int e = min(tid + 256 * j, C * G - 1);
+      las[j] = la[tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1))];
+    }
+  }
+  constexpr int NBET = 4;                              // up to 4 * 256 beta values (C * Rb)
+  TIn bets[NBET];
+#pragma unroll
+  for (int j = 0; j < NBET; ++j) {
+    const int e = min(tid + 256 * j, C * Rb - 1);      // e = rb * C + t
+    bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
+  }
+  // first Gram pair's operands
+  auto pair_of = [&](int pi, int &I, int &J) __attribute__((always_inline)) {
+    I = 0;
+    while ((I + 1) * (I + 2) / 2 <= pi) ++I;
+    J = pi - I * (I + 1) / 2;
+  };
+  const TIn *kbase = kp + (size_t)hk * DK;
+  const TIn *qbase = qp + (size_t)hk * DK;
+  Raw8<TIn> kt[KS], qt[KS], kj[KS];
+  auto load_pair = [&](int pi) __attribute__((always_inline)) {
+    int I, J;
+    pair_of(min(pi, NPAIR - 1), I, J);
+    const size_t rt = tok(16 * I + lr) * row_stride, rj = tok(16 * J + lr) * row_stride;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kt[s].load(kbase + rt + 32 * s + 8 * lq);
+      qt[s].load(qbase + rt + 32 * s + 8 * lq);
+      kj[s].load(kbase + rj + 32 * s + 8 * lq);
+    }
+  };
+  load_pair(w);
+
+  // ---- Lambda: raw log alpha -> lam, then in-place prefix sum per column
+  if (la_vec) {
+#pragma unroll
+    for (int j = 0; j < NKV; ++j) {
+      const int e = 8 * (tid + 256 * j);
+      if (e < C * G) {
+        const int t = e >> lgG, g = e & (G - 1);
+        float x[8];
+        lav[j].to_float(x);
+        const float keep = (t0 + t < T) ? 1.f : 0.f;
+        *reinterpret_cast<float4 *>(lam + t * G + g) = make_float4(x[0] * keep, x[1] * keep, x[2] * keep, x[3] * keep);
+        *reinterpret_cast<float4 *>(lam + t * G + g + 4) = make_float4(x[4] * keep, x[5] * keep, x[6] * keep, x[7] * keep);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NKV; ++j) {
+      const int e = tid + 256 * j;
+      if (e < C * G) lam[e] = (t0 + (e >> lgG) < T) ? static_cast<float>(las[j]) : 0.f;
+    }
+  }
   if (tid < NB) flags[tid] = 0;
-  for (int i = tid; i < C * C; i += blockDim.x) gmat[i] = 0.f;
+  for (int i = tid; i < C * (C + 4); i += blockDim.x) gmat[i] = 0.f;
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
   __syncthreads();
   for (int idx = tid; idx < NB * G; idx += blockDim.x) {
     const int I = idx / G, g = idx - I * G;
     float lo = lam[(16 * I) * G + g], hi = lo;
+#pragma unroll
     for (int r = 1; r < 16; ++r) {
       const float x = lam[(16 * I + r) * G + g];
       lo = fminf(lo, x);
@@ -232,45 +355,58 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
-  // Gram G_c (beta-free, strictly lower) and L_c (lower incl. diagonal).
+  // Lambda of row t for eight consecutive channels (vector reads per channel,
+  // one broadcast read when the eight share a decay group)
+  auto lam8 = [&](int t, int ch0, float (&x)[8]) __attribute__((always_inline)) {
+    if (gs == 0) {
+      const float4 u = *reinterpret_cast<const float4 *>(lam + t * G + ch0);
+      const float4 v = *reinterpret_cast<const float4 *>(lam + t * G + ch0 + 4);
+      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else if (gs >= 3) {
+      const float u = lam[t * G + (ch0 >> gs)];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = u;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = lam[t * G + ((ch0 + e) >> gs)];
+    }
+  };
+
+  // ---- Gram G_c (beta-free, strictly lower) and L_c (lower incl. diagonal)
   float *Lout = a.L_ws + (((size_t)b * a.H_k + hk) * a.N_c + c) * (size_t)(C * C);
-  const size_t row_stride = (size_t)a.H_k * DK;
-  const TIn *kbase = kp + ((size_t)(b * T + t0) * a.H_k + hk) * DK;
-  const TIn *qbase = qp + ((size_t)(b * T + t0) * a.H_k + hk) * DK;
-  for (int pi = w; pi < NB * (NB + 1) / 2; pi += blockDim.x / kWave) {
-    int I = 0;
-    while ((I + 1) * (I + 2) / 2 <= pi) ++I;
-    const int J = pi - I * (I + 1) / 2;
+  for (int pi = w; pi < NPAIR; pi += blockDim.x / kWave) {
+    int I, J;
+    pair_of(pi, I, J);
+    Raw8<TIn> ckt[KS], cqt[KS], ckj[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      ckt[s] = kt[s];
+      cqt[s] = qt[s];
+      ckj[s] = kj[s];
+    }
+    load_pair(pi + blockDim.x / kWave);                  // next pair of this wave (clamped)
     f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
+    const int tr = 16 * I + lr, jr = 16 * J + lr, piv = 16 * I;
+    const float mt = (t0 + tr < T) ? 1.f : 0.f, mj = (t0 + jr < T) ? 1.f : 0.f;
     if (!(I == J && flags[I])) {
-      const int tr = 16 * I + (l & 15), jr = 16 * J + (l & 15), piv = 16 * I;
-      const bool vt = t0 + tr < T, vj = t0 + jr < T;
-      for (int s = 0; s < DK / 32; ++s) {
-        const int ch0 = 32 * s + 8 * (l >> 4);
-        float kt[8], qt[8], kj[8];
-        if (vt) {
-          ld8(kbase + tr * row_stride + ch0, kt);
-          ld8(qbase + tr * row_stride + ch0, qt);
-        } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kt[e] = qt[e] = 0.f;
-        }
-        if (vj) {
-          ld8(kbase + jr * row_stride + ch0, kj);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kj[e] = 0.f;
-        }
+      for (int s = 0; s < KS; ++s) {
+        const int ch0 = 32 * s + 8 * lq;
         float xk[8], xq[8], xj[8];
+        ckt[s].to_float(xk);
+        cqt[s].to_float(xq);
+        ckj[s].to_float(xj);
+        float lp[8], lt[8], lj[8];
+        lam8(piv, ch0, lp);
+        lam8(tr, ch0, lt);
+        lam8(jr, ch0, lj);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int g = (ch0 + e) >> gs;
-          const float lp = lam[piv * G + g];
-          const float ea = __expf(lam[tr * G + g] - lp);
-          const float eb = __expf(lp - lam[jr * G + g]);
-          xk[e] = kt[e] * ea;
-          xq[e] = qt[e] * ea;
-          xj[e] = kj[e] * eb;
+          const float ea = __expf(lt[e] - lp[e]) * mt;
+          const float eb = __expf(lp[e] - lj[e]) * mj;
+          xk[e] *= ea;
+          xq[e] *= ea;
+          xj[e] *= eb;
         }
         const Split fk = make_frag<Split>(xk), fq = make_frag<Split>(xq), fj = make_frag<Split>(xj);
         mma(accG, fk, fj);
@@ -281,15 +417,16 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       // entry by its definition, causal mask before the exponential.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
+        const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
         float sg = 0.f, sl = 0.f;
         if (row >= col && t0 + row < T) {
+          const size_t rrow = tok(row) * row_stride, rcol = tok(col) * row_stride;
           for (int ch = 0; ch < DK; ++ch) {
             const int g = ch >> gs;
             const float d = __expf(lam[row * G + g] - lam[col * G + g]);
-            const float kc = ldf(kbase + col * row_stride + ch);
-            sg += ldf(kbase + row * row_stride + ch) * kc * d;
-            sl += ldf(qbase + row * row_stride + ch) * kc * d;
+            const float kc = static_cast<float>(kbase[rcol + ch]);
+            sg += static_cast<float>(kbase[rrow + ch]) * kc * d;
+            sl += static_cast<float>(qbase[rrow + ch]) * kc * d;
           }
         }
         accG[r] = sg;
@@ -298,8 +435,8 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-      gmat[row * C + col] = (I > J || row > col) ? accG[r] : 0.f;
+      const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
+      gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[r] : 0.f;
       Lout[row * C + col] = (I > J || row >= col) ? accL[r] : 0.f;
     }
   }
@@ -307,14 +444,14 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     if ((i / C) / 16 < (i % C) / 16) Lout[i] = 0.f;   // blocks above the diagonal
   }
 
-  // Solve per beta head.
-  const int Rb = a.H_beta / a.H_k;
+  // ---- solve per beta head
   for (int rb = 0; rb < Rb; ++rb) {
     const int hb = hk * Rb + rb;
     __syncthreads();
-    for (int t = tid; t < C; t += blockDim.x) {
-      bet[t] = (t0 + t < T) ? ldf(reinterpret_cast<const TIn *>(a.beta) + (size_t)(b * T + t0 + t) * a.H_beta + hb)
-                            : 0.f;
+#pragma unroll
+    for (int j = 0; j < NBET; ++j) {
+      const int e = tid + 256 * j;
+      if (e / C == rb && e < C * Rb) bet[e % C] = (t0 + e % C < T) ? static_cast<float>(bets[j]) : 0.f;
     }
     __syncthreads();
     if (a.solve == 0) {
@@ -325,7 +462,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     __syncthreads();
     float *Aout = a.A_ws + (((size_t)b * a.H_beta + hb) * a.N_c + c) * (size_t)(C * C);
     for (int i = 4 * tid; i < C * C; i += 4 * blockDim.x) {
-      *reinterpret_cast<float4 *>(Aout + i) = *reinterpret_cast<const float4 *>(amat + i);
+      *reinterpret_cast<float4 *>(Aout + i) = *reinterpret_cast<const float4 *>(amat + (i / C) * (C + 4) + i % C);
     }
   }
 }

@@ -37,40 +37,6 @@
 
 namespace gdr {
 
-// --------------------------------------------------------------- raw loads
-// Eight consecutive input elements kept in registers until use.
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16> {
-  uint4 v;
-  __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const uint4 *>(p); }
-  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
-  __device__ __forceinline__ void store(bf16 *p) const { *reinterpret_cast<uint4 *>(p) = v; }
-  __device__ __forceinline__ void to_float(float (&x)[8]) const {
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(u[i] << 16);
-      x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-    }
-  }
-};
-template <> struct Raw8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float *p) {
-    a = *reinterpret_cast<const float4 *>(p);
-    b = *reinterpret_cast<const float4 *>(p + 4);
-  }
-  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
-  __device__ __forceinline__ void store(float *p) const {
-    *reinterpret_cast<float4 *>(p) = a;
-    *reinterpret_cast<float4 *>(p + 4) = b;
-  }
-  __device__ __forceinline__ void to_float(float (&x)[8]) const {
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-};
-
 // ------------------------------------------------------------- LDS layout
 template <int C, int DK, int BV, typename TIn>
 struct ScanLayout {
@@ -253,23 +219,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ChunkArgs a) {
       for (int s = 0; s < MAX_AS; ++s) ld8(M + (16 * I + lr) * C + 32 * s + 8 * lq, dst[rb][s]);
     }
   };
-  // In-place prefix sum over the chunk's rows of each decay column of lam,
-  // 16 rows at a time (reads of a block issued together).
   auto lambda_prefix = [&]() __attribute__((always_inline)) {
-    for (int g = tid; g < G; g += blockDim.x) {
-      float acc = 0.f;
-#pragma unroll
-      for (int t0_ = 0; t0_ < C; t0_ += 16) {
-        float x[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) x[t] = lam[(t0_ + t) * LAM_LD + g];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          acc += x[t];
-          lam[(t0_ + t) * LAM_LD + g] = acc;
-        }
-      }
-    }
+    for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, LAM_LD);
   };
   // exp(Lambda_t) for eight consecutive channels of row t
   auto decay8 = [&](int t, int ch0, float (&d)[8]) {
