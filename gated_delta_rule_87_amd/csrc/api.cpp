@@ -76,6 +76,9 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
     if (p->chunk * beta_heads_per_key > 1024)
       return fail(GDR_ERR_UNSUPPORTED, "chunk * (H_v / H_k) = %d: at most 1024 beta values per chunk",
                   p->chunk * beta_heads_per_key);
+    if (p->gate_groups != p->d_k && p->gate_groups > 8)
+      return fail(GDR_ERR_UNSUPPORTED, "G=%d: gates must be per channel (G = d_k = %d) or in at most 8 groups",
+                  p->gate_groups, p->d_k);
     if (!gdr::prep_supported(p->chunk, p->d_k, p->gate_groups) ||
         gdr::scan_choose_bv(p->B, p->H_v, p->chunk, p->d_k, p->d_v, p->gate_groups, p->in_dtype == GDR_BF16) == 0)
       return fail(GDR_ERR_UNSUPPORTED, "chunk=%d d_k=%d G=%d exceeds the 160 KiB LDS budget", p->chunk, p->d_k,

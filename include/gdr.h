@@ -104,7 +104,8 @@ size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p);
  *               bytes, 256-byte aligned; its contents on return are the A_c
  *               and L_c of every chunk in the layout documented there.
  * Supported here: in_dtype bf16 or f32, chunk 64 or 128, d_k in {64,128,256},
- * d_v a multiple of 16, G a divisor of d_k; beyond that GDR_ERR_UNSUPPORTED.
+ * d_v a multiple of 16, G = d_k (per-channel gates) or a divisor of d_k no
+ * larger than 8 (grouped gates); beyond that GDR_ERR_UNSUPPORTED.
  */
 gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v,
                          const void *beta, const void *log_alpha, const float *h0, void *o,

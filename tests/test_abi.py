@@ -97,6 +97,8 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, la=FAKE, h0=None, o=FAKE, hT=
     (dict(chunk=48), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=32), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=128, d_k=256, gate_groups=256), gb.GDR_ERR_UNSUPPORTED),
+    (dict(gate_groups=16), gb.GDR_ERR_UNSUPPORTED),
+    (dict(d_k=256, gate_groups=32), gb.GDR_ERR_UNSUPPORTED),
     (dict(B=1 << 20, T=1 << 20), gb.GDR_ERR_INVALID_ARG),
 ])
 def test_invalid_problems(kw, status):
