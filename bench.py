@@ -39,7 +39,13 @@ def source_sha(kernel):
 
 
 def work_model(w):
-    """Algorithmic FLOPs and bytes per kernel ("Roofline")."""
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel (see the design doc,
+    "Roofline").  prep: Gram and L (2 C d_k per key-head token, causal halves)
+    and the solve (C^2/3 per value-head token); it must read the key side (q, k,
+    beta, log alpha) once.  scan: W/U, L E and the three state products per
+    value-head token; it must read v and write o (fp32) and hT once.  The
+    workspace that carries prepared chunks from prep to scan is not
+    algorithmic traffic: it shows up in the measured ``traffic``."""
     C, dk, dv = w.chunk, w.d_k, w.d_v
     R = w.H_v // w.H_k
     token_heads = w.B * w.T * w.H_v
@@ -47,9 +53,8 @@ def work_model(w):
     flops_prep = token_heads * (2.0 * C * dk / R + C * C / 3.0)
     flops_scan = token_heads * ((C + 1.0) * (dk + 2.0 * dv) + 6.0 * dk * dv)
     bt = w.B * w.T
-    key_side = es * bt * (2 * w.H_k * dk + w.H_k * w.G + w.H_beta)   # q, k, log_alpha, beta
-    bytes_prep = key_side
-    bytes_scan = key_side + es * bt * w.H_v * dv + 4 * bt * w.H_v * dv + 4 * w.B * w.H_v * dk * dv
+    bytes_prep = es * bt * (2 * w.H_k * dk + w.H_k * w.G + w.H_beta)     # q, k, log_alpha, beta
+    bytes_scan = es * bt * w.H_v * dv + 4 * bt * w.H_v * dv + 4 * w.B * w.H_v * dk * dv   # v, o, hT
     return {"prep": (flops_prep, bytes_prep), "scan": (flops_scan, bytes_scan)}
 
 
@@ -202,8 +207,7 @@ def main():
     dom = "scan" if scan_ms >= prep_ms else "prep"
     dom_ms = scan_ms if dom == "scan" else prep_ms
     f_dom, b_dom = model[dom]
-    path_bytes = model["scan"][1]
-    hbm_bound = path_bytes / (HBM_PEAK_GBS * 1e9) >= flops_total / (MFMA_PEAK_TFS[dtype] * 1e12)
+    hbm_bound = b_dom / (HBM_PEAK_GBS * 1e9) >= f_dom / (MFMA_PEAK_TFS[dtype] * 1e12)
     if hbm_bound:
         achieved = b_dom / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -17,8 +17,10 @@ GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP
 GDR_F32, GDR_BF16 = 0, 1
 GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
 
-EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_prepare", "gdr_chunk_scan",
-           "gdr_recurrent_step", "gdr_status_string", "gdr_last_error")
+EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_workspace_layout", "gdr_chunk_prepare",
+           "gdr_chunk_scan", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error")
+# Workspace regions, in order (include/gdr.h, gdr_chunk_fwd_workspace_size).
+WS_REGIONS = ("A", "L", "KB", "QB", "KH", "GM")
 
 
 class GdrProblem(ctypes.Structure):
@@ -50,7 +52,9 @@ def load():
         lib.gdr_chunk_fwd.restype = ctypes.c_int
         lib.gdr_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.gdr_chunk_scan.restype = ctypes.c_int
-        lib.gdr_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_workspace_layout.restype = ctypes.c_int
+        lib.gdr_chunk_workspace_layout.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_prepare.restype = ctypes.c_int
         lib.gdr_chunk_prepare.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
@@ -143,6 +147,15 @@ def gdr_chunk_fwd_workspace_size(problem):
     return int(load().gdr_chunk_fwd_workspace_size(ctypes.byref(problem)))
 
 
+def gdr_chunk_workspace_layout(problem):
+    """{region name: byte offset} for the six workspace regions, plus "total"."""
+    out = (ctypes.c_size_t * 7)()
+    _check(load().gdr_chunk_workspace_layout(ctypes.byref(problem), out))
+    d = dict(zip(WS_REGIONS, (int(x) for x in out[:6])))
+    d["total"] = int(out[6])
+    return d
+
+
 def _chunk_call(entry, q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order, neumann_residual_steps,
                 out_dtype, o, hT, return_final_state, workspace, stream):
     lib = load()
@@ -157,16 +170,19 @@ def _chunk_call(entry, q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order
         hT = torch.empty(state_shape, dtype=torch.float32, device=dev)
     ws_bytes = gdr_chunk_fwd_workspace_size(p)
     if ws_bytes == 0 and p.B * p.T > 0:
-        _check(getattr(lib, entry)(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None))
+        _check(lib.gdr_chunk_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None))
     if workspace is None:
         if entry == "gdr_chunk_scan":
             raise ValueError("gdr_chunk_scan needs the workspace gdr_chunk_prepare filled")
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    _check(getattr(lib, entry)(
-        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"),
-        _ptr(log_alpha, "log_alpha"), _ptr(h0, "h0", torch.float32, state_shape),
-        _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _ptr(hT, "hT", torch.float32, state_shape),
-        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    h0p, hTp = _ptr(h0, "h0", torch.float32, state_shape), _ptr(hT, "hT", torch.float32, state_shape)
+    op = _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v))
+    wsp, wsn = _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    if entry == "gdr_chunk_scan":
+        _check(lib.gdr_chunk_scan(ctypes.byref(p), _ptr(v, "v"), h0p, op, hTp, wsp, wsn, _stream(stream)))
+    else:
+        _check(lib.gdr_chunk_fwd(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"),
+                                 _ptr(log_alpha, "log_alpha"), h0p, op, hTp, wsp, wsn, _stream(stream)))
     return o, hT
 
 
@@ -176,7 +192,7 @@ def gdr_chunk_fwd(q, k, v, beta, log_alpha, h0=None, *, chunk=64, solve="exact",
     """Chunkwise forward.  Returns (o [B,T,H_v,d_v], hT [B,H_v,d_k,d_v] fp32 or None).
 
     ``workspace`` (a GPU tensor) may be passed to avoid an allocation; on
-    return it holds A_c and L_c (see gdr_chunk_fwd_workspace_size)."""
+    return it holds the prepared chunk quantities (gdr_chunk_workspace_layout)."""
     return _chunk_call("gdr_chunk_fwd", q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order,
                        neumann_residual_steps, out_dtype, o, hT, return_final_state, workspace, stream)
 
@@ -184,15 +200,18 @@ def gdr_chunk_fwd(q, k, v, beta, log_alpha, h0=None, *, chunk=64, solve="exact",
 def gdr_chunk_scan(q, k, v, beta, log_alpha, h0=None, *, workspace, chunk=64, solve="exact", neumann_order=4,
                    neumann_residual_steps=1, out_dtype=torch.float32, o=None, hT=None,
                    return_final_state=True, stream=None):
-    """State scan and output over a workspace filled by gdr_chunk_prepare."""
+    """State scan and output over a workspace filled by gdr_chunk_prepare.  The
+    tensors q, k, beta and log_alpha only describe the problem (shapes and
+    dtype); the library reads v, h0 and the workspace."""
     return _chunk_call("gdr_chunk_scan", q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order,
                        neumann_residual_steps, out_dtype, o, hT, return_final_state, workspace, stream)
 
 
 def gdr_chunk_prepare(q, k, beta, log_alpha, *, chunk=64, solve="exact", neumann_order=4,
                       neumann_residual_steps=1, H_v=None, workspace=None, stream=None):
-    """Per-chunk matrices only.  Returns (A [B,H_beta,N_c,C,C], L [B,H_k,N_c,C,C]) fp32,
-    views into ``workspace`` (allocated if not given; a float32 GPU tensor)."""
+    """The parallel half of the chunk forward.  Returns (workspace, problem):
+    ``workspace`` (allocated as uint8 if not given) holds the prepared chunk
+    quantities laid out as gdr_chunk_workspace_layout(problem) gives."""
     lib = load()
     B, T, Hk, dk = q.shape
     Hv = beta.shape[2] if H_v is None else H_v
@@ -201,18 +220,12 @@ def gdr_chunk_prepare(q, k, beta, log_alpha, *, chunk=64, solve="exact", neumann
     p = make_problem(q, fake_v, log_alpha, beta, chunk=chunk, solve=solve, neumann_order=neumann_order,
                      neumann_residual_steps=neumann_residual_steps)
     ws_bytes = gdr_chunk_fwd_workspace_size(p)
-    nc = (T + chunk - 1) // chunk
-    Hb = Hk if p.beta_per_key_head else Hv
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 256) // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     _check(lib.gdr_chunk_prepare(ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(beta, "beta"),
                                  _ptr(log_alpha, "log_alpha"), _ptr(workspace, "workspace"),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
-    ws = workspace.view(torch.float32) if workspace.dtype != torch.float32 else workspace
-    nA = B * Hb * nc * chunk * chunk
-    A = ws[:nA].view(B, Hb, nc, chunk, chunk)
-    L = ws[nA:nA + B * Hk * nc * chunk * chunk].view(B, Hk, nc, chunk, chunk)
-    return A, L
+    return workspace, p
 
 
 def gdr_recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None, stream=None):

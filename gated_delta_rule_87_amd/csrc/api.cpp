@@ -76,11 +76,8 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
     if (p->chunk * beta_heads_per_key > 1024)
       return fail(GDR_ERR_UNSUPPORTED, "chunk * (H_v / H_k) = %d: at most 1024 beta values per chunk",
                   p->chunk * beta_heads_per_key);
-    if (p->gate_groups != p->d_k && p->gate_groups > 8)
-      return fail(GDR_ERR_UNSUPPORTED, "G=%d: gates must be per channel (G = d_k = %d) or in at most 8 groups",
-                  p->gate_groups, p->d_k);
     if (!gdr::prep_supported(p->chunk, p->d_k, p->gate_groups) ||
-        gdr::scan_choose_bv(p->B, p->H_v, p->chunk, p->d_k, p->d_v, p->gate_groups, p->in_dtype == GDR_BF16) == 0)
+        gdr::scan_choose_bv(p->B, p->H_v, p->chunk, p->d_k, p->d_v, p->in_dtype == GDR_BF16) == 0)
       return fail(GDR_ERR_UNSUPPORTED, "chunk=%d d_k=%d G=%d exceeds the 160 KiB LDS budget", p->chunk, p->d_k,
                   p->gate_groups);
   }
@@ -96,11 +93,13 @@ gdr_status check_ptr(const void *ptr, const char *name, bool required, uintptr_t
   return GDR_OK;
 }
 
-size_t ws_bytes(const gdr_problem *p) {
-  const size_t nc = ((size_t)p->T + p->chunk - 1) / p->chunk;
-  const size_t hb = p->beta_per_key_head ? p->H_k : p->H_v;
-  return sizeof(float) * (size_t)p->chunk * p->chunk * nc * p->B * (hb + p->H_k);
+gdr::WsLayout layout_of(const gdr_problem *p) {
+  const int nc = (int)(((size_t)p->T + p->chunk - 1) / p->chunk);
+  const int hb = p->beta_per_key_head ? p->H_k : p->H_v;
+  return gdr::ws_layout(p->B, p->H_k, hb, nc, p->chunk, p->d_k, p->in_dtype == GDR_BF16);
 }
+
+size_t ws_bytes(const gdr_problem *p) { return layout_of(p).total; }
 
 gdr::ChunkArgs make_chunk_args(const gdr_problem *p, void *workspace) {
   gdr::ChunkArgs a{};
@@ -119,8 +118,8 @@ gdr::ChunkArgs make_chunk_args(const gdr_problem *p, void *workspace) {
   a.solve = p->solve;
   a.order = p->neumann_order;
   a.residual = p->neumann_residual_steps;
-  a.A_ws = static_cast<float *>(workspace);
-  a.L_ws = a.A_ws + (size_t)p->chunk * p->chunk * a.N_c * p->B * a.H_beta;
+  a.ws = static_cast<unsigned char *>(workspace);
+  a.wl = layout_of(p);
   return a;
 }
 
@@ -136,6 +135,16 @@ extern "C" {
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p) {
   if (check_problem(p, true) != GDR_OK) return 0;
   return ws_bytes(p);
+}
+
+gdr_status gdr_chunk_workspace_layout(const gdr_problem *p, size_t *offsets) {
+  gdr_status s = check_problem(p, true);
+  if (s != GDR_OK) return s;
+  if (!offsets) return fail(GDR_ERR_INVALID_ARG, "offsets is NULL");
+  const gdr::WsLayout w = layout_of(p);
+  for (int r = 0; r < 6; ++r) offsets[r] = w.off[r];
+  offsets[6] = w.total;
+  return GDR_OK;
 }
 
 gdr_status gdr_chunk_prepare(const gdr_problem *p, const void *q, const void *k, const void *beta,
@@ -177,8 +186,8 @@ gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, con
     a.hT = hT;
     return launched(gdr::launch_scan(a, in_bf16, out_bf16, st), "scan kernel");
   }
-  if ((s = check_ptr(q, "q", true)) || (s = check_ptr(k, "k", true)) || (s = check_ptr(v, "v", true)) ||
-      (s = check_ptr(beta, "beta", true)) || (s = check_ptr(log_alpha, "log_alpha", true)) ||
+  if ((s = check_ptr(q, "q", prepare)) || (s = check_ptr(k, "k", prepare)) || (s = check_ptr(v, "v", true)) ||
+      (s = check_ptr(beta, "beta", prepare)) || (s = check_ptr(log_alpha, "log_alpha", prepare)) ||
       (s = check_ptr(o, "o", true)) || (s = check_ptr(workspace, "workspace", true, 256)))
     return s;
   if (workspace_bytes < ws_bytes(p))
@@ -204,10 +213,10 @@ gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, con
   return chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true);
 }
 
-gdr_status gdr_chunk_scan(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
-                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
-                          size_t workspace_bytes, void *stream) {
-  return chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, false);
+gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, void *o, float *hT,
+                          const void *workspace, size_t workspace_bytes, void *stream) {
+  return chunk_forward(p, nullptr, nullptr, v, nullptr, nullptr, h0, o, hT, workspace, workspace_bytes, stream,
+                       false);
 }
 
 gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,

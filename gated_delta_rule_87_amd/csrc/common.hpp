@@ -232,6 +232,17 @@ template <> struct OperandLds<PrecBF16> {
     *reinterpret_cast<bf16x8 *>(hi + n * ld + k) = h;
     *reinterpret_cast<bf16x8 *>(lo + n * ld + k) = l;
   }
+  // two consecutive k for one n (one dword per plane)
+  __device__ __forceinline__ void put2(int n, int k, float x0, float x1) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 h, l;
+    h[0] = to_bf16(x0);
+    h[1] = to_bf16(x1);
+    l[0] = to_bf16(x0 - static_cast<float>(h[0]));
+    l[1] = to_bf16(x1 - static_cast<float>(h[1]));
+    *reinterpret_cast<bf16x2 *>(hi + n * ld + k) = h;
+    *reinterpret_cast<bf16x2 *>(lo + n * ld + k) = l;
+  }
   __device__ __forceinline__ FragS get(int n, int k) const {
     FragS f;
     f.h = *reinterpret_cast<const bf16x8 *>(hi + n * ld + k);
@@ -256,6 +267,9 @@ template <> struct OperandLds<PrecF32> {
     *reinterpret_cast<float4 *>(v + n * ld + k) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4 *>(v + n * ld + k + 4) = make_float4(x[4], x[5], x[6], x[7]);
   }
+  __device__ __forceinline__ void put2(int n, int k, float x0, float x1) {
+    *reinterpret_cast<float2 *>(v + n * ld + k) = make_float2(x0, x1);
+  }
   __device__ __forceinline__ FragF get(int n, int k) const {
     FragF f;
     const float4 a = *reinterpret_cast<const float4 *>(v + n * ld + k);
@@ -264,6 +278,131 @@ template <> struct OperandLds<PrecF32> {
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
     return f;
   }
+};
+
+// LDS storage of an operand read back as Plain fragments, same addressing as
+// OperandLds: bf16 policy one bf16 plane, fp32 policy one fp32 plane.
+template <class P> struct PlainLds;
+
+template <> struct PlainLds<PrecBF16> {
+  bf16 *v;
+  int ld;
+  static constexpr int kBytesPerElem = 2;
+  __device__ __forceinline__ void init(void *base, int ld_) {
+    v = reinterpret_cast<bf16 *>(base);
+    ld = ld_;
+  }
+  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
+    bf16x8 h;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) h[r] = to_bf16(x[r]);
+    *reinterpret_cast<bf16x8 *>(v + n * ld + k) = h;
+  }
+  __device__ __forceinline__ FragP get(int n, int k) const {
+    FragP f;
+    f.h = *reinterpret_cast<const bf16x8 *>(v + n * ld + k);
+    return f;
+  }
+};
+
+template <> struct PlainLds<PrecF32> {
+  float *v;
+  int ld;
+  static constexpr int kBytesPerElem = 4;
+  __device__ __forceinline__ void init(void *base, int ld_) {
+    v = reinterpret_cast<float *>(base);
+    ld = ld_;
+  }
+  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
+    *reinterpret_cast<float4 *>(v + n * ld + k) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(v + n * ld + k + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+  __device__ __forceinline__ FragF get(int n, int k) const {
+    FragF f;
+    const float4 a = *reinterpret_cast<const float4 *>(v + n * ld + k);
+    const float4 b = *reinterpret_cast<const float4 *>(v + n * ld + k + 4);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+};
+
+// ------------------------------------------------------------ workspace tiles
+// Fragment-major tiles: an R x K tile (R a multiple of 16, K of 32) is stored
+// as (R/16) x (K/32) blocks in row-block-major order; block (i, j) holds its
+// 16 x 32 elements as 64 fragments of eight consecutive columns, fragment
+// f = 16 q + r being row 16 i + r, columns 32 j + 8 q .. + 7: exactly the
+// operand lane f of a 16x16x32 MFMA reads, so a wave loads a block as one
+// contiguous run.  bf16 policy: plain block 1 KiB (fragment f at byte 16 f),
+// split block 2 KiB (hi fragments, then lo fragments at +1 KiB); fp32 policy:
+// 2 KiB blocks, fragment f at byte 32 f, for both kinds.
+struct FragPos {
+  int blk, f, e;   // block, fragment, element within the fragment
+};
+__device__ __forceinline__ FragPos frag_pos(int r, int k, int K) {
+  return FragPos{(r >> 4) * (K >> 5) + (k >> 5), 16 * ((k & 31) >> 3) + (r & 15), k & 7};
+}
+
+template <class P> struct TileIO;
+
+template <> struct TileIO<PrecBF16> {
+  __device__ static unsigned char *plain_at(void *t, int blk, int f) {
+    return static_cast<unsigned char *>(t) + blk * 1024 + f * 16;
+  }
+  __device__ static unsigned char *split_at(void *t, int blk, int f) {
+    return static_cast<unsigned char *>(t) + blk * 2048 + f * 16;
+  }
+  __device__ static void put_plain8(void *t, int blk, int f, const float (&x)[8]) {
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = to_bf16(x[e]);
+    *reinterpret_cast<bf16x8 *>(plain_at(t, blk, f)) = h;
+  }
+  __device__ static void put_split8(void *t, int blk, int f, const float (&x)[8]) {
+    const FragS v = make_frag<FragS>(x);
+    *reinterpret_cast<bf16x8 *>(split_at(t, blk, f)) = v.h;
+    *reinterpret_cast<bf16x8 *>(split_at(t, blk, f) + 1024) = v.l;
+  }
+  __device__ static void put_split(void *t, FragPos p, float x) {
+    const bf16 h = to_bf16(x);
+    reinterpret_cast<bf16 *>(split_at(t, p.blk, p.f))[p.e] = h;
+    reinterpret_cast<bf16 *>(split_at(t, p.blk, p.f) + 1024)[p.e] = to_bf16(x - static_cast<float>(h));
+  }
+  __device__ static FragP get_plain(const void *t, int blk, int f) {
+    FragP v;
+    v.h = *reinterpret_cast<const bf16x8 *>(plain_at(const_cast<void *>(t), blk, f));
+    return v;
+  }
+  __device__ static FragS get_split(const void *t, int blk, int f) {
+    FragS v;
+    const unsigned char *p = split_at(const_cast<void *>(t), blk, f);
+    v.h = *reinterpret_cast<const bf16x8 *>(p);
+    v.l = *reinterpret_cast<const bf16x8 *>(p + 1024);
+    return v;
+  }
+};
+
+template <> struct TileIO<PrecF32> {
+  __device__ static float *at(void *t, int blk, int f) {
+    return reinterpret_cast<float *>(static_cast<unsigned char *>(t) + blk * 2048 + f * 32);
+  }
+  __device__ static void put_plain8(void *t, int blk, int f, const float (&x)[8]) {
+    float *p = at(t, blk, f);
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+  __device__ static void put_split8(void *t, int blk, int f, const float (&x)[8]) { put_plain8(t, blk, f, x); }
+  __device__ static void put_split(void *t, FragPos p, float x) { at(t, p.blk, p.f)[p.e] = x; }
+  __device__ static FragF get_plain(const void *t, int blk, int f) {
+    const float *p = at(const_cast<void *>(t), blk, f);
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    FragF v;
+    v.v[0] = a.x; v.v[1] = a.y; v.v[2] = a.z; v.v[3] = a.w;
+    v.v[4] = b.x; v.v[5] = b.y; v.v[6] = b.z; v.v[7] = b.w;
+    return v;
+  }
+  __device__ static FragF get_split(const void *t, int blk, int f) { return get_plain(t, blk, f); }
 };
 
 }  // namespace gdr

@@ -6,19 +6,62 @@
 
 namespace gdr {
 
+// Workspace written by the prep kernel and read by the scan kernel: one
+// fragment-major tile (layout at TileIO in common.hpp) per (batch, head,
+// chunk) in each region, regions in this order, each 256-byte aligned:
+//   A   diag(beta) A_c     [C][C]    plain  per beta head
+//   L   L_c                [C][C]    split  per key head
+//   KB  Kbar_c             [C][d_k]  plain  per key head
+//   QB  Qbar_c             [C][d_k]  split  per key head
+//   KH  Khat_c^T           [d_k][C]  split  per key head
+//   GM  exp(Lambda_C)      [d_k]     fp32   per key head
+// plain: bf16 (bf16 inputs) or fp32; split: bf16 hi and lo fragments (bf16
+// inputs) or fp32.  GM is a plain fp32 vector.
+struct WsLayout {
+  size_t tile[6];   // bytes per tile, in region order
+  size_t off[6];    // region offsets
+  size_t total;
+};
+enum WsRegion { kWsA = 0, kWsL, kWsKB, kWsQB, kWsKH, kWsGM };
+
+__host__ __device__ inline WsLayout ws_layout(int B, int H_k, int H_beta, int N_c, int C, int d_k, bool bf16) {
+  const size_t pb = bf16 ? 2 : 4, sb = 4;
+  WsLayout w;
+  w.tile[kWsA] = pb * C * C;
+  w.tile[kWsL] = sb * C * C;
+  w.tile[kWsKB] = pb * C * d_k;
+  w.tile[kWsQB] = sb * C * d_k;
+  w.tile[kWsKH] = sb * d_k * C;
+  w.tile[kWsGM] = 4 * (size_t)d_k;
+  size_t at = 0;
+  for (int r = 0; r < 6; ++r) {
+    w.off[r] = at;
+    const size_t heads = r == kWsA ? H_beta : H_k;
+    at += (size_t)B * heads * N_c * w.tile[r];
+    at = (at + 255) & ~(size_t)255;
+  }
+  w.total = at;
+  return w;
+}
+
 struct ChunkArgs {
   const void *q, *k, *v, *beta, *log_alpha;  // inputs (in_dtype)
   const float *h0;                            // nullable
   void *o;                                    // out_dtype
   float *hT;                                  // nullable
-  float *A_ws;                                // [B, H_beta, N_c, C, C]
-  float *L_ws;                                // [B, H_k, N_c, C, C]
+  unsigned char *ws;                          // workspace, laid out by wl
+  WsLayout wl;
   int B, T, H_k, H_v, d_k, d_v, C, G, gshift;
   int H_beta;                                 // H_v, or H_k when beta is per key head
   int N_c;
   int beta_per_key_head;
   int solve, order, residual;
 };
+
+// Tile of region r for (batch b, head, chunk c).
+__device__ inline unsigned char *ws_tile(const ChunkArgs &a, int r, int heads, int head, int b, int c) {
+  return a.ws + a.wl.off[r] + (((size_t)b * heads + head) * a.N_c + c) * a.wl.tile[r];
+}
 
 struct StepArgs {
   const void *q, *k, *v, *beta, *log_alpha;
@@ -36,7 +79,7 @@ hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream
 
 // Whether a shape is compiled in (the API layer reports GDR_ERR_UNSUPPORTED otherwise).
 bool prep_supported(int C, int d_k, int G);
-int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, int G, bool in_bf16);
+int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16);
 size_t prep_lds_bytes(int C, int G);
 
 }  // namespace gdr

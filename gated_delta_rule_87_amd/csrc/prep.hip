@@ -1,7 +1,11 @@
 // Chunk preparation: per (batch, key head, chunk) build the beta-free Gram
 // G_c (strictly lower) and the score matrix L_c (lower, diagonal included)
 // with division-free relative decay, then for every beta head solve
-// A_c = (I + G_c diag(beta))^{-1} and store A_c and L_c as fp32 C x C.
+// A_c = (I + G_c diag(beta))^{-1}.  Everything the sequential scan needs from
+// q, k, beta and log alpha is written to the workspace here, where all
+// chunks are processed in parallel, as ready MFMA operands: diag(beta) A_c
+// (plain), L_c (split), Kbar_c (plain), Qbar_c and Khat_c^T (split) and
+// exp(Lambda_C).
 //
 // Systolic Linear Attention (paperpeel 2611.06828):
 //  - cumulative log-decay Lambda and the chunk matrices: Table 2;
@@ -245,6 +249,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   constexpr int NKV = C * DK / (8 * 256);   // bound on 8-element log-alpha vectors per thread
   constexpr int KS = DK / 32;
   using Split = typename P::Split;
+  using IO = TileIO<P>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float *smem = reinterpret_cast<float *>(smem_raw);
   const int c = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -372,8 +377,58 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     }
   };
 
+  // ---- scan operands (Systolic Linear Attention, Table 2): Kbar = K (.)
+  // exp(Lambda_t) and Qbar = Q (.) exp(Lambda_t) by token rows, Khat^T = (K (.)
+  // exp(Lambda_C - Lambda_t))^T by channel rows, and exp(Lambda_C).  Every
+  // exponent is <= 0.  Rows past T are zero.
+  {
+    void *tKB = ws_tile(a, kWsKB, a.H_k, hk, b, c);
+    void *tQB = ws_tile(a, kWsQB, a.H_k, hk, b, c);
+    void *tKH = ws_tile(a, kWsKH, a.H_k, hk, b, c);
+    float *tGM = reinterpret_cast<float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c));
+    constexpr int NIT = C * DK / (8 * 256);   // 8-element units per thread
+    static_assert(C * DK % (8 * 256) == 0, "units must divide evenly");
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {        // unit = fragment (token t, channels ch0 .. ch0 + 7)
+      const int u = tid + 256 * it;
+      const int blk = u >> 6, f = u & 63;
+      const int t = 16 * (blk / (DK / 32)) + (f & 15), ch0 = 32 * (blk % (DK / 32)) + 8 * (f >> 4);
+      Raw8<TIn> rk, rq;
+      rk.load(kbase + tok(t) * row_stride + ch0);
+      rq.load(qbase + tok(t) * row_stride + ch0);
+      const float keep = (t0 + t < T) ? 1.f : 0.f;
+      float xk[8], xq[8], lt[8];
+      rk.to_float(xk);
+      rq.to_float(xq);
+      lam8(t, ch0, lt);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = __expf(lt[e]) * keep;
+        xk[e] *= d;
+        xq[e] *= d;
+      }
+      IO::put_plain8(tKB, blk, f, xk);
+      IO::put_split8(tQB, blk, f, xq);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {        // unit = fragment (channel ch, tokens tt0 .. tt0 + 7)
+      const int u = tid + 256 * it;
+      const int blk = u >> 6, f = u & 63;
+      const int ch = 16 * (blk / (C / 32)) + (f & 15), tt0 = 32 * (blk % (C / 32)) + 8 * (f >> 4);
+      const int g = ch >> gs;
+      const float lC = lam[(C - 1) * G + g];
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(kbase[tok(tt0 + e) * row_stride + ch]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= (t0 + tt0 + e < T) ? __expf(lC - lam[(tt0 + e) * G + g]) : 0.f;
+      IO::put_split8(tKH, blk, f, x);
+    }
+    if (tid < DK) tGM[tid] = __expf(lam[(C - 1) * G + (tid >> gs)]);
+  }
+
   // ---- Gram G_c (beta-free, strictly lower) and L_c (lower incl. diagonal)
-  float *Lout = a.L_ws + (((size_t)b * a.H_k + hk) * a.N_c + c) * (size_t)(C * C);
+  void *tL = ws_tile(a, kWsL, a.H_k, hk, b, c);
   for (int pi = w; pi < NPAIR; pi += blockDim.x / kWave) {
     int I, J;
     pair_of(pi, I, J);
@@ -437,11 +492,11 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
       gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[r] : 0.f;
-      Lout[row * C + col] = (I > J || row >= col) ? accL[r] : 0.f;
+      IO::put_split(tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[r] : 0.f);
     }
   }
   for (int i = tid; i < C * C; i += blockDim.x) {
-    if ((i / C) / 16 < (i % C) / 16) Lout[i] = 0.f;   // blocks above the diagonal
+    if ((i / C) / 16 < (i % C) / 16) IO::put_split(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
   }
 
   // ---- solve per beta head
@@ -460,9 +515,16 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       solve_neumann<C>(gmat, bet, amat, tmp, a.order, a.residual);
     }
     __syncthreads();
-    float *Aout = a.A_ws + (((size_t)b * a.H_beta + hb) * a.N_c + c) * (size_t)(C * C);
-    for (int i = 4 * tid; i < C * C; i += 4 * blockDim.x) {
-      *reinterpret_cast<float4 *>(Aout + i) = *reinterpret_cast<const float4 *>(amat + (i / C) * (C + 4) + i % C);
+    // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y
+    void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
+    for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
+      const int blk = u >> 6, f = u & 63;
+      const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
+      const float4 a0 = *reinterpret_cast<const float4 *>(amat + row * (C + 4) + col);
+      const float4 a1 = *reinterpret_cast<const float4 *>(amat + row * (C + 4) + col + 4);
+      const float bt = bet[row];
+      const float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
+      IO::put_plain8(tA, blk, f, x);
     }
   }
 }

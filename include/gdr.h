@@ -85,12 +85,38 @@ typedef struct {
 
 /*
  * Bytes of device workspace gdr_chunk_fwd needs for problem p (0 for an
- * invalid problem).  The workspace holds, per chunk, A_c for every beta head
- * and L_c for every key head, as fp32 C x C matrices:
- *   A: [B, H_beta, N_c, C, C] followed by L: [B, H_k, N_c, C, C],
- * N_c = ceil(T / C), H_beta = H_v (or H_k with beta_per_key_head).
+ * invalid problem).  The workspace holds every per-chunk quantity of the WY
+ * form (Systolic Linear Attention, Table 2), prepared once per chunk and
+ * head so that the sequential state scan only multiplies.  Six regions, in
+ * this order, each a stack of tiles indexed [B][heads][N_c] (N_c =
+ * ceil(T / C), H_beta = H_v, or H_k with beta_per_key_head):
+ *   0  A    diag(beta_c) A_c           C x C     plain   per beta head
+ *   1  L    L_c (decayed q.k, t >= j)  C x C     split   per key head
+ *   2  KB   Kbar_c = K (.) exp(Lambda) C x d_k   plain   per key head
+ *   3  QB   Qbar_c = Q (.) exp(Lambda) C x d_k   split   per key head
+ *   4  KH   Khat_c^T, Khat = K (.) exp(Lambda_C - Lambda)
+ *                                      d_k x C   split   per key head
+ *   5  GM   exp(Lambda_C) per channel  d_k       fp32    per key head
+ * Tiles are fragment-major, the order in which 16x16x32 MFMA operands are
+ * read: an R x K tile is (R/16) x (K/32) blocks, row-block-major; a block is
+ * 64 fragments of 8 consecutive columns, fragment f = 16 q + r holding row r,
+ * columns 8 q .. 8 q + 7 of the block.  plain (bf16 inputs): bf16, 1 KiB per
+ * block, fragment f at byte 16 f.  split (bf16 inputs): x = hi + lo with hi =
+ * bf16(x), lo = bf16(x - hi) (about 16 significant bits), 2 KiB per block:
+ * hi fragments at 16 f, lo fragments at 1024 + 16 f.  fp32 inputs: plain and
+ * split are fp32, 2 KiB per block, fragment f at byte 32 f.  GM is a plain
+ * fp32 vector.  Token rows (columns of KH) of a short final chunk past T are
+ * zero and its gate values are those of its last real token.  Region
+ * offsets: gdr_chunk_workspace_layout.
  */
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p);
+
+/*
+ * Byte offsets of the six workspace regions above: offsets[0..5], and the
+ * total size (== gdr_chunk_fwd_workspace_size) in offsets[6].  `offsets` is a
+ * host array of 7 size_t.  For inspecting a prepared workspace.
+ */
+gdr_status gdr_chunk_workspace_layout(const gdr_problem *p, size_t *offsets);
 
 /*
  * Chunkwise forward (Systolic Linear Attention Table 2 / section 2.4.2 WY
@@ -101,38 +127,38 @@ size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p);
  *   o         : output, out_dtype [B,T,H_v,d_v].
  *   hT        : final state, fp32 [B,H_v,d_k,d_v]; NULL = not written; may alias h0.
  *   workspace : device scratch of at least gdr_chunk_fwd_workspace_size(p)
- *               bytes, 256-byte aligned; its contents on return are the A_c
- *               and L_c of every chunk in the layout documented there.
+ *               bytes, 256-byte aligned; its contents on return are the
+ *               per-chunk quantities documented there.
  * Supported here: in_dtype bf16 or f32, chunk 64 or 128, d_k in {64,128,256},
- * d_v a multiple of 16, G = d_k (per-channel gates) or a divisor of d_k no
- * larger than 8 (grouped gates); beyond that GDR_ERR_UNSUPPORTED.
+ * d_v a multiple of 16, G a divisor of d_k; beyond that GDR_ERR_UNSUPPORTED.
  */
 gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v,
                          const void *beta, const void *log_alpha, const float *h0, void *o,
                          float *hT, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Only the per-chunk matrices of gdr_chunk_fwd: fills `workspace` with A_c
- * (per beta head) and L_c (per key head) exactly as gdr_chunk_fwd leaves them,
- * without touching any state or output.  For inspecting the in-chunk solve.
+ * The parallel half of gdr_chunk_fwd: fills `workspace` with every per-chunk
+ * quantity listed at gdr_chunk_fwd_workspace_size, exactly as gdr_chunk_fwd
+ * leaves it, without touching any state or output.  All chunks of all heads
+ * are independent here (one workgroup each).
  */
 gdr_status gdr_chunk_prepare(const gdr_problem *p, const void *q, const void *k,
                              const void *beta, const void *log_alpha, void *workspace,
                              size_t workspace_bytes, void *stream);
 
 /*
- * Only the state scan and output of gdr_chunk_fwd, over a workspace that
- * gdr_chunk_prepare filled for the same q, k, beta, log_alpha and problem:
+ * The sequential half of gdr_chunk_fwd: the state scan and output over a
+ * workspace that gdr_chunk_prepare filled for the same problem, so
  * gdr_chunk_fwd(...) == gdr_chunk_prepare(...) then gdr_chunk_scan(...).
- * Running it again with another h0 (or v) reuses the prepared chunks; that
- * is the second pass of a sequence split across devices, where each piece
- * re-reads its output from the state handed over by the previous piece
- * (Systolic Linear Attention, section 3.3, the affine chunk map).
- * Arguments as for gdr_chunk_fwd; the workspace is read only.
+ * Only v, h0 and the workspace are read (everything derived from q, k, beta
+ * and log_alpha is in the workspace).  Running it again with another h0 (or
+ * v) reuses the prepared chunks; that is the second pass of a sequence split
+ * across devices, where each piece re-reads its output from the state handed
+ * over by the previous piece (Systolic Linear Attention, section 3.3, the
+ * affine chunk map).  Other arguments as for gdr_chunk_fwd.
  */
-gdr_status gdr_chunk_scan(const gdr_problem *p, const void *q, const void *k, const void *v,
-                          const void *beta, const void *log_alpha, const float *h0, void *o,
-                          float *hT, const void *workspace, size_t workspace_bytes, void *stream);
+gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, void *o, float *hT,
+                          const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Token recurrence, p->T tokens in order (Systolic Linear Attention, section

@@ -51,17 +51,39 @@ def problem(**kw):
     return p
 
 
+def expected_regions(B, T, H_k, H_v, d_k, chunk, bf16=True, beta_per_key_head=0):
+    """Region sizes as documented in include/gdr.h (each region padded to 256 B)."""
+    nc = -(-T // chunk)
+    hb = H_k if beta_per_key_head else H_v
+    pb = 2 if bf16 else 4
+    tiles = [("A", hb, pb * chunk * chunk), ("L", H_k, 4 * chunk * chunk), ("KB", H_k, pb * chunk * d_k),
+             ("QB", H_k, 4 * chunk * d_k), ("KH", H_k, 4 * d_k * chunk), ("GM", H_k, 4 * d_k)]
+    out, at = {}, 0
+    for name, heads, tile in tiles:
+        out[name] = at
+        at += B * heads * nc * tile
+        at = -(-at // 256) * 256
+    out["total"] = at
+    return out
+
+
 def test_workspace_size():
     lib = gb.load()
     p = problem()
-    # A per value head and L per key head, fp32 C x C per chunk
-    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 64 * 64 * 128 * 2 * (32 + 32)
+    exp = expected_regions(2, 8192, 32, 32, 128, 64)
+    assert exp["total"] == 876_609_536
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == exp["total"]
+    assert gb.gdr_chunk_workspace_layout(p) == exp
     p = problem(H_k=8, H_v=32, d_k=256, gate_groups=4, T=100)
-    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 64 * 64 * 2 * 2 * (32 + 8)
+    assert gb.gdr_chunk_workspace_layout(p) == expected_regions(2, 100, 8, 32, 256, 64)
     p = problem(H_k=8, H_v=32, d_k=256, gate_groups=4, T=100, beta_per_key_head=1)
-    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 64 * 64 * 2 * 2 * (8 + 8)
+    assert gb.gdr_chunk_workspace_layout(p) == expected_regions(2, 100, 8, 32, 256, 64, beta_per_key_head=1)
+    p = problem(T=333, chunk=128, in_dtype=gb.GDR_F32, d_v=32)
+    assert gb.gdr_chunk_workspace_layout(p) == expected_regions(2, 333, 32, 32, 128, 128, bf16=False)
     assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(problem(H_v=30))) == 0
     assert lib.gdr_chunk_fwd_workspace_size(None) == 0
+    with pytest.raises(gb.GdrError):
+        gb.gdr_chunk_workspace_layout(problem(H_v=30))
 
 
 FAKE = 0x10000          # 64 KiB-aligned non-null address, never dereferenced
@@ -97,8 +119,6 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, la=FAKE, h0=None, o=FAKE, hT=
     (dict(chunk=48), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=32), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=128, d_k=256, gate_groups=256), gb.GDR_ERR_UNSUPPORTED),
-    (dict(gate_groups=16), gb.GDR_ERR_UNSUPPORTED),
-    (dict(d_k=256, gate_groups=32), gb.GDR_ERR_UNSUPPORTED),
     (dict(B=1 << 20, T=1 << 20), gb.GDR_ERR_INVALID_ARG),
 ])
 def test_invalid_problems(kw, status):
@@ -143,6 +163,15 @@ def test_prepare_and_step_validate():
     assert lib.gdr_recurrent_step(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(0),
                                   vp(FAKE), None) == gb.GDR_ERR_INVALID_ARG
     assert "state" in gb.last_error()
+    # the scan reads only v, h0 and the workspace
+    p = problem()
+    assert lib.gdr_chunk_scan(ctypes.byref(p), vp(0), None, vp(FAKE), None, vp(FAKE), 1 << 40,
+                              None) == gb.GDR_ERR_INVALID_ARG
+    assert "v is NULL" in gb.last_error()
+    assert lib.gdr_chunk_scan(ctypes.byref(p), vp(FAKE), None, vp(FAKE), None, vp(FAKE), 1024,
+                              None) == gb.GDR_ERR_WORKSPACE
+    assert lib.gdr_chunk_scan(ctypes.byref(p), vp(FAKE), None, vp(FAKE), None, vp(MIS), 1 << 40,
+                              None) == gb.GDR_ERR_INVALID_ARG
     p = problem(d_k=32, gate_groups=32)
     assert lib.gdr_recurrent_step(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
                                   vp(FAKE), None) == gb.GDR_ERR_UNSUPPORTED

@@ -15,7 +15,7 @@ import torch
 
 from gated_delta_rule_87_amd import binding as gb
 from gated_delta_rule_87_amd.inputs import Workload
-from gpu_common import TOL, device_inputs, draw, need_gpu, rel_err, run_chunk, to_torch
+from gpu_common import decode_workspace, TOL, device_inputs, draw, need_gpu, rel_err, run_chunk, to_torch
 from oracle import chunk as och
 from oracle.recurrence import recurrence_c
 
@@ -92,26 +92,61 @@ def test_neumann_small(name, order, res):
     assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong"])
+def expected_operands(x, w):
+    """The scan operands of every chunk from the fp64 chunk pieces: Kbar,
+    Qbar, Khat^T and exp(Lambda_C) per key head, token rows past T zero."""
+    B, T, Hk, dk = x["q"].shape
+    C = w.chunk
+    nc = -(-T // C)
+    KB = np.zeros((B, Hk, nc, C, dk)); QB = np.zeros_like(KB)
+    KH = np.zeros((B, Hk, nc, dk, C)); GM = np.zeros((B, Hk, nc, dk))
+    for b in range(B):
+        for hk in range(Hk):
+            q = np.asarray(x["q"][b, :, hk], np.float64)
+            k = np.asarray(x["k"][b, :, hk], np.float64)
+            la = np.repeat(np.asarray(x["log_alpha"][b, :, hk], np.float64), dk // w.G, axis=1)
+            for c in range(nc):
+                s, e = c * C, min(c * C + C, T)
+                pc = och.chunk_pieces(q[s:e], k[s:e], np.ones(e - s), la[s:e])
+                KB[b, hk, c, :e - s] = pc["Kbar"]
+                QB[b, hk, c, :e - s] = pc["Qbar"]
+                KH[b, hk, c, :, :e - s] = pc["Khat"].T
+                GM[b, hk, c] = pc["gamma"]
+    return {"KB": KB, "QB": QB, "KH": KH, "GM": GM}
+
+
+@pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong",
+                                  "dk64_bkh_gva"])
 @pytest.mark.parametrize("solve", ["exact", "neumann"])
-def test_prepare_matrices(name, solve):
-    """A_c and L_c of every chunk against the fp64 chunk quantities."""
+def test_prepared_workspace(name, solve):
+    """Every prepared chunk quantity against the fp64 chunk pieces: diag(beta)
+    A_c, L_c, Kbar, Qbar, Khat^T, exp(Lambda_C).  Bars on max|err| / max|ref|:
+    plain bf16 tiles 4e-3 (one bf16 rounding), split tiles 1e-4, fp32 1e-5."""
     w = SMALL[name]
     raw, x = draw(w)
     dev = device_inputs(raw)
     print(f"[case] prepare {name} {solve}", flush=True)
-    A, L = gb.gdr_chunk_prepare(dev["q"], dev["k"], dev["beta"], dev["log_alpha"], chunk=w.chunk, solve=solve,
-                                neumann_order=w.neumann_order, neumann_residual_steps=w.neumann_residual,
-                                H_v=w.H_v)
+    ws, p = gb.gdr_chunk_prepare(dev["q"], dev["k"], dev["beta"], dev["log_alpha"], chunk=w.chunk, solve=solve,
+                                 neumann_order=w.neumann_order, neumann_residual_steps=w.neumann_residual,
+                                 H_v=w.H_v)
+    got = decode_workspace(ws, p)
     A_ref, L_ref = och.chunk_stage_matrices(x["q"], x["k"], x["beta"], x["log_alpha"], w.chunk, solve=solve,
                                             order=w.neumann_order, residual_steps=w.neumann_residual,
                                             beta_per_key_head=w.beta_per_key_head)
-    A, L = A.cpu().numpy(), L.cpu().numpy()
-    tol = 1e-5 if w.dtype == "f32" else 1e-4
-    ea = np.max(np.abs(A - A_ref)) / np.max(np.abs(A_ref))
-    el = np.max(np.abs(L - L_ref)) / np.max(np.abs(L_ref))
-    print(f"  err A={ea:.3e} L={el:.3e}", flush=True)
-    assert ea <= tol and el <= tol
+    B, T = x["q"].shape[:2]
+    C = w.chunk
+    nc = A_ref.shape[2]
+    beta = np.zeros((B, nc * C, x["beta"].shape[2]))
+    beta[:, :T] = x["beta"]
+    beta = beta.reshape(B, nc, C, -1).transpose(0, 3, 1, 2)      # [B, H_beta, N_c, C]
+    ref = dict(expected_operands(x, w), A=beta[..., None] * A_ref, L=L_ref)
+    f32 = w.dtype == "f32"
+    bars = {"A": 1e-5 if f32 else 4e-3, "KB": 1e-5 if f32 else 4e-3}
+    for key in ("A", "L", "KB", "QB", "KH", "GM"):
+        err = np.max(np.abs(got[key] - ref[key])) / np.max(np.abs(ref[key]))
+        bar = bars.get(key, 1e-5 if f32 else 1e-4)
+        print(f"  {key}: max err / max ref = {err:.3e} (bar {bar:g})", flush=True)
+        assert err <= bar, key
 
 
 RECUR = {
