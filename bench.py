@@ -39,13 +39,14 @@ def source_sha(kernel):
 
 
 def work_model(w):
-    """Algorithmic FLOPs and HBM bytes per launch of each kernel (see the design doc,
-    "Roofline").  prep: Gram and L (2 C d_k per key-head token, causal halves)
-    and the solve (C^2/3 per value-head token); it must read the key side (q, k,
-    beta, log alpha) once.  scan: W/U, L E and the three state products per
-    value-head token; it must read v and write o (fp32) and hT once.  The
-    workspace that carries prepared chunks from prep to scan is not
-    algorithmic traffic: it shows up in the measured ``traffic``."""
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel.
+
+    prep: Gram and L (2 C d_k per key-head token, causal halves) and the solve
+    (C^2/3 per value-head token); it must read the key side (q, k, beta, log
+    alpha) once.  scan: W/U, L E and the three state products per value-head
+    token; it must read v and write o (fp32) and hT once.  The workspace that
+    carries prepared chunks from prep to scan is not algorithmic traffic: it
+    shows up in the measured ``traffic``."""
     C, dk, dv = w.chunk, w.d_k, w.d_v
     R = w.H_v // w.H_k
     token_heads = w.B * w.T * w.H_v
@@ -141,9 +142,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each (batch, head) unit is independent; see DESIGN.md for how it would shard).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path here.  Every "
+              "(batch, value head) unit is independent, so B * H_v would be split across GPUs "
+              "with no communication; run one process per GPU on its slice.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, args.steps)
