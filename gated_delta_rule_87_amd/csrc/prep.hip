@@ -47,10 +47,11 @@ __host__ __device__ inline int prep_tmp_floats(int C) {
   return merge > neumann ? merge : neumann;
 }
 
+constexpr int kXbLd = 20;   // row stride (floats) of the per-wave transpose buffers
+
 size_t prep_lds_bytes(int C, int G) {
-  const int nb = C / 16;
   return sizeof(float) * (size_t)(prep_region0_floats(C, G) + C * prep_ld(C) + prep_tmp_floats(C) + C) +
-         sizeof(int) * (size_t)nb;
+         sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd;
 }
 
 // --------------------------------------------------------------- fp32 tiles
@@ -245,7 +246,6 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
 template <typename TIn, class P, int C, int DK>
 __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   constexpr int NB = C / 16;
-  constexpr int NPAIR = NB * (NB + 1) / 2;
   constexpr int NKV = C * DK / (8 * 256);   // bound on 8-element log-alpha vectors per thread
   constexpr int KS = DK / 32;
   using Split = typename P::Split;
@@ -266,6 +266,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   float *tmp = gmat + C * prep_ld(C);
   float *bet = tmp + prep_tmp_floats(C);               // [C]
   int *flags = reinterpret_cast<int *>(bet + C);       // [NB]
+  float *xbuf = reinterpret_cast<float *>(flags + 16);  // [4 waves][32][kXbLd]
 
   const TIn *la = reinterpret_cast<const TIn *>(a.log_alpha);
   const TIn *qp = reinterpret_cast<const TIn *>(a.q);
@@ -292,34 +293,22 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       las[j] = la[tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1))];
     }
   }
-  constexpr int NBET = 4;                              // up to 4 * 256 beta values (C * Rb)
-  TIn bets[NBET];
-#pragma unroll
-  for (int j = 0; j < NBET; ++j) {
-    const int e = min(tid + 256 * j, C * Rb - 1);      // e = rb * C + t
-    bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
-  }
-  // first Gram pair's operands
-  auto pair_of = [&](int pi, int &I, int &J) __attribute__((always_inline)) {
-    I = 0;
-    while ((I + 1) * (I + 2) / 2 <= pi) ++I;
-    J = pi - I * (I + 1) / 2;
-  };
+  // Gram and L by 16-token row blocks: wave w owns blocks w (and 7 - w when
+  // C = 128), builds their decayed row operands once and pairs them with every
+  // earlier block.
+  constexpr int NR = NB / 4;                           // row blocks per wave
+  auto own = [&](int r) { return (r & 1) ? 4 * r + 3 - w : 4 * r + w; };
   const TIn *kbase = kp + (size_t)hk * DK;
   const TIn *qbase = qp + (size_t)hk * DK;
   Raw8<TIn> kt[KS], qt[KS], kj[KS];
-  auto load_pair = [&](int pi) __attribute__((always_inline)) {
-    int I, J;
-    pair_of(min(pi, NPAIR - 1), I, J);
-    const size_t rt = tok(16 * I + lr) * row_stride, rj = tok(16 * J + lr) * row_stride;
+  auto load_rows = [&](Raw8<TIn> (&dst)[KS], const TIn *base, int blk) __attribute__((always_inline)) {
+    const size_t rt = tok(16 * blk + lr) * row_stride;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kt[s].load(kbase + rt + 32 * s + 8 * lq);
-      qt[s].load(qbase + rt + 32 * s + 8 * lq);
-      kj[s].load(kbase + rj + 32 * s + 8 * lq);
-    }
+    for (int s = 0; s < KS; ++s) dst[s].load(base + rt + 32 * s + 8 * lq);
   };
-  load_pair(w);
+  load_rows(kt, kbase, own(0));
+  load_rows(qt, qbase, own(0));
+  load_rows(kj, kbase, 0);
 
   // ---- Lambda: raw log alpha -> lam, then in-place prefix sum per column
   if (la_vec) {
@@ -377,129 +366,136 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     }
   };
 
-  // ---- scan operands (Systolic Linear Attention, Table 2): Kbar = K (.)
-  // exp(Lambda_t) and Qbar = Q (.) exp(Lambda_t) by token rows, Khat^T = (K (.)
-  // exp(Lambda_C - Lambda_t))^T by channel rows, and exp(Lambda_C).  Every
-  // exponent is <= 0.  Rows past T are zero.
-  {
-    void *tKB = ws_tile(a, kWsKB, a.H_k, hk, b, c);
-    void *tQB = ws_tile(a, kWsQB, a.H_k, hk, b, c);
-    void *tKH = ws_tile(a, kWsKH, a.H_k, hk, b, c);
-    float *tGM = reinterpret_cast<float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c));
-    constexpr int NIT = C * DK / (8 * 256);   // 8-element units per thread
-    static_assert(C * DK % (8 * 256) == 0, "units must divide evenly");
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {        // unit = fragment (token t, channels ch0 .. ch0 + 7)
-      const int u = tid + 256 * it;
-      const int blk = u >> 6, f = u & 63;
-      const int t = 16 * (blk / (DK / 32)) + (f & 15), ch0 = 32 * (blk % (DK / 32)) + 8 * (f >> 4);
-      Raw8<TIn> rk, rq;
-      rk.load(kbase + tok(t) * row_stride + ch0);
-      rq.load(qbase + tok(t) * row_stride + ch0);
-      const float keep = (t0 + t < T) ? 1.f : 0.f;
-      float xk[8], xq[8], lt[8];
-      rk.to_float(xk);
-      rq.to_float(xq);
-      lam8(t, ch0, lt);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = __expf(lt[e]) * keep;
-        xk[e] *= d;
-        xq[e] *= d;
-      }
-      IO::put_plain8(tKB, blk, f, xk);
-      IO::put_split8(tQB, blk, f, xq);
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {        // unit = fragment (channel ch, tokens tt0 .. tt0 + 7)
-      const int u = tid + 256 * it;
-      const int blk = u >> 6, f = u & 63;
-      const int ch = 16 * (blk / (C / 32)) + (f & 15), tt0 = 32 * (blk % (C / 32)) + 8 * (f >> 4);
-      const int g = ch >> gs;
-      const float lC = lam[(C - 1) * G + g];
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(kbase[tok(tt0 + e) * row_stride + ch]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= (t0 + tt0 + e < T) ? __expf(lC - lam[(tt0 + e) * G + g]) : 0.f;
-      IO::put_split8(tKH, blk, f, x);
-    }
-    if (tid < DK) tGM[tid] = __expf(lam[(C - 1) * G + (tid >> gs)]);
-  }
-
-  // ---- Gram G_c (beta-free, strictly lower) and L_c (lower incl. diagonal)
+  // ---- per row block I owned by this wave:
+  //  (1) the scan operands of its 16 tokens (Systolic Linear Attention,
+  //      Table 2): Kbar = K (.) exp(Lambda_t), Qbar = Q (.) exp(Lambda_t), and
+  //      Khat = K (.) exp(Lambda_C - Lambda_t), the last transposed through a
+  //      small per-wave LDS buffer into channel-row fragments;
+  //  (2) the pivot-decayed row operands K (.) exp(Lambda_t - Lambda_p) and
+  //      Q (.) exp(Lambda_t - Lambda_p), p = first token of I, kept as split
+  //      fragments;
+  //  (3) Gram and L for the pairs (I, J), J <= I, each one MFMA product with the
+  //      decayed keys K_J (.) exp(Lambda_p - Lambda_j) of block J.
+  // Every exponent on the causal side is <= 0, except on a diagonal block,
+  // where it is at most the block's decay range (<= kPivotRange unless the
+  // block is flagged and evaluated entry by entry).
+  void *tKB = ws_tile(a, kWsKB, a.H_k, hk, b, c);
+  void *tQB = ws_tile(a, kWsQB, a.H_k, hk, b, c);
+  void *tKH = ws_tile(a, kWsKH, a.H_k, hk, b, c);
   void *tL = ws_tile(a, kWsL, a.H_k, hk, b, c);
-  for (int pi = w; pi < NPAIR; pi += blockDim.x / kWave) {
-    int I, J;
-    pair_of(pi, I, J);
-    Raw8<TIn> ckt[KS], cqt[KS], ckj[KS];
+  if (tid < DK) reinterpret_cast<float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c))[tid] =
+      __expf(lam[(C - 1) * G + (tid >> gs)]);
+  float *xb = xbuf + w * 32 * kXbLd;                   // this wave's transpose buffer [32 channels][kXbLd]
+  for (int r = 0; r < NR; ++r) {
+    const int I = own(r);
+    const int tr = 16 * I + lr, piv = 16 * I;
+    const float mt = (t0 + tr < T) ? 1.f : 0.f;
+    Split ak[KS], aq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      ckt[s] = kt[s];
-      cqt[s] = qt[s];
-      ckj[s] = kj[s];
-    }
-    load_pair(pi + blockDim.x / kWave);                  // next pair of this wave (clamped)
-    f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
-    const int tr = 16 * I + lr, jr = 16 * J + lr, piv = 16 * I;
-    const float mt = (t0 + tr < T) ? 1.f : 0.f, mj = (t0 + jr < T) ? 1.f : 0.f;
-    if (!(I == J && flags[I])) {
+      const int ch0 = 32 * s + 8 * lq;
+      float xk[8], xq[8], lt[8], lp[8], lc[8];
+      kt[s].to_float(xk);
+      qt[s].to_float(xq);
+      lam8(tr, ch0, lt);
+      lam8(piv, ch0, lp);
+      lam8(C - 1, ch0, lc);
+      float yk[8], yq[8], kbar[8], qbar[8], kh[8];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int ch0 = 32 * s + 8 * lq;
-        float xk[8], xq[8], xj[8];
-        ckt[s].to_float(xk);
-        cqt[s].to_float(xq);
-        ckj[s].to_float(xj);
-        float lp[8], lt[8], lj[8];
-        lam8(piv, ch0, lp);
-        lam8(tr, ch0, lt);
-        lam8(jr, ch0, lj);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ea = __expf(lt[e] - lp[e]) * mt;
-          const float eb = __expf(lp[e] - lj[e]) * mj;
-          xk[e] *= ea;
-          xq[e] *= ea;
-          xj[e] *= eb;
-        }
-        const Split fk = make_frag<Split>(xk), fq = make_frag<Split>(xq), fj = make_frag<Split>(xj);
-        mma(accG, fk, fj);
-        mma(accL, fq, fj);
+      for (int e = 0; e < 8; ++e) {
+        const float ea = __expf(lt[e] - lp[e]) * mt;
+        const float d = __expf(lt[e]) * mt;
+        const float h = __expf(lc[e] - lt[e]) * mt;
+        yk[e] = xk[e] * ea;
+        yq[e] = xq[e] * ea;
+        kbar[e] = xk[e] * d;
+        qbar[e] = xq[e] * d;
+        kh[e] = xk[e] * h;
       }
-    } else {
-      // Diagonal block whose decay range is too wide for one pivot: each
-      // entry by its definition, causal mask before the exponential.
+      ak[s] = make_frag<Split>(yk);
+      aq[s] = make_frag<Split>(yq);
+      IO::put_plain8(tKB, I * KS + s, l, kbar);
+      IO::put_split8(tQB, I * KS + s, l, qbar);
+      // Khat^T: lane (token lr, channels 8 lq ..) writes, lane (channel
+      // 16 (l >> 5) + (l & 15), tokens 8 g ..) reads back a fragment
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
-        float sg = 0.f, sl = 0.f;
-        if (row >= col && t0 + row < T) {
-          const size_t rrow = tok(row) * row_stride, rcol = tok(col) * row_stride;
-          for (int ch = 0; ch < DK; ++ch) {
-            const int g = ch >> gs;
-            const float d = __expf(lam[row * G + g] - lam[col * G + g]);
-            const float kc = static_cast<float>(kbase[rcol + ch]);
-            sg += static_cast<float>(kbase[rrow + ch]) * kc * d;
-            sl += static_cast<float>(qbase[rrow + ch]) * kc * d;
+      for (int e = 0; e < 8; ++e) xb[(8 * lq + e) * kXbLd + lr] = kh[e];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int chl = 16 * (l >> 5) + (l & 15), g = (l >> 4) & 1;
+      float xt[8];
+      const float4 u0 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g);
+      const float4 u1 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g + 4);
+      xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      IO::put_split8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+    }
+    if (r + 1 < NR) {                                  // next owned block's rows
+      load_rows(kt, kbase, own(r + 1));
+      load_rows(qt, qbase, own(r + 1));
+    }
+    for (int J = 0; J <= I; ++J) {
+      Raw8<TIn> ckj[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) ckj[s] = kj[s];
+      load_rows(kj, kbase, J < I ? J + 1 : 0);          // next pair's key rows (first block of the next round)
+      f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
+      const int jr = 16 * J + lr;
+      const float mj = (t0 + jr < T) ? 1.f : 0.f;
+      if (!(I == J && flags[I])) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int ch0 = 32 * s + 8 * lq;
+          float xj[8], lp[8], lj[8];
+          ckj[s].to_float(xj);
+          lam8(piv, ch0, lp);
+          lam8(jr, ch0, lj);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xj[e] *= __expf(lp[e] - lj[e]) * mj;
+          const Split fj = make_frag<Split>(xj);
+          mma(accG, ak[s], fj);
+          mma(accL, aq[s], fj);
+        }
+      } else {
+        // Diagonal block whose decay range is too wide for one pivot: each
+        // entry by its definition, causal mask before the exponential.
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
+          float sg = 0.f, sl = 0.f;
+          if (row >= col && t0 + row < T) {
+            const size_t rrow = tok(row) * row_stride, rcol = tok(col) * row_stride;
+            for (int ch = 0; ch < DK; ++ch) {
+              const int g = ch >> gs;
+              const float d = __expf(lam[row * G + g] - lam[col * G + g]);
+              const float kc = static_cast<float>(kbase[rcol + ch]);
+              sg += static_cast<float>(kbase[rrow + ch]) * kc * d;
+              sl += static_cast<float>(qbase[rrow + ch]) * kc * d;
+            }
           }
+          accG[q4] = sg;
+          accL[q4] = sl;
         }
-        accG[r] = sg;
-        accL[r] = sl;
       }
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
-      gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[r] : 0.f;
-      IO::put_split(tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[r] : 0.f);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
+        gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[q4] : 0.f;
+        IO::put_split(tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[q4] : 0.f);
+      }
     }
   }
   for (int i = tid; i < C * C; i += blockDim.x) {
     if ((i / C) / 16 < (i % C) / 16) IO::put_split(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
   }
 
-  // ---- solve per beta head
+  // ---- solve per beta head (beta loaded here: short-lived registers)
+  constexpr int NBET = 4;                              // up to 4 * 256 beta values (C * Rb)
+  TIn bets[NBET];
+#pragma unroll
+  for (int j = 0; j < NBET; ++j) {
+    const int e = min(tid + 256 * j, C * Rb - 1);      // e = rb * C + t
+    bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
+  }
   for (int rb = 0; rb < Rb; ++rb) {
     const int hb = hk * Rb + rb;
     __syncthreads();

@@ -180,3 +180,27 @@ def test_recurrent_matches_chunk():
     o_r = gb.gdr_recurrent_step(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], state)
     assert rel_err(o_c.cpu().numpy(), o_r.cpu().numpy()) <= TOL["bf16"]
     assert rel_err(h_c.cpu().numpy(), state.cpu().numpy()) <= TOL["bf16"]
+
+
+def test_prepare_is_deterministic_across_interleaved_calls():
+    """The prepared workspace is bit-identical however other launches are
+    interleaved between calls (different shapes, scans, torch kernels)."""
+    from test_gpu_parity import SMALL
+    names = ["gva_g4_bf16", "dk256_kda_bf16", "kda_bf16"]
+    cases = {}
+    for n in names:
+        w = SMALL[n]
+        raw, _ = draw(w)
+        cases[n] = (w, device_inputs(raw))
+    first = {}
+    for it in range(4):
+        for n in names:
+            w, dev = cases[n]
+            ws, p = gb.gdr_chunk_prepare(dev["q"], dev["k"], dev["beta"], dev["log_alpha"], chunk=w.chunk, H_v=w.H_v)
+            gb.gdr_chunk_scan(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], None, workspace=ws,
+                              chunk=w.chunk)
+            torch.cuda.synchronize()
+            if n not in first:
+                first[n] = ws.clone()
+            else:
+                assert torch.equal(ws, first[n]), (n, it)

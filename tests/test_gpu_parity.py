@@ -116,7 +116,7 @@ def expected_operands(x, w):
 
 
 @pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong",
-                                  "dk64_bkh_gva"])
+                                  "dk64_bkh_gva", "dk256_kda_bf16"])
 @pytest.mark.parametrize("solve", ["exact", "neumann"])
 def test_prepared_workspace(name, solve):
     """Every prepared chunk quantity against the fp64 chunk pieces: diag(beta)
