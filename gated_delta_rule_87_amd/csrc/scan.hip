@@ -48,7 +48,11 @@ struct ScanLayout {
   static constexpr int Y_LD = C + 8;    // Y^T, E^T rows
   static constexpr size_t s_bytes = 4 * (size_t)BV * S_LD;
   static constexpr size_t y_bytes = 4 * (size_t)BV * Y_LD;
-  static constexpr size_t total = s_bytes + 2 * y_bytes;
+  // Y split over channel steps (fewer row blocks than waves, d_k = 256):
+  // partial Y and Qbar S products exchanged through [C/16][BV/16][2][64] f32x4
+  static constexpr bool kYSplit = (C / 16 < 8) && DK >= 256;
+  static constexpr size_t x_bytes = kYSplit ? (size_t)(C / 16) * (BV / 16) * 2 * 64 * 16 : 0;
+  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes;
 };
 
 // Distribution of (block, tile) jobs over the eight waves: with at least
@@ -84,6 +88,17 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   using SJ = WaveJobs<DK / 16, NT>;           // S jobs
   constexpr int KSTEPS = DK / 32;             // contraction steps over channels
   constexpr int CSTEPS = C / 32;              // contraction steps over tokens
+  // Y jobs: when two waves share a row block (J::WPR = 2) and the rows are
+  // long (d_k = 256), they split its channel steps (each loads half of the
+  // block's Kbar / Qbar rows and forms partial products for every column
+  // tile) instead of loading the same rows twice; the partials are summed
+  // through LDS by the wave that owns the tile.  At d_k <= 128 the extra
+  // barrier costs more than the halved loads save, and the two waves split
+  // the column tiles instead.
+  constexpr int YS = Lay::kYSplit ? 2 : 1;    // waves splitting a row block's channel steps
+  static_assert(!Lay::kYSplit || J::WPR == 2, "channel split needs two waves per row block");
+  constexpr int YKS = KSTEPS / YS;            // channel steps per wave in Y
+  constexpr int YNT = YS == 1 ? J::TPW : NT;  // tiles a wave forms partial products for
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int T = a.T;
@@ -107,6 +122,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   sT.init(smem_raw, BV, Lay::S_LD);
   yT.init(smem_raw + Lay::s_bytes, BV, Lay::Y_LD);
   eT.init(smem_raw + Lay::s_bytes + Lay::y_bytes, BV, Lay::Y_LD);
+  f32x4 *xch = reinterpret_cast<f32x4 *>(smem_raw + Lay::s_bytes + 2 * Lay::y_bytes);
+  const int yh = YS == 1 ? 0 : w / NB;        // this wave's half of the channel steps (YS = 2)
 
   const TIn *vp = reinterpret_cast<const TIn *>(a.v);
   TOut *op = reinterpret_cast<TOut *>(a.o);
@@ -117,8 +134,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   auto tile = [&](int r, int heads, int head, int c) -> const void * { return ws_tile(a, r, heads, head, b, c); };
 
   // ---------------------------------------------------- prefetch registers
-  Plain fkb[J::RPW][KSTEPS];          // Kbar rows of each row block
-  Split fqb[J::RPW][KSTEPS];          // Qbar rows
+  Plain fkb[J::RPW][YKS];             // Kbar rows of each row block (this wave's channel steps)
+  Split fqb[J::RPW][YKS];             // Qbar rows
   Plain fa[J::RPW][CSTEPS];           // diag(beta) A_c rows
   Split fl[J::RPW][CSTEPS];           // L_c rows
   Split fkh[SJ::RPW][CSTEPS];         // Khat^T rows (channels) of each S block
@@ -131,9 +148,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     for (int r = 0; r < J::RPW; ++r) {
       const int I = J::blk(w, r);
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        fkb[r][s] = IO::get_plain(tkb, I * KSTEPS + s, l);
-        fqb[r][s] = IO::get_split(tqb, I * KSTEPS + s, l);
+      for (int s = 0; s < YKS; ++s) {
+        fkb[r][s] = IO::get_plain(tkb, I * KSTEPS + yh * YKS + s, l);
+        fqb[r][s] = IO::get_split(tqb, I * KSTEPS + yh * YKS + s, l);
       }
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) {
@@ -211,23 +228,41 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
     for (int r = 0; r < J::RPW; ++r) {
       const int I = J::blk(w, r);
-      f32x4 accY[J::TPW];
+      f32x4 accY[YNT], accQ[YNT];             // (partial) products per tile
 #pragma unroll
-      for (int u = 0; u < J::TPW; ++u) accY[u] = accO[r][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < YNT; ++u) accY[u] = accQ[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
+      for (int s = 0; s < YKS; ++s) {
 #pragma unroll
-        for (int u = 0; u < J::TPW; ++u) {
-          const int n = J::tile(w, u);
+        for (int u = 0; u < YNT; ++u) {
+          const int n = YS == 1 ? J::tile(w, u) : u;
           if (n >= NT) continue;
-          const Split fs = sT.get(16 * n + lr, 32 * s + 8 * lq);
+          const Split fs = sT.get(16 * n + lr, 32 * (yh * YKS + s) + 8 * lq);
           mma(accY[u], fkb[r][s], fs);
-          mma(accO[r][u], fqb[r][s], fs);
+          mma(accQ[u], fqb[r][s], fs);
+        }
+      }
+      if constexpr (YS == 2) {
+        // hand the partials of the tile the other wave owns to it: tile n is
+        // finished by the wave with yh == n
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          if (n == yh) continue;
+          f32x4 *slot = xch + ((I * NT + n) * 2) * 64;
+          slot[l] = accY[n];
+          slot[64 + l] = accQ[n];
+        }
+        __syncthreads();
+        if (yh < NT) {
+          const f32x4 *slot = xch + ((I * NT + yh) * 2) * 64;
+          accY[0] = accY[yh] + slot[l];
+          accQ[0] = accQ[yh] + slot[64 + l];
         }
       }
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) {
         const int n = J::tile(w, u);
+        accO[r][u] = accQ[u];
         if (n >= NT) continue;
         f32x4 y;
 #pragma unroll
