@@ -27,6 +27,8 @@ namespace gdr {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -121,6 +123,12 @@ struct FragS {            // split bf16 hi + lo
 struct FragF {            // fp32
   float v[8];
 };
+struct FragH {            // plain fp16
+  f16x8 h;
+};
+struct FragHS {           // split fp16 hi + lo
+  f16x8 h, l;
+};
 
 template <class F> __device__ __forceinline__ F make_frag(const float (&x)[8]);
 
@@ -140,6 +148,22 @@ template <> __device__ __forceinline__ FragS make_frag<FragS>(const float (&x)[8
   }
   return f;
 }
+template <> __device__ __forceinline__ FragH make_frag<FragH>(const float (&x)[8]) {
+  FragH f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.h[e] = static_cast<f16>(x[e]);
+  return f;
+}
+template <> __device__ __forceinline__ FragHS make_frag<FragHS>(const float (&x)[8]) {
+  FragHS f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const f16 h = static_cast<f16>(x[e]);
+    f.h[e] = h;
+    f.l[e] = static_cast<f16>(x[e] - static_cast<float>(h));
+  }
+  return f;
+}
 template <> __device__ __forceinline__ FragF make_frag<FragF>(const float (&x)[8]) {
   FragF f;
 #pragma unroll
@@ -149,6 +173,9 @@ template <> __device__ __forceinline__ FragF make_frag<FragF>(const float (&x)[8
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8 &a, const f16x8 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -170,6 +197,10 @@ __device__ __forceinline__ void mma(f32x4 &c, const FragS &a, const FragS &b) {
   c = mfma_bf16(a.h, b.l, c);
   c = mfma_bf16(a.h, b.h, c);
 }
+__device__ __forceinline__ void mma(f32x4 &c, const FragH &a, const FragHS &b) {
+  c = mfma_f16(a.h, b.l, c);
+  c = mfma_f16(a.h, b.h, c);
+}
 __device__ __forceinline__ void mma(f32x4 &c, const FragF &a, const FragF &b) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) c = mfma_f32(a.v[s], b.v[s], c);
@@ -186,6 +217,14 @@ struct PrecF32 {
   using Plain = FragF;
   using Split = FragF;
   static constexpr bool kF32 = true;
+};
+// fp16 operands for the state scan of bf16 inputs: the prepared chunk
+// operands are single fp16 (11 significant bits, 2 bytes), the state and the
+// chunk intermediates split fp16 pairs.
+struct PrecF16 {
+  using Plain = FragH;
+  using Split = FragHS;
+  static constexpr bool kF32 = false;
 };
 
 // LDS storage of an operand that is read back as B fragments: element (n, k)
@@ -247,6 +286,35 @@ template <> struct OperandLds<PrecBF16> {
     FragS f;
     f.h = *reinterpret_cast<const bf16x8 *>(hi + n * ld + k);
     f.l = *reinterpret_cast<const bf16x8 *>(lo + n * ld + k);
+    return f;
+  }
+};
+
+template <> struct OperandLds<PrecF16> {
+  f16 *hi;
+  f16 *lo;
+  int ld;
+  static constexpr int kBytesPerElem = 4;
+  __device__ __forceinline__ void init(void *base, int n_rows, int ld_) {
+    hi = reinterpret_cast<f16 *>(base);
+    lo = hi + n_rows * ld_;
+    ld = ld_;
+  }
+  __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
+    typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 h, l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = static_cast<f16>(x[r]);
+      l[r] = static_cast<f16>(x[r] - static_cast<float>(h[r]));
+    }
+    *reinterpret_cast<f16x4 *>(hi + n * ld + k) = h;
+    *reinterpret_cast<f16x4 *>(lo + n * ld + k) = l;
+  }
+  __device__ __forceinline__ FragHS get(int n, int k) const {
+    FragHS f;
+    f.h = *reinterpret_cast<const f16x8 *>(hi + n * ld + k);
+    f.l = *reinterpret_cast<const f16x8 *>(lo + n * ld + k);
     return f;
   }
 };
@@ -333,9 +401,8 @@ template <> struct PlainLds<PrecF32> {
 // 16 x 32 elements as 64 fragments of eight consecutive columns, fragment
 // f = 16 q + r being row 16 i + r, columns 32 j + 8 q .. + 7: exactly the
 // operand lane f of a 16x16x32 MFMA reads, so a wave loads a block as one
-// contiguous run.  bf16 policy: plain block 1 KiB (fragment f at byte 16 f),
-// split block 2 KiB (hi fragments, then lo fragments at +1 KiB); fp32 policy:
-// 2 KiB blocks, fragment f at byte 32 f, for both kinds.
+// contiguous run.  fp16 tiles: 1 KiB blocks, fragment f at byte 16 f; fp32
+// tiles: 2 KiB blocks, fragment f at byte 32 f.
 struct FragPos {
   int blk, f, e;   // block, fragment, element within the fragment
 };
@@ -345,39 +412,23 @@ __device__ __forceinline__ FragPos frag_pos(int r, int k, int K) {
 
 template <class P> struct TileIO;
 
-template <> struct TileIO<PrecBF16> {
-  __device__ static unsigned char *plain_at(void *t, int blk, int f) {
+// fp16 tiles (operands prepared from bf16 inputs): plain only, 1 KiB blocks.
+template <> struct TileIO<PrecF16> {
+  __device__ static unsigned char *at(void *t, int blk, int f) {
     return static_cast<unsigned char *>(t) + blk * 1024 + f * 16;
   }
-  __device__ static unsigned char *split_at(void *t, int blk, int f) {
-    return static_cast<unsigned char *>(t) + blk * 2048 + f * 16;
-  }
   __device__ static void put_plain8(void *t, int blk, int f, const float (&x)[8]) {
-    bf16x8 h;
+    f16x8 h;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = to_bf16(x[e]);
-    *reinterpret_cast<bf16x8 *>(plain_at(t, blk, f)) = h;
+    for (int e = 0; e < 8; ++e) h[e] = static_cast<f16>(x[e]);
+    *reinterpret_cast<f16x8 *>(at(t, blk, f)) = h;
   }
-  __device__ static void put_split8(void *t, int blk, int f, const float (&x)[8]) {
-    const FragS v = make_frag<FragS>(x);
-    *reinterpret_cast<bf16x8 *>(split_at(t, blk, f)) = v.h;
-    *reinterpret_cast<bf16x8 *>(split_at(t, blk, f) + 1024) = v.l;
+  __device__ static void put_plain(void *t, FragPos p, float x) {
+    reinterpret_cast<f16 *>(at(t, p.blk, p.f))[p.e] = static_cast<f16>(x);
   }
-  __device__ static void put_split(void *t, FragPos p, float x) {
-    const bf16 h = to_bf16(x);
-    reinterpret_cast<bf16 *>(split_at(t, p.blk, p.f))[p.e] = h;
-    reinterpret_cast<bf16 *>(split_at(t, p.blk, p.f) + 1024)[p.e] = to_bf16(x - static_cast<float>(h));
-  }
-  __device__ static FragP get_plain(const void *t, int blk, int f) {
-    FragP v;
-    v.h = *reinterpret_cast<const bf16x8 *>(plain_at(const_cast<void *>(t), blk, f));
-    return v;
-  }
-  __device__ static FragS get_split(const void *t, int blk, int f) {
-    FragS v;
-    const unsigned char *p = split_at(const_cast<void *>(t), blk, f);
-    v.h = *reinterpret_cast<const bf16x8 *>(p);
-    v.l = *reinterpret_cast<const bf16x8 *>(p + 1024);
+  __device__ static FragH get_plain(const void *t, int blk, int f) {
+    FragH v;
+    v.h = *reinterpret_cast<const f16x8 *>(at(const_cast<void *>(t), blk, f));
     return v;
   }
 };
@@ -393,6 +444,7 @@ template <> struct TileIO<PrecF32> {
   }
   __device__ static void put_split8(void *t, int blk, int f, const float (&x)[8]) { put_plain8(t, blk, f, x); }
   __device__ static void put_split(void *t, FragPos p, float x) { at(t, p.blk, p.f)[p.e] = x; }
+  __device__ static void put_plain(void *t, FragPos p, float x) { at(t, p.blk, p.f)[p.e] = x; }
   __device__ static FragF get_plain(const void *t, int blk, int f) {
     const float *p = at(const_cast<void *>(t), blk, f);
     const float4 a = *reinterpret_cast<const float4 *>(p);

@@ -9,14 +9,13 @@ namespace gdr {
 // Workspace written by the prep kernel and read by the scan kernel: one
 // fragment-major tile (layout at TileIO in common.hpp) per (batch, head,
 // chunk) in each region, regions in this order, each 256-byte aligned:
-//   A   diag(beta) A_c     [C][C]    plain  per beta head
-//   L   L_c                [C][C]    split  per key head
-//   KB  Kbar_c             [C][d_k]  plain  per key head
-//   QB  Qbar_c             [C][d_k]  split  per key head
-//   KH  Khat_c^T           [d_k][C]  split  per key head
-//   GM  exp(Lambda_C)      [d_k]     fp32   per key head
-// plain: bf16 (bf16 inputs) or fp32; split: bf16 hi and lo fragments (bf16
-// inputs) or fp32.  GM is a plain fp32 vector.
+//   A   diag(beta) A_c     [C][C]    per beta head
+//   L   L_c                [C][C]    per key head
+//   KB  Kbar_c             [C][d_k]  per key head
+//   QB  Qbar_c             [C][d_k]  per key head
+//   KH  Khat_c^T           [d_k][C]  per key head
+//   GM  exp(Lambda_C)      [d_k]     per key head, fp32 vector
+// Tile elements are fp16 for bf16 inputs and fp32 for fp32 inputs.
 struct WsLayout {
   size_t tile[6];   // bytes per tile, in region order
   size_t off[6];    // region offsets
@@ -25,13 +24,13 @@ struct WsLayout {
 enum WsRegion { kWsA = 0, kWsL, kWsKB, kWsQB, kWsKH, kWsGM };
 
 __host__ __device__ inline WsLayout ws_layout(int B, int H_k, int H_beta, int N_c, int C, int d_k, bool bf16) {
-  const size_t pb = bf16 ? 2 : 4, sb = 4;
+  const size_t pb = bf16 ? 2 : 4;
   WsLayout w;
   w.tile[kWsA] = pb * C * C;
-  w.tile[kWsL] = sb * C * C;
+  w.tile[kWsL] = pb * C * C;
   w.tile[kWsKB] = pb * C * d_k;
-  w.tile[kWsQB] = sb * C * d_k;
-  w.tile[kWsKH] = sb * d_k * C;
+  w.tile[kWsQB] = pb * C * d_k;
+  w.tile[kWsKH] = pb * d_k * C;
   w.tile[kWsGM] = 4 * (size_t)d_k;
   size_t at = 0;
   for (int r = 0; r < 6; ++r) {

@@ -3,9 +3,9 @@
 // with division-free relative decay, then for every beta head solve
 // A_c = (I + G_c diag(beta))^{-1}.  Everything the sequential scan needs from
 // q, k, beta and log alpha is written to the workspace here, where all
-// chunks are processed in parallel, as ready MFMA operands: diag(beta) A_c
-// (plain), L_c (split), Kbar_c (plain), Qbar_c and Khat_c^T (split) and
-// exp(Lambda_C).
+// chunks are processed in parallel, as ready MFMA operands (fp16 tiles for
+// bf16 inputs, fp32 for fp32 inputs): diag(beta) A_c, L_c, Kbar_c, Qbar_c,
+// Khat_c^T, and exp(Lambda_C).
 //
 // Systolic Linear Attention (paperpeel 2611.06828):
 //  - cumulative log-decay Lambda and the chunk matrices: Table 2;
@@ -29,6 +29,8 @@
 // any channel the block is evaluated element by element with the causal mask
 // applied before the exponential.  No exponential of a positive Lambda
 // difference on the causal side is ever formed.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
   constexpr int NKV = C * DK / (8 * 256);   // bound on 8-element log-alpha vectors per thread
   constexpr int KS = DK / 32;
   using Split = typename P::Split;
-  using IO = TileIO<P>;
+  // workspace tiles: fp16 for bf16 inputs, fp32 for fp32 inputs
+  using IO = TileIO<typename std::conditional<P::kF32, PrecF32, PrecF16>::type>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float *smem = reinterpret_cast<float *>(smem_raw);
   const int c = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       ak[s] = make_frag<Split>(yk);
       aq[s] = make_frag<Split>(yq);
       IO::put_plain8(tKB, I * KS + s, l, kbar);
-      IO::put_split8(tQB, I * KS + s, l, qbar);
+      IO::put_plain8(tQB, I * KS + s, l, qbar);
       // Khat^T: lane (token lr, channels 8 lq ..) writes, lane (channel
       // 16 (l >> 5) + (l & 15), tokens 8 g ..) reads back a fragment
 #pragma unroll
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       const float4 u1 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g + 4);
       xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      IO::put_split8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+      IO::put_plain8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
     }
     if (r + 1 < NR) {                                  // next owned block's rows
       load_rows(kt, kbase, own(r + 1));
@@ -480,12 +483,12 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
         gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[q4] : 0.f;
-        IO::put_split(tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[q4] : 0.f);
+        IO::put_plain(tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[q4] : 0.f);
       }
     }
   }
   for (int i = tid; i < C * C; i += blockDim.x) {
-    if ((i / C) / 16 < (i % C) / 16) IO::put_split(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
+    if ((i / C) / 16 < (i % C) / 16) IO::put_plain(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
   }
 
   // ---- solve per beta head (beta loaded here: short-lived registers)

@@ -16,10 +16,12 @@
 // recurrence (each column of S evolves on its own), so tiling d_v across
 // workgroups is exact.
 //
-// Operand precision (bf16 policy): Kbar and A_c plain bf16; S, Y, Qbar, L_c,
-// E and Khat split into bf16 hi + lo (x = hi + lo to ~16 bits).  Rounding
-// any one of the latter to plain bf16 alone breaks a 1e-2 max-error bar on
-// the per-channel-gate workload; Kbar or A_c alone costs about 1e-3.
+// Operand precision (bf16 inputs): the prepared operands diag(beta) A_c, L_c,
+// Kbar, Qbar and Khat are single fp16 (11 significant bits); the state S and
+// the intermediates Y and E are split fp16 pairs (x = hi + lo, hi = fp16(x)),
+// so every product is two fp16 MFMAs with fp32 accumulation.  bf16 (8 bits)
+// is too coarse for Qbar, Khat, L, S, Y and E: rounding any one of them to
+// bf16 breaks a 1e-2 max-error bar on the per-channel-gate workload.
 //
 // Organisation.  Eight waves, two per SIMD, so one wave's memory and LDS
 // latency hides behind the other's arithmetic.  Jobs per chunk: Y, E and O
@@ -135,10 +137,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 
   // ---------------------------------------------------- prefetch registers
   Plain fkb[J::RPW][YKS];             // Kbar rows of each row block (this wave's channel steps)
-  Split fqb[J::RPW][YKS];             // Qbar rows
+  Plain fqb[J::RPW][YKS];             // Qbar rows
   Plain fa[J::RPW][CSTEPS];           // diag(beta) A_c rows
-  Split fl[J::RPW][CSTEPS];           // L_c rows
-  Split fkh[SJ::RPW][CSTEPS];         // Khat^T rows (channels) of each S block
+  Plain fl[J::RPW][CSTEPS];           // L_c rows
+  Plain fkh[SJ::RPW][CSTEPS];         // Khat^T rows (channels) of each S block
   f32x4 gm[SJ::RPW];                  // exp(Lambda_C) of the block's rows of S
   TIn vr[J::RPW][J::TPW][4];          // v entries (D layout)
 
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
       for (int s = 0; s < YKS; ++s) {
         fkb[r][s] = IO::get_plain(tkb, I * KSTEPS + yh * YKS + s, l);
-        fqb[r][s] = IO::get_split(tqb, I * KSTEPS + yh * YKS + s, l);
+        fqb[r][s] = IO::get_plain(tqb, I * KSTEPS + yh * YKS + s, l);
       }
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) {
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     for (int r = 0; r < J::RPW; ++r) {
 #pragma unroll
       for (int s = 0; s < CSTEPS; ++s)
-        fl[r][s] = IO::get_split(tl, J::blk(w, r) * CSTEPS + s, l);
+        fl[r][s] = IO::get_plain(tl, J::blk(w, r) * CSTEPS + s, l);
     }
   };
   auto load_s = [&](int c) __attribute__((always_inline)) {
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     for (int r = 0; r < SJ::RPW; ++r) {
       const int i0 = 16 * SJ::blk(w, r);
 #pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) fkh[r][s] = IO::get_split(tkh, SJ::blk(w, r) * CSTEPS + s, l);
+      for (int s = 0; s < CSTEPS; ++s) fkh[r][s] = IO::get_plain(tkh, SJ::blk(w, r) * CSTEPS + s, l);
       gm[r] = *reinterpret_cast<const f32x4 *>(tgm + i0 + 4 * lq);
     }
   };
@@ -433,8 +435,8 @@ static hipError_t launch_scan_shape(const ChunkArgs &a, hipStream_t s) {
 
 hipError_t launch_scan(const ChunkArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream) {
   if (in_bf16) {
-    if (out_bf16) return launch_scan_shape<bf16, bf16, PrecBF16>(a, stream);
-    return launch_scan_shape<bf16, float, PrecBF16>(a, stream);
+    if (out_bf16) return launch_scan_shape<bf16, bf16, PrecF16>(a, stream);
+    return launch_scan_shape<bf16, float, PrecF16>(a, stream);
   }
   if (out_bf16) return launch_scan_shape<float, bf16, PrecF32>(a, stream);
   return launch_scan_shape<float, float, PrecF32>(a, stream);

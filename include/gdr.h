@@ -90,23 +90,21 @@ typedef struct {
  * head so that the sequential state scan only multiplies.  Six regions, in
  * this order, each a stack of tiles indexed [B][heads][N_c] (N_c =
  * ceil(T / C), H_beta = H_v, or H_k with beta_per_key_head):
- *   0  A    diag(beta_c) A_c           C x C     plain   per beta head
- *   1  L    L_c (decayed q.k, t >= j)  C x C     split   per key head
- *   2  KB   Kbar_c = K (.) exp(Lambda) C x d_k   plain   per key head
- *   3  QB   Qbar_c = Q (.) exp(Lambda) C x d_k   split   per key head
+ *   0  A    diag(beta_c) A_c           C x C     per beta head
+ *   1  L    L_c (decayed q.k, t >= j)  C x C     per key head
+ *   2  KB   Kbar_c = K (.) exp(Lambda) C x d_k   per key head
+ *   3  QB   Qbar_c = Q (.) exp(Lambda) C x d_k   per key head
  *   4  KH   Khat_c^T, Khat = K (.) exp(Lambda_C - Lambda)
- *                                      d_k x C   split   per key head
- *   5  GM   exp(Lambda_C) per channel  d_k       fp32    per key head
- * Tiles are fragment-major, the order in which 16x16x32 MFMA operands are
- * read: an R x K tile is (R/16) x (K/32) blocks, row-block-major; a block is
- * 64 fragments of 8 consecutive columns, fragment f = 16 q + r holding row r,
- * columns 8 q .. 8 q + 7 of the block.  plain (bf16 inputs): bf16, 1 KiB per
- * block, fragment f at byte 16 f.  split (bf16 inputs): x = hi + lo with hi =
- * bf16(x), lo = bf16(x - hi) (about 16 significant bits), 2 KiB per block:
- * hi fragments at 16 f, lo fragments at 1024 + 16 f.  fp32 inputs: plain and
- * split are fp32, 2 KiB per block, fragment f at byte 32 f.  GM is a plain
- * fp32 vector.  Token rows (columns of KH) of a short final chunk past T are
- * zero and its gate values are those of its last real token.  Region
+ *                                      d_k x C   per key head
+ *   5  GM   exp(Lambda_C) per channel  d_k       per key head, fp32
+ * Tile elements are fp16 for bf16 inputs (round to nearest even) and fp32
+ * for fp32 inputs.  Tiles are fragment-major, the order in which 16x16x32
+ * MFMA operands are read: an R x K tile is (R/16) x (K/32) blocks,
+ * row-block-major; a block is 64 fragments of 8 consecutive columns,
+ * fragment f = 16 q + r holding row r, columns 8 q .. 8 q + 7 of the block,
+ * at byte 16 f (fp16, 1 KiB blocks) or 32 f (fp32, 2 KiB blocks).  Token rows
+ * (columns of KH) of a short final chunk past T are zero and its gate values
+ * are those of its last real token.  Region
  * offsets: gdr_chunk_workspace_layout.
  */
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p);

@@ -47,51 +47,41 @@ def run_chunk(dev, w, h0=None, solve="exact", **kw):
     return o, hT
 
 
-def _bf16(u16):
-    return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32)
-
-
 def decode_workspace(ws, p):
     """The six prepared regions of a workspace (include/gdr.h) as fp64 arrays:
     A [B,H_beta,N_c,C,C], L [B,H_k,N_c,C,C], KB and QB [B,H_k,N_c,C,d_k],
     KH [B,H_k,N_c,d_k,C], GM [B,H_k,N_c,d_k].  Tiles are fragment-major: an
     R x K tile is (R/16) x (K/32) blocks of 64 fragments, fragment 16 q + r
-    holding row r and columns 8 q .. 8 q + 7 of its block; split bf16 blocks
-    hold the hi fragments then the lo fragments, and the value is hi + lo."""
+    holding row r and columns 8 q .. 8 q + 7 of its block; elements are fp16
+    for bf16 inputs and fp32 for fp32 inputs."""
     from gated_delta_rule_87_amd import binding as gb
     lay = gb.gdr_chunk_workspace_layout(p)
     raw = ws.detach().cpu().contiguous().view(torch.uint8).numpy()
-    bf16 = p.in_dtype == gb.GDR_BF16
+    elem = np.float16 if p.in_dtype == gb.GDR_BF16 else np.float32
+    es = np.dtype(elem).itemsize
     C, dk = p.chunk, p.d_k
     nc = -(-p.T // C)
     hb = p.H_k if p.beta_per_key_head else p.H_v
 
-    def region(name, heads, shape, kind):
+    def region(name, heads, shape, vector=False):
         n_tiles = p.B * heads * nc
         m = int(np.prod(shape))
         off = lay[name]
-        if kind == "vector":
+        if vector:
             x = raw[off:off + 4 * n_tiles * m].view(np.float32).astype(np.float64)
             return x.reshape((p.B, heads, nc) + tuple(shape))
         R, K = shape
-        blocks = (n_tiles, R // 16, K // 32)
-        if not bf16:
-            x = raw[off:off + 4 * n_tiles * m].view(np.float32).astype(np.float64).reshape(blocks + (4, 16, 8))
-        elif kind == "plain":
-            x = _bf16(raw[off:off + 2 * n_tiles * m].view(np.uint16)).astype(np.float64)
-            x = x.reshape(blocks + (4, 16, 8))
-        else:
-            u = raw[off:off + 4 * n_tiles * m].view(np.uint16).reshape(blocks + (2, 4, 16, 8))
-            x = _bf16(u[..., 0, :, :, :]).astype(np.float64) + _bf16(u[..., 1, :, :, :]).astype(np.float64)
+        x = raw[off:off + es * n_tiles * m].view(elem).astype(np.float64)
+        x = x.reshape((n_tiles, R // 16, K // 32, 4, 16, 8))
         # (tile, row block, col block, q, r, e) -> (tile, row block, r, col block, q, e)
         x = x.transpose(0, 1, 4, 2, 3, 5).reshape(n_tiles, R, K)
         return x.reshape((p.B, heads, nc, R, K))
 
     return {
-        "A": region("A", hb, (C, C), "plain"),
-        "L": region("L", p.H_k, (C, C), "split"),
-        "KB": region("KB", p.H_k, (C, dk), "plain"),
-        "QB": region("QB", p.H_k, (C, dk), "split"),
-        "KH": region("KH", p.H_k, (dk, C), "split"),
-        "GM": region("GM", p.H_k, (dk,), "vector"),
+        "A": region("A", hb, (C, C)),
+        "L": region("L", p.H_k, (C, C)),
+        "KB": region("KB", p.H_k, (C, dk)),
+        "QB": region("QB", p.H_k, (C, dk)),
+        "KH": region("KH", p.H_k, (dk, C)),
+        "GM": region("GM", p.H_k, (dk,), vector=True),
     }

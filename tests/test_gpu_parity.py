@@ -121,7 +121,8 @@ def expected_operands(x, w):
 def test_prepared_workspace(name, solve):
     """Every prepared chunk quantity against the fp64 chunk pieces: diag(beta)
     A_c, L_c, Kbar, Qbar, Khat^T, exp(Lambda_C).  Bars on max|err| / max|ref|:
-    plain bf16 tiles 4e-3 (one bf16 rounding), split tiles 1e-4, fp32 1e-5."""
+    fp16 tiles (bf16 inputs) 1e-3 (one fp16 rounding is 2^-11 relative),
+    fp32 tiles and the fp32 gate vector 1e-5."""
     w = SMALL[name]
     raw, x = draw(w)
     dev = device_inputs(raw)
@@ -141,10 +142,9 @@ def test_prepared_workspace(name, solve):
     beta = beta.reshape(B, nc, C, -1).transpose(0, 3, 1, 2)      # [B, H_beta, N_c, C]
     ref = dict(expected_operands(x, w), A=beta[..., None] * A_ref, L=L_ref)
     f32 = w.dtype == "f32"
-    bars = {"A": 1e-5 if f32 else 4e-3, "KB": 1e-5 if f32 else 4e-3}
     for key in ("A", "L", "KB", "QB", "KH", "GM"):
         err = np.max(np.abs(got[key] - ref[key])) / np.max(np.abs(ref[key]))
-        bar = bars.get(key, 1e-5 if f32 else 1e-4)
+        bar = 1e-5 if (f32 or key == "GM") else 1e-3
         print(f"  {key}: max err / max ref = {err:.3e} (bar {bar:g})", flush=True)
         assert err <= bar, key
 
