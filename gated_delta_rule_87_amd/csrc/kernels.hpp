@@ -79,6 +79,6 @@ hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream
 // Whether a shape is compiled in (the API layer reports GDR_ERR_UNSUPPORTED otherwise).
 bool prep_supported(int C, int d_k, int G);
 int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16);
-size_t prep_lds_bytes(int C, int G);
+size_t prep_lds_bytes(int C, int d_k, int G);
 
 }  // namespace gdr

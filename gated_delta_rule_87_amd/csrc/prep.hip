@@ -29,6 +29,17 @@
 // any channel the block is evaluated element by element with the causal mask
 // applied before the exponential.  No exponential of a positive Lambda
 // difference on the causal side is ever formed.
+//
+// Chunk pivot.  When the range of Lambda over the whole chunk is within
+// kPivotRange in every channel (true for any chunk of mild decay), the first
+// token of the chunk serves as the pivot of every pair: the row operand
+// K_t (.) exp(Lambda_t - Lambda_0) and the column operand
+// K_j (.) exp(Lambda_0 - Lambda_j) then no longer depend on the pair, each
+// block builds both once, and a pair is MFMA work only.  The factors stay in
+// [exp(-kPivotRange), exp(kPivotRange)], so neither overflows nor underflows
+// in fp32 and every product keeps its relative precision; entries with j > t
+// can be large but are masked.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -50,10 +61,45 @@ __host__ __device__ inline int prep_tmp_floats(int C) {
 }
 
 constexpr int kXbLd = 20;   // row stride (floats) of the per-wave transpose buffers
+constexpr int kChunkWide = 8;  // flags slot: the chunk's decay range exceeds kPivotRange
 
-size_t prep_lds_bytes(int C, int G) {
-  return sizeof(float) * (size_t)(prep_region0_floats(C, G) + C * prep_ld(C) + prep_tmp_floats(C) + C) +
+// Chunk-pivot column operands of blocks 0 .. NB - 2 (split fragments, two
+// 1 KiB planes per block and channel step); only C = 64 (one row block per
+// wave) takes the chunk-pivot route.
+__host__ __device__ inline int prep_colop_floats(int C, int DK) {
+  return C == 64 ? (C / 16 - 1) * DK * 16 : 0;
+}
+// The region after Lambda: G (slow route) or the solve's A (chunk-pivot
+// route), followed by the solve's scratch; the chunk-pivot column operands
+// overlay it before the solve.
+__host__ __device__ inline int prep_union_floats(int C, int DK) {
+  const int solve = C * prep_ld(C) + prep_tmp_floats(C), colop = prep_colop_floats(C, DK);
+  return solve > colop ? solve : colop;
+}
+
+size_t prep_lds_bytes(int C, int DK, int G) {
+  return sizeof(float) * (size_t)(prep_region0_floats(C, G) + prep_union_floats(C, DK) + C) +
          sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd;
+}
+
+// One lane's 32-byte fragment in LDS as two planes of 16 bytes per lane, so
+// a wave's read of a plane is 1 KiB of consecutive bytes.
+template <class F>
+__device__ __forceinline__ void lds_put_frag(unsigned char *base, int idx, const F &f) {
+  static_assert(sizeof(F) == 32, "two 16-byte planes");
+  uint4 u[2];
+  __builtin_memcpy(u, &f, sizeof(F));
+  *reinterpret_cast<uint4 *>(base + 2048 * idx + 16 * lane_id()) = u[0];
+  *reinterpret_cast<uint4 *>(base + 2048 * idx + 1024 + 16 * lane_id()) = u[1];
+}
+template <class F>
+__device__ __forceinline__ F lds_get_frag(const unsigned char *base, int idx) {
+  uint4 u[2];
+  u[0] = *reinterpret_cast<const uint4 *>(base + 2048 * idx + 16 * lane_id());
+  u[1] = *reinterpret_cast<const uint4 *>(base + 2048 * idx + 1024 + 16 * lane_id());
+  F f;
+  __builtin_memcpy(&f, u, sizeof(F));
+  return f;
 }
 
 // --------------------------------------------------------------- fp32 tiles
@@ -96,7 +142,7 @@ __device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, i
 // substitution (one lane per column), then block-doubling merges
 // A[B,T] = -A[B,B] (M[B,T] A[T,T]) with fp32 MFMA.
 template <int C>
-__device__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
+__device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
@@ -171,7 +217,7 @@ __device__ void solve_exact(const float *gmat, const float *bet, float *amat, fl
 // block of M X needs only the same column block of X, and X Rm[:, J] needs the
 // columns of X at and right of J, which are still the old ones.
 template <int C>
-__device__ void solve_neumann(const float *gmat, const float *bet, float *amat, float *tmp, int order,
+__device__ __forceinline__ void solve_neumann(const float *gmat, const float *bet, float *amat, float *tmp, int order,
                               int residual) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
@@ -241,120 +287,149 @@ __device__ void solve_neumann(const float *gmat, const float *bet, float *amat, 
   }
 }
 
-// ------------------------------------------------------------------ kernel
+// ------------------------------------------------------------------ kernels
 // Loads are unconditional (tokens past T read a clamped, valid address and
 // are zeroed where used): a load behind a branch forces an early wait for
 // every memory operation in flight.
+//
+// Two kernels share the per-chunk steps below.  The chunk-pivot kernel
+// (C = 64) takes every chunk; a chunk whose decay range is too wide for the
+// chunk pivot is left to the block-pivot kernel, which runs after it and
+// finds such chunks by a mark in their exp(Lambda_C) row (a negative value,
+// which an exponential never produces).  For C = 128 the block-pivot kernel
+// takes every chunk.
+
+constexpr float kWideMark = -1.f;
+
+// One (batch, key head, chunk) work item: indices, LDS carve-up, pointers.
 template <typename TIn, class P, int C, int DK>
-__global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
-  constexpr int NB = C / 16;
-  constexpr int NKV = C * DK / (8 * 256);   // bound on 8-element log-alpha vectors per thread
-  constexpr int KS = DK / 32;
+struct PrepItem {
+  static constexpr int NB = C / 16;
+  static constexpr int NKV = C * DK / (8 * 256);  // bound on 8-element log-alpha vectors per thread
+  static constexpr int KS = DK / 32;
   using Split = typename P::Split;
   // workspace tiles: fp16 for bf16 inputs, fp32 for fp32 inputs
   using IO = TileIO<typename std::conditional<P::kF32, PrecF32, PrecF16>::type>;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  float *smem = reinterpret_cast<float *>(smem_raw);
-  const int c = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int G = a.G, gs = a.gshift, T = a.T;
-  const int t0 = c * C;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int lr = l & 15, lq = l >> 4;
-  const int lgG = __builtin_ctz(DK) - gs;
-  const int Rb = a.H_beta / a.H_k;
 
-  float *lam = smem;                                   // [C][G] (Gram phase)
-  float *amat = smem;                                  // [C][C + 4] (solve phase, aliases lam)
-  float *gmat = smem + prep_region0_floats(C, G);      // [C][C + 4]
-  float *tmp = gmat + C * prep_ld(C);
-  float *bet = tmp + prep_tmp_floats(C);               // [C]
-  int *flags = reinterpret_cast<int *>(bet + C);       // [NB]
-  float *xbuf = reinterpret_cast<float *>(flags + 16);  // [4 waves][32][kXbLd]
+  const ChunkArgs &a;
+  const int c, hk, b, G, gs, T, t0, tid, w, l, lr, lq, lgG, Rb;
+  // Block-pivot route: Lambda, then A, over region 0; G in the union region.
+  // Chunk-pivot route: the column operands in the union region until the
+  // pairs are done, then G over region 0 (Lambda is dead by then) and A in
+  // the union region.  The solve's scratch follows C (C + 4) floats into the
+  // union region on both routes.
+  float *const smem, *const lam, *const ureg, *const tmp, *const bet;
+  int *const flags;                                    // [NB] block ranges, [kChunkWide]
+  float *const xb;                                     // this wave's transpose buffer [32 channels][kXbLd]
+  const TIn *const la, *const bp, *const kbase, *const qbase;
+  const size_t row_stride, la_row;                     // token strides of q / k and of log alpha
+  void *const tKB, *const tQB, *const tKH, *const tL;
 
-  const TIn *la = reinterpret_cast<const TIn *>(a.log_alpha);
-  const TIn *qp = reinterpret_cast<const TIn *>(a.q);
-  const TIn *kp = reinterpret_cast<const TIn *>(a.k);
-  const TIn *bp = reinterpret_cast<const TIn *>(a.beta);
-  const size_t row_stride = (size_t)a.H_k * DK;        // token stride of q, k
-  const size_t la_row = (size_t)a.H_k * G;
-  auto tok = [&](int t) { return (size_t)b * T + min(t0 + t, T - 1); };
+  __device__ __forceinline__ PrepItem(const ChunkArgs &a_, int c_, int hk_, int b_, float *smem_)
+      : a(a_), c(c_), hk(hk_), b(b_), G(a_.G), gs(a_.gshift), T(a_.T), t0(c_ * C), tid(threadIdx.x),
+        w(wave_id()), l(lane_id()), lr(lane_id() & 15), lq(lane_id() >> 4),
+        lgG(__builtin_ctz(DK) - a_.gshift), Rb(a_.H_beta / a_.H_k), smem(smem_), lam(smem_),
+        ureg(smem_ + prep_region0_floats(C, a_.G)), tmp(ureg + C * prep_ld(C)),
+        bet(ureg + prep_union_floats(C, DK)), flags(reinterpret_cast<int *>(bet + C)),
+        xb(reinterpret_cast<float *>(flags + 16) + wave_id() * 32 * kXbLd),
+        la(reinterpret_cast<const TIn *>(a_.log_alpha)), bp(reinterpret_cast<const TIn *>(a_.beta)),
+        kbase(reinterpret_cast<const TIn *>(a_.k) + (size_t)hk_ * DK),
+        qbase(reinterpret_cast<const TIn *>(a_.q) + (size_t)hk_ * DK), row_stride((size_t)a_.H_k * DK),
+        la_row((size_t)a_.H_k * a_.G), tKB(ws_tile(a_, kWsKB, a_.H_k, hk_, b_, c_)),
+        tQB(ws_tile(a_, kWsQB, a_.H_k, hk_, b_, c_)), tKH(ws_tile(a_, kWsKH, a_.H_k, hk_, b_, c_)),
+        tL(ws_tile(a_, kWsL, a_.H_k, hk_, b_, c_)) {}
 
-  // ---- all loads of the chunk's key side, issued together
-  Raw8<TIn> lav[NKV];
-  TIn las[NKV];
-  const bool la_vec = G >= 8;
-  if (la_vec) {
-#pragma unroll
-    for (int j = 0; j < NKV; ++j) {
-      const int e = min(8 * (tid + 256 * j), C * G - 8);
-      lav[j].load(la + tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1)));
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NKV; ++j) {
-      const int e = min(tid + 256 * j, C * G - 1);
-      las[j] = la[tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1))];
-    }
-  }
-  // Gram and L by 16-token row blocks: wave w owns blocks w (and 7 - w when
-  // C = 128), builds their decayed row operands once and pairs them with every
-  // earlier block.
-  constexpr int NR = NB / 4;                           // row blocks per wave
-  auto own = [&](int r) { return (r & 1) ? 4 * r + 3 - w : 4 * r + w; };
-  const TIn *kbase = kp + (size_t)hk * DK;
-  const TIn *qbase = qp + (size_t)hk * DK;
-  Raw8<TIn> kt[KS], qt[KS], kj[KS];
-  auto load_rows = [&](Raw8<TIn> (&dst)[KS], const TIn *base, int blk) __attribute__((always_inline)) {
+  __device__ __forceinline__ size_t tok(int t) const { return (size_t)b * T + min(t0 + t, T - 1); }
+
+  // rows 16 blk + lr of a q / k head, channels 32 s + 8 lq ..
+  __device__ __forceinline__ void load_rows(Raw8<TIn> (&dst)[KS], const TIn *base, int blk) const {
     const size_t rt = tok(16 * blk + lr) * row_stride;
 #pragma unroll
     for (int s = 0; s < KS; ++s) dst[s].load(base + rt + 32 * s + 8 * lq);
-  };
-  load_rows(kt, kbase, own(0));
-  load_rows(qt, qbase, own(0));
-  load_rows(kj, kbase, 0);
+  }
 
-  // ---- Lambda: raw log alpha -> lam, then in-place prefix sum per column
-  if (la_vec) {
+  // Raw log alpha of the chunk, in flight between issue and use.
+  struct LaRegs {
+    Raw8<TIn> v[NKV];
+    TIn s[NKV];
+  };
+  __device__ __forceinline__ void issue_la(LaRegs &r) const {
+    if (G >= 8) {
 #pragma unroll
-    for (int j = 0; j < NKV; ++j) {
-      const int e = 8 * (tid + 256 * j);
-      if (e < C * G) {
-        const int t = e >> lgG, g = e & (G - 1);
-        float x[8];
-        lav[j].to_float(x);
-        const float keep = (t0 + t < T) ? 1.f : 0.f;
-        *reinterpret_cast<float4 *>(lam + t * G + g) = make_float4(x[0] * keep, x[1] * keep, x[2] * keep, x[3] * keep);
-        *reinterpret_cast<float4 *>(lam + t * G + g + 4) = make_float4(x[4] * keep, x[5] * keep, x[6] * keep, x[7] * keep);
+      for (int j = 0; j < NKV; ++j) {
+        const int e = min(8 * (tid + 256 * j), C * G - 8);
+        r.v[j].load(la + tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1)));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NKV; ++j) {
+        const int e = min(tid + 256 * j, C * G - 1);
+        r.s[j] = la[tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1))];
       }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NKV; ++j) {
-      const int e = tid + 256 * j;
-      if (e < C * G) lam[e] = (t0 + (e >> lgG) < T) ? static_cast<float>(las[j]) : 0.f;
-    }
   }
-  if (tid < NB) flags[tid] = 0;
-  for (int i = tid; i < C * (C + 4); i += blockDim.x) gmat[i] = 0.f;
-  __syncthreads();
-  for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
-  __syncthreads();
-  for (int idx = tid; idx < NB * G; idx += blockDim.x) {
-    const int I = idx / G, g = idx - I * G;
-    float lo = lam[(16 * I) * G + g], hi = lo;
+
+  // Lambda = in-chunk prefix sum of log alpha per decay group (Systolic
+  // Linear Attention, Table 2), and the decay range flags: per 16-token block
+  // and over the chunk.  Ends with a barrier.
+  __device__ __forceinline__ void lambda(const LaRegs &r) {
+    if (G >= 8) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      const float x = lam[(16 * I + r) * G + g];
-      lo = fminf(lo, x);
-      hi = fmaxf(hi, x);
+      for (int j = 0; j < NKV; ++j) {
+        const int e = 8 * (tid + 256 * j);
+        if (e < C * G) {
+          const int t = e >> lgG, g = e & (G - 1);
+          float x[8];
+          r.v[j].to_float(x);
+          const float keep = (t0 + t < T) ? 1.f : 0.f;
+          *reinterpret_cast<float4 *>(lam + t * G + g) =
+              make_float4(x[0] * keep, x[1] * keep, x[2] * keep, x[3] * keep);
+          *reinterpret_cast<float4 *>(lam + t * G + g + 4) =
+              make_float4(x[4] * keep, x[5] * keep, x[6] * keep, x[7] * keep);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NKV; ++j) {
+        const int e = tid + 256 * j;
+        if (e < C * G) lam[e] = (t0 + (e >> lgG) < T) ? static_cast<float>(r.s[j]) : 0.f;
+      }
     }
-    if (!(hi - lo <= kPivotRange)) atomicOr(&flags[I], 1);
+    if (tid < 16) flags[tid] = 0;
+    __syncthreads();
+    for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
+    __syncthreads();
+    // several threads may store the same 1
+    for (int g = tid; g < G; g += blockDim.x) {
+      float clo = lam[g], chi = clo;
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        float lo = lam[(16 * I) * G + g], hi = lo;
+#pragma unroll
+        for (int q = 1; q < 16; ++q) {
+          const float x = lam[(16 * I + q) * G + g];
+          lo = fminf(lo, x);
+          hi = fmaxf(hi, x);
+        }
+        if (!(hi - lo <= kPivotRange)) flags[I] = 1;
+        clo = fminf(clo, lo);
+        chi = fmaxf(chi, hi);
+      }
+      if (!(chi - clo <= kPivotRange)) flags[kChunkWide] = 1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
+
+  __device__ __forceinline__ float *gm_row() const {
+    return reinterpret_cast<float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c));
+  }
+  __device__ __forceinline__ void write_gm() const {
+    if (tid < DK) gm_row()[tid] = __expf(lam[(C - 1) * G + (tid >> gs)]);
+  }
 
   // Lambda of row t for eight consecutive channels (vector reads per channel,
   // one broadcast read when the eight share a decay group)
-  auto lam8 = [&](int t, int ch0, float (&x)[8]) __attribute__((always_inline)) {
+  __device__ __forceinline__ void lam8(int t, int ch0, float (&x)[8]) const {
     if (gs == 0) {
       const float4 u = *reinterpret_cast<const float4 *>(lam + t * G + ch0);
       const float4 v = *reinterpret_cast<const float4 *>(lam + t * G + ch0 + 4);
@@ -367,28 +442,205 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = lam[t * G + ((ch0 + e) >> gs)];
     }
-  };
+  }
 
-  // ---- per row block I owned by this wave:
-  //  (1) the scan operands of its 16 tokens (Systolic Linear Attention,
-  //      Table 2): Kbar = K (.) exp(Lambda_t), Qbar = Q (.) exp(Lambda_t), and
-  //      Khat = K (.) exp(Lambda_C - Lambda_t), the last transposed through a
-  //      small per-wave LDS buffer into channel-row fragments;
-  //  (2) the pivot-decayed row operands K (.) exp(Lambda_t - Lambda_p) and
-  //      Q (.) exp(Lambda_t - Lambda_p), p = first token of I, kept as split
-  //      fragments;
-  //  (3) Gram and L for the pairs (I, J), J <= I, each one MFMA product with the
-  //      decayed keys K_J (.) exp(Lambda_p - Lambda_j) of block J.
-  // Every exponent on the causal side is <= 0, except on a diagonal block,
-  // where it is at most the block's decay range (<= kPivotRange unless the
-  // block is flagged and evaluated entry by entry).
-  void *tKB = ws_tile(a, kWsKB, a.H_k, hk, b, c);
-  void *tQB = ws_tile(a, kWsQB, a.H_k, hk, b, c);
-  void *tKH = ws_tile(a, kWsKH, a.H_k, hk, b, c);
-  void *tL = ws_tile(a, kWsL, a.H_k, hk, b, c);
-  if (tid < DK) reinterpret_cast<float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c))[tid] =
-      __expf(lam[(C - 1) * G + (tid >> gs)]);
-  float *xb = xbuf + w * 32 * kXbLd;                   // this wave's transpose buffer [32 channels][kXbLd]
+  // The scan operands of channel step s of block I (Systolic Linear
+  // Attention, Table 2; lane: token 16 I + lr, channels 32 s + 8 lq ..):
+  // Kbar = K (.) exp(Lambda_t), Qbar = Q (.) exp(Lambda_t), and
+  // Khat = K (.) exp(Lambda_C - Lambda_t), the last transposed through the
+  // wave's LDS buffer into channel-row fragments.  lt, lc: Lambda of the
+  // token and of the last token.
+  __device__ __forceinline__ void scan_operands(int I, int s, const float (&xk)[8], const float (&xq)[8],
+                                                const float (&lt)[8], const float (&lc)[8], float mt) const {
+    float kbar[8], qbar[8], kh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = __expf(lt[e]) * mt;
+      const float h = __expf(lc[e] - lt[e]) * mt;
+      kbar[e] = xk[e] * d;
+      qbar[e] = xq[e] * d;
+      kh[e] = xk[e] * h;
+    }
+    IO::put_plain8(tKB, I * KS + s, l, kbar);
+    IO::put_plain8(tQB, I * KS + s, l, qbar);
+    // Khat^T: lane (token lr, channels 8 lq ..) writes, lane (channel
+    // 16 (l >> 5) + (l & 15), tokens 8 g ..) reads back a fragment
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xb[(8 * lq + e) * kXbLd + lr] = kh[e];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int chl = 16 * (l >> 5) + (l & 15), g = (l >> 4) & 1;
+    float xt[8];
+    const float4 u0 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g);
+    const float4 u1 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g + 4);
+    xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    IO::put_plain8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+  }
+
+  __device__ __forceinline__ void zero_upper_L() const {
+    for (int i = tid; i < C * C; i += blockDim.x) {
+      if ((i / C) / 16 < (i % C) / 16) IO::put_plain(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
+    }
+  }
+
+  // Per beta head: A = (I + G diag(beta))^{-1} from gsolve into asolve (row
+  // stride C + 4 both), then diag(beta) A to the workspace.  beta is loaded
+  // here, into short-lived registers.
+  __device__ __forceinline__ void solve_store(float *gsolve, float *asolve) const {
+    constexpr int NBET = 4;                            // up to 4 * 256 beta values (C * Rb)
+    TIn bets[NBET];
+#pragma unroll
+    for (int j = 0; j < NBET; ++j) {
+      const int e = min(tid + 256 * j, C * Rb - 1);    // e = rb * C + t
+      bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
+    }
+    for (int rb = 0; rb < Rb; ++rb) {
+      const int hb = hk * Rb + rb;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NBET; ++j) {
+        const int e = tid + 256 * j;
+        if (e / C == rb && e < C * Rb) bet[e % C] = (t0 + e % C < T) ? static_cast<float>(bets[j]) : 0.f;
+      }
+      __syncthreads();
+      if (a.solve == 0) {
+        solve_exact<C>(gsolve, bet, asolve, tmp);
+      } else {
+        solve_neumann<C>(gsolve, bet, asolve, tmp, a.order, a.residual);
+      }
+      __syncthreads();
+      // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y
+      void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
+      for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
+        const int blk = u >> 6, f = u & 63;
+        const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
+        const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
+        const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
+        const float bt = bet[row];
+        const float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
+        IO::put_plain8(tA, blk, f, x);
+      }
+    }
+  }
+};
+
+// Per row block I owned by a wave, both routes build
+//  (1) the scan operands of its 16 tokens (scan_operands);
+//  (2) the pivot-decayed row operands K (.) exp(Lambda_t - Lambda_p) and
+//      Q (.) exp(Lambda_t - Lambda_p), kept as split fragments;
+//  (3) Gram and L for the pairs (I, J), J <= I, each one MFMA product with the
+//      decayed keys K_J (.) exp(Lambda_p - Lambda_j) of block J.
+
+// Chunk-pivot route, C = 64: p = 0 for every pair; wave w owns block w and
+// builds its column operand once; the operands of blocks 0 .. 2 are shared
+// through LDS.
+template <typename TIn, class P, int DK>
+__global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
+  constexpr int C = 64;
+  using X = PrepItem<TIn, P, C, DK>;
+  using Split = typename X::Split;
+  using IO = typename X::IO;
+  constexpr int NB = X::NB, KS = X::KS;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw));
+  const int I = x.w, lr = x.lr, lq = x.lq;
+  typename X::LaRegs lar;
+  x.issue_la(lar);
+  Raw8<TIn> kt[KS], qt[KS];
+  x.load_rows(kt, x.kbase, I);
+  x.load_rows(qt, x.qbase, I);
+  x.lambda(lar);
+  if (__builtin_amdgcn_readfirstlane(x.flags[kChunkWide])) {
+    if (x.tid == 0) x.gm_row()[0] = kWideMark;         // left to the block-pivot kernel
+    return;
+  }
+  x.write_gm();
+  unsigned char *colop = reinterpret_cast<unsigned char *>(x.ureg);
+  const int tr = 16 * I + lr;
+  const float mt = (x.t0 + tr < x.T) ? 1.f : 0.f;
+  Split ak[KS], aq[KS];
+  f32x4 dG = {0.f, 0.f, 0.f, 0.f}, dL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int ch0 = 32 * s + 8 * lq;
+    float xk[8], xq[8], lt[8], l0[8], lc[8];
+    kt[s].to_float(xk);
+    qt[s].to_float(xq);
+    x.lam8(tr, ch0, lt);
+    x.lam8(0, ch0, l0);
+    x.lam8(C - 1, ch0, lc);
+    float yk[8], yq[8], yb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float ea = __expf(lt[e] - l0[e]) * mt;     // row side
+      const float eb = __expf(l0[e] - lt[e]) * mt;     // column side
+      yk[e] = xk[e] * ea;
+      yq[e] = xq[e] * ea;
+      yb[e] = xk[e] * eb;
+    }
+    ak[s] = make_frag<Split>(yk);
+    aq[s] = make_frag<Split>(yq);
+    const Split bk = make_frag<Split>(yb);
+    mma(dG, ak[s], bk);
+    mma(dL, aq[s], bk);
+    if (I < NB - 1) lds_put_frag(colop, I * KS + s, bk);
+    x.scan_operands(I, s, xk, xq, lt, lc, mt);
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int row = 16 * I + 4 * lq + q4, col = 16 * I + lr;
+    IO::put_plain(x.tL, frag_pos(row, col, C), row >= col ? dL[q4] : 0.f);
+  }
+  __syncthreads();                                     // column operands complete, Lambda dead
+  float *gsolve = x.smem;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int row = 16 * I + 4 * lq + q4, col = 16 * I + lr;
+    gsolve[row * (C + 4) + col] = row > col ? dG[q4] : 0.f;
+  }
+  for (int J = 0; J < I; ++J) {
+    f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const Split bj = lds_get_frag<Split>(colop, J * KS + s);
+      mma(accG, ak[s], bj);
+      mma(accL, aq[s], bj);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
+      gsolve[row * (C + 4) + col] = accG[q4];
+      IO::put_plain(x.tL, frag_pos(row, col, C), accL[q4]);
+    }
+  }
+  x.zero_upper_L();
+  x.solve_store(gsolve, x.ureg);
+}
+
+// Block-pivot route for one chunk: p = first token of the row block; every
+// exponent on the causal side is <= 0, except on a diagonal block, where it
+// is at most the block's decay range (<= kPivotRange unless the block is
+// flagged and evaluated entry by entry).  Wave w owns blocks w (and 7 - w
+// when C = 128).
+template <typename TIn, class P, int C, int DK>
+__device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int hk, int b, float *smem) {
+  using X = PrepItem<TIn, P, C, DK>;
+  using Split = typename X::Split;
+  using IO = typename X::IO;
+  constexpr int NB = X::NB, KS = X::KS;
+  constexpr int NR = NB / 4;                           // row blocks per wave
+  X x(a, c, hk, b, smem);
+  const int w = x.w, lr = x.lr, lq = x.lq, T = x.T, t0 = x.t0;
+  auto own = [&](int r) { return (r & 1) ? 4 * r + 3 - w : 4 * r + w; };
+  typename X::LaRegs lar;
+  x.issue_la(lar);
+  Raw8<TIn> kt[KS], qt[KS], kj[KS];
+  x.load_rows(kt, x.kbase, own(0));
+  x.load_rows(qt, x.qbase, own(0));
+  x.load_rows(kj, x.kbase, 0);
+  x.lambda(lar);
+  x.write_gm();
+  float *gmat = x.ureg;
   for (int r = 0; r < NR; ++r) {
     const int I = own(r);
     const int tr = 16 * I + lr, piv = 16 * I;
@@ -400,58 +652,40 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       float xk[8], xq[8], lt[8], lp[8], lc[8];
       kt[s].to_float(xk);
       qt[s].to_float(xq);
-      lam8(tr, ch0, lt);
-      lam8(piv, ch0, lp);
-      lam8(C - 1, ch0, lc);
-      float yk[8], yq[8], kbar[8], qbar[8], kh[8];
+      x.lam8(tr, ch0, lt);
+      x.lam8(piv, ch0, lp);
+      x.lam8(C - 1, ch0, lc);
+      float yk[8], yq[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float ea = __expf(lt[e] - lp[e]) * mt;
-        const float d = __expf(lt[e]) * mt;
-        const float h = __expf(lc[e] - lt[e]) * mt;
         yk[e] = xk[e] * ea;
         yq[e] = xq[e] * ea;
-        kbar[e] = xk[e] * d;
-        qbar[e] = xq[e] * d;
-        kh[e] = xk[e] * h;
       }
       ak[s] = make_frag<Split>(yk);
       aq[s] = make_frag<Split>(yq);
-      IO::put_plain8(tKB, I * KS + s, l, kbar);
-      IO::put_plain8(tQB, I * KS + s, l, qbar);
-      // Khat^T: lane (token lr, channels 8 lq ..) writes, lane (channel
-      // 16 (l >> 5) + (l & 15), tokens 8 g ..) reads back a fragment
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xb[(8 * lq + e) * kXbLd + lr] = kh[e];
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int chl = 16 * (l >> 5) + (l & 15), g = (l >> 4) & 1;
-      float xt[8];
-      const float4 u0 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g);
-      const float4 u1 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g + 4);
-      xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      IO::put_plain8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+      x.scan_operands(I, s, xk, xq, lt, lc, mt);
     }
     if (r + 1 < NR) {                                  // next owned block's rows
-      load_rows(kt, kbase, own(r + 1));
-      load_rows(qt, qbase, own(r + 1));
+      x.load_rows(kt, x.kbase, own(r + 1));
+      x.load_rows(qt, x.qbase, own(r + 1));
     }
     for (int J = 0; J <= I; ++J) {
       Raw8<TIn> ckj[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) ckj[s] = kj[s];
-      load_rows(kj, kbase, J < I ? J + 1 : 0);          // next pair's key rows (first block of the next round)
+      x.load_rows(kj, x.kbase, J < I ? J + 1 : 0);     // next pair's key rows (first block of the next round)
       f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
       const int jr = 16 * J + lr;
       const float mj = (t0 + jr < T) ? 1.f : 0.f;
-      if (!(I == J && flags[I])) {
+      if (!(I == J && x.flags[I])) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const int ch0 = 32 * s + 8 * lq;
           float xj[8], lp[8], lj[8];
           ckj[s].to_float(xj);
-          lam8(piv, ch0, lp);
-          lam8(jr, ch0, lj);
+          x.lam8(piv, ch0, lp);
+          x.lam8(jr, ch0, lj);
 #pragma unroll
           for (int e = 0; e < 8; ++e) xj[e] *= __expf(lp[e] - lj[e]) * mj;
           const Split fj = make_frag<Split>(xj);
@@ -466,13 +700,13 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
           const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
           float sg = 0.f, sl = 0.f;
           if (row >= col && t0 + row < T) {
-            const size_t rrow = tok(row) * row_stride, rcol = tok(col) * row_stride;
+            const size_t rrow = x.tok(row) * x.row_stride, rcol = x.tok(col) * x.row_stride;
             for (int ch = 0; ch < DK; ++ch) {
-              const int g = ch >> gs;
-              const float d = __expf(lam[row * G + g] - lam[col * G + g]);
-              const float kc = static_cast<float>(kbase[rcol + ch]);
-              sg += static_cast<float>(kbase[rrow + ch]) * kc * d;
-              sl += static_cast<float>(qbase[rrow + ch]) * kc * d;
+              const int g = ch >> x.gs;
+              const float d = __expf(x.lam[row * x.G + g] - x.lam[col * x.G + g]);
+              const float kc = static_cast<float>(x.kbase[rcol + ch]);
+              sg += static_cast<float>(x.kbase[rrow + ch]) * kc * d;
+              sl += static_cast<float>(x.qbase[rrow + ch]) * kc * d;
             }
           }
           accG[q4] = sg;
@@ -483,47 +717,58 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
         gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[q4] : 0.f;
-        IO::put_plain(tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[q4] : 0.f);
+        IO::put_plain(x.tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[q4] : 0.f);
       }
     }
   }
-  for (int i = tid; i < C * C; i += blockDim.x) {
-    if ((i / C) / 16 < (i % C) / 16) IO::put_plain(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
-  }
+  x.zero_upper_L();
+  x.solve_store(gmat, x.smem);
+}
 
-  // ---- solve per beta head (beta loaded here: short-lived registers)
-  constexpr int NBET = 4;                              // up to 4 * 256 beta values (C * Rb)
-  TIn bets[NBET];
-#pragma unroll
-  for (int j = 0; j < NBET; ++j) {
-    const int e = min(tid + 256 * j, C * Rb - 1);      // e = rb * C + t
-    bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
+// Grid (N_c, H_k, B), one chunk per work group.
+template <typename TIn, class P, int C, int DK>
+__global__ __launch_bounds__(256) void prep_block_kernel(ChunkArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  prep_block_item<TIn, P, C, DK>(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw));
+}
+
+// 1-D grid: work group g checks the items g + j * gridDim.x (j < 256) for the
+// chunk-pivot kernel's mark and runs the marked ones in turn.
+template <typename TIn, class P, int C, int DK>
+__global__ __launch_bounds__(256) void prep_block_listed_kernel(ChunkArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float *smem = reinterpret_cast<float *>(smem_raw);
+  const int n = a.N_c * a.H_k * a.B, tid = threadIdx.x;
+  bool mine = false;
+  {
+    const int u = blockIdx.x + tid * gridDim.x;
+    if (u < n) {
+      const int c = u % a.N_c, hk = (u / a.N_c) % a.H_k, b = u / (a.N_c * a.H_k);
+      mine = reinterpret_cast<const float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c))[0] == kWideMark;
+    }
   }
-  for (int rb = 0; rb < Rb; ++rb) {
-    const int hb = hk * Rb + rb;
-    __syncthreads();
+  // the 256 marks as four 64-bit wave masks, shared through LDS
+  unsigned long long *masks = reinterpret_cast<unsigned long long *>(smem);
+  const unsigned long long m = __ballot(mine);
+  if (lane_id() == 0) masks[wave_id()] = m;
+  __syncthreads();
+  unsigned long long mk[4];
 #pragma unroll
-    for (int j = 0; j < NBET; ++j) {
-      const int e = tid + 256 * j;
-      if (e / C == rb && e < C * Rb) bet[e % C] = (t0 + e % C < T) ? static_cast<float>(bets[j]) : 0.f;
-    }
-    __syncthreads();
-    if (a.solve == 0) {
-      solve_exact<C>(gmat, bet, amat, tmp);
-    } else {
-      solve_neumann<C>(gmat, bet, amat, tmp, a.order, a.residual);
-    }
-    __syncthreads();
-    // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y
-    void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
-    for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
-      const int blk = u >> 6, f = u & 63;
-      const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
-      const float4 a0 = *reinterpret_cast<const float4 *>(amat + row * (C + 4) + col);
-      const float4 a1 = *reinterpret_cast<const float4 *>(amat + row * (C + 4) + col + 4);
-      const float bt = bet[row];
-      const float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
-      IO::put_plain8(tA, blk, f, x);
+  for (int q = 0; q < 4; ++q) {
+    const unsigned long long v = masks[q];
+    mk[q] = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32)) << 32) |
+            (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
+  }
+  __syncthreads();
+  for (int q = 0; q < 4; ++q) {
+    unsigned long long v = mk[q];
+    while (v) {
+      const int j = 64 * q + __builtin_ctzll(v);
+      v &= v - 1;
+      const int u = blockIdx.x + j * gridDim.x;
+      const int c = u % a.N_c, hk = (u / a.N_c) % a.H_k, b = u / (a.N_c * a.H_k);
+      prep_block_item<TIn, P, C, DK>(a, c, hk, b, smem);
+      __syncthreads();
     }
   }
 }
@@ -531,19 +776,38 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 bool prep_supported(int C, int d_k, int G) {
   if (!(C == 64 || C == 128)) return false;
   if (!(d_k == 64 || d_k == 128 || d_k == 256)) return false;
-  return prep_lds_bytes(C, G) <= 160 * 1024;
+  return prep_lds_bytes(C, d_k, G) <= 160 * 1024;
+}
+
+template <class K>
+static hipError_t set_lds(K kern, size_t lds) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
 }
 
 template <typename TIn, class P, int C, int DK>
 static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
-  const size_t lds = prep_lds_bytes(C, a.G);
-  auto kern = prep_kernel<TIn, P, C, DK>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  dim3 grid(a.N_c, a.H_k, a.B);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, a);
+  const size_t lds = prep_lds_bytes(C, DK, a.G);
+  const dim3 grid(a.N_c, a.H_k, a.B);
+  hipError_t e;
+  if constexpr (C != 64) {
+    auto block = prep_block_kernel<TIn, P, C, DK>;
+    if ((e = set_lds(block, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(block, grid, dim3(256), lds, stream, a);
+    return hipGetLastError();
+  } else {
+  auto chunk = prep_chunk_kernel<TIn, P, DK>;
+  auto listed = prep_block_listed_kernel<TIn, P, C, DK>;
+  if ((e = set_lds(chunk, lds)) != hipSuccess) return e;
+  if ((e = set_lds(listed, lds)) != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk, grid, dim3(256), lds, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // wide-range chunks, if any: at most 256 items per work group
+  const long n = (long)a.N_c * a.H_k * a.B;
+  const long groups = std::max(std::min(n, 1024L), (n + 255) / 256);
+  hipLaunchKernelGGL(listed, dim3((unsigned)groups), dim3(256), lds, stream, a);
   return hipGetLastError();
+  }
 }
 
 template <typename TIn, class P>

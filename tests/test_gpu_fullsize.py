@@ -27,6 +27,13 @@ def _gpu():
     need_gpu()
 
 
+# C = 64 with about half of the chunks too wide in decay range for the chunk
+# pivot: 4096 (chunk, key head) items, several per work group of the
+# block-pivot fallback kernel
+MIXED_LONG = Workload("kda_c64_mixed_long", 1, 16384, 16, 16, 128, 128, 64, 128, "bf16",
+                      alpha_mu=0.75, alpha_sigma=2.0, seed=31)
+
+
 def sample_units(w, n=3):
     total = w.B * w.H_v
     return sorted({0, total // 2, total - 1} if n == 3 else set(range(min(n, total))))
@@ -53,6 +60,23 @@ def test_workload_exact(cfg):
     eh = rel_err(np.stack([hT[u // w.H_v, u % w.H_v] for u in units]),
                  np.stack([h_ref[u // w.H_v, u % w.H_v] for u in units]))
     print(f"  {w.name}: units {units} err o={eo:.3e} hT={eh:.3e} (bar {TOL[w.dtype]:g})", flush=True)
+    assert np.all(np.isfinite(o))
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
+
+
+def test_mixed_range_chunks_full_size():
+    w = MIXED_LONG
+    print(f"\n[case] full-size mixed-range {w.name}", flush=True)
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    o, hT = run_chunk(dev, w)
+    o, hT = o.cpu().numpy(), hT.cpu().numpy()
+    units = sample_units(w)
+    o_ref, h_ref = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], units=units)
+    eo = unit_err(o, o_ref, w, units)
+    eh = rel_err(np.stack([hT[u // w.H_v, u % w.H_v] for u in units]),
+                 np.stack([h_ref[u // w.H_v, u % w.H_v] for u in units]))
+    print(f"  {w.name}: units {units} err o={eo:.3e} hT={eh:.3e}", flush=True)
     assert np.all(np.isfinite(o))
     assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
 

@@ -31,7 +31,16 @@ SMALL = {
                                 alpha_mu=1.0, alpha_sigma=2.0, seed=6),
     "dk64_bkh_gva": Workload("dk64_bkh_gva", 2, 190, 2, 4, 64, 48, 64, 8, "bf16", beta_per_key_head=True, seed=7),
     "dk256_kda_bf16": Workload("dk256_kda_bf16", 1, 200, 1, 1, 256, 64, 64, 256, "bf16", seed=8),
+    # C = 64 with some chunks whose decay range exceeds the chunk-pivot limit
+    # and some within it (both kinds present: test_input_cases.py)
+    "kda_c64_mixed": Workload("kda_c64_mixed", 1, 700, 2, 2, 128, 64, 64, 128, "bf16",
+                              alpha_mu=0.75, alpha_sigma=2.0, seed=9),
+    "gdn_f32_c64_mixed": Workload("gdn_f32_c64_mixed", 2, 450, 2, 2, 64, 64, 64, 1, "f32",
+                                  alpha_mu=0.0, alpha_sigma=2.0, seed=10),
 }
+
+# the cases above with chunks on both sides of the chunk-pivot range limit
+MIXED = ("kda_c64_mixed", "gdn_f32_c64_mixed")
 
 
 def oracle(x, w, h0=None, units=None):
@@ -116,7 +125,7 @@ def expected_operands(x, w):
 
 
 @pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong",
-                                  "dk64_bkh_gva", "dk256_kda_bf16"])
+                                  "dk64_bkh_gva", "dk256_kda_bf16", "kda_c64_mixed", "gdn_f32_c64_mixed"])
 @pytest.mark.parametrize("solve", ["exact", "neumann"])
 def test_prepared_workspace(name, solve):
     """Every prepared chunk quantity against the fp64 chunk pieces: diag(beta)
