@@ -93,6 +93,21 @@ template <> struct Raw8<float> {
   }
 };
 
+// Value of the lane N places lower in the same 16-lane DPP row, 0 for the
+// first N lanes of the row.
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + N, 0xf, 0xf, true));
+}
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16 r .. 16 r + 15).
+__device__ __forceinline__ float row_prefix16(float v) {
+  v += dpp_row_shr<1>(v);
+  v += dpp_row_shr<2>(v);
+  v += dpp_row_shr<4>(v);
+  v += dpp_row_shr<8>(v);
+  return v;
+}
+
 // In-place prefix sum over rows of one column of a row-major LDS matrix
 // (the cumulative log-decay Lambda_t = sum_{s<=t} log alpha_s of Systolic
 // Linear Attention, Table 2), 16 rows at a time so the reads of a block are

@@ -81,6 +81,13 @@ size_t prep_lds_bytes(int C, int DK, int G) {
   return sizeof(float) * (size_t)(prep_region0_floats(C, G) + prep_union_floats(C, DK) + C) +
          sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd;
 }
+// The chunk-pivot kernel keeps Lambda in registers: region 0 holds the
+// block totals of Lambda during the build and G after it.
+__host__ __device__ inline int prep_chunk_region0_floats(int C) { return C * prep_ld(C); }
+size_t prep_chunk_lds_bytes(int C, int DK) {
+  return sizeof(float) * (size_t)(prep_chunk_region0_floats(C) + prep_union_floats(C, DK) + C) +
+         sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd;
+}
 
 // One lane's 32-byte fragment in LDS as two planes of 16 bytes per lane, so
 // a wave's read of a plane is 1 KiB of consecutive bytes.
@@ -325,11 +332,12 @@ struct PrepItem {
   const size_t row_stride, la_row;                     // token strides of q / k and of log alpha
   void *const tKB, *const tQB, *const tKH, *const tL;
 
-  __device__ __forceinline__ PrepItem(const ChunkArgs &a_, int c_, int hk_, int b_, float *smem_)
+  // region0: floats before the union region
+  __device__ __forceinline__ PrepItem(const ChunkArgs &a_, int c_, int hk_, int b_, float *smem_, int region0)
       : a(a_), c(c_), hk(hk_), b(b_), G(a_.G), gs(a_.gshift), T(a_.T), t0(c_ * C), tid(threadIdx.x),
         w(wave_id()), l(lane_id()), lr(lane_id() & 15), lq(lane_id() >> 4),
         lgG(__builtin_ctz(DK) - a_.gshift), Rb(a_.H_beta / a_.H_k), smem(smem_), lam(smem_),
-        ureg(smem_ + prep_region0_floats(C, a_.G)), tmp(ureg + C * prep_ld(C)),
+        ureg(smem_ + region0), tmp(ureg + C * prep_ld(C)),
         bet(ureg + prep_union_floats(C, DK)), flags(reinterpret_cast<int *>(bet + C)),
         xb(reinterpret_cast<float *>(flags + 16) + wave_id() * 32 * kXbLd),
         la(reinterpret_cast<const TIn *>(a_.log_alpha)), bp(reinterpret_cast<const TIn *>(a_.beta)),
@@ -477,9 +485,13 @@ struct PrepItem {
     IO::put_plain8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
   }
 
+  // L above the diagonal blocks, one fragment (row, 8 columns) per store
   __device__ __forceinline__ void zero_upper_L() const {
-    for (int i = tid; i < C * C; i += blockDim.x) {
-      if ((i / C) / 16 < (i % C) / 16) IO::put_plain(tL, frag_pos(i / C, i % C, C), 0.f);   // above the diagonal
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int u = tid; u < (C / 16) * (C / 32) * 64; u += blockDim.x) {
+      const int blk = u >> 6, f = u & 63;
+      const int rb = blk / (C / 32), kb = blk % (C / 32);
+      if (2 * kb + (f >> 5) > rb) IO::put_plain8(tL, blk, f, z);   // column block 2 kb + (f >> 4) / 2
     }
   }
 
@@ -531,10 +543,21 @@ struct PrepItem {
 //  (3) Gram and L for the pairs (I, J), J <= I, each one MFMA product with the
 //      decayed keys K_J (.) exp(Lambda_p - Lambda_j) of block J.
 
+// f[i] for a lane-varying i in [0, 8) by selects (no indexed register access)
+__device__ __forceinline__ float pick(const float (&f)[8], int i) {
+  const float a = (i & 1) ? f[1] : f[0], b = (i & 1) ? f[3] : f[2];
+  const float c = (i & 1) ? f[5] : f[4], d = (i & 1) ? f[7] : f[6];
+  const float lo = (i & 2) ? b : a, hi = (i & 2) ? d : c;
+  return (i & 4) ? hi : lo;
+}
+
 // Chunk-pivot route, C = 64: p = 0 for every pair; wave w owns block w and
 // builds its column operand once; the operands of blocks 0 .. 2 are shared
-// through LDS.
-template <typename TIn, class P, int DK>
+// through LDS.  Lambda never goes through LDS whole: each lane holds log
+// alpha of its token for its channels, the in-block prefix runs over the
+// 16 lanes of a DPP row, and only the block totals and the first token's
+// values are exchanged.  kVecLa: G >= 8 (log alpha read as 8-element vectors).
+template <typename TIn, class P, int DK, bool kVecLa>
 __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   using X = PrepItem<TIn, P, C, DK>;
@@ -542,38 +565,124 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   using IO = typename X::IO;
   constexpr int NB = X::NB, KS = X::KS;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw));
-  const int I = x.w, lr = x.lr, lq = x.lq;
-  typename X::LaRegs lar;
-  x.issue_la(lar);
+  X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw), prep_chunk_region0_floats(C));
+  const int I = x.w, lr = x.lr, lq = x.lq, gs = x.gs, G = x.G;
+  const int tr = 16 * I + lr;
+  const float mt = (x.t0 + tr < x.T) ? 1.f : 0.f;
+
+  // ---- loads: log alpha of the lane's token, then its key and query rows
+  const TIn *larow = x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G;
+  Raw8<TIn> lav[kVecLa ? KS : 1];
+  TIn las[4];
+  if constexpr (kVecLa) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) lav[s].load(larow + min((32 * s + 8 * lq) >> gs, G - 8));
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) las[g] = larow[min(g, G - 1)];
+  }
   Raw8<TIn> kt[KS], qt[KS];
   x.load_rows(kt, x.kbase, I);
   x.load_rows(qt, x.qbase, I);
-  x.lambda(lar);
+
+  // ---- Lambda of the lane's token: in-block prefix, then block offsets
+  float lt[KS][8];
+  bool rising = false;                                 // a positive log alpha: Lambda not monotone
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int ch0 = 32 * s + 8 * lq;
+    if constexpr (kVecLa) {
+      float f[8];
+      lav[s].to_float(f);
+      const int g0 = min(ch0 >> gs, G - 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lt[s][e] = (gs == 0 ? f[e] : pick(f, ((ch0 + e) >> gs) - g0)) * mt;
+    } else {
+      // G < 8 < d_k / G: the lane's eight channels share one group
+      const int g = ch0 >> gs;
+      const float v = static_cast<float>(g == 0 ? las[0] : g == 1 ? las[1] : g == 2 ? las[2] : las[3]) * mt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lt[s][e] = v;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rising |= lt[s][e] > 0.f;
+  }
+  // Block totals of log alpha -> LDS; then one thread per channel turns them
+  // into exclusive block offsets and Lambda_{C-1}, and checks the range.
+  float *off = x.smem;                                 // [NB][DK] block totals, then block offsets
+  float *row0 = off + NB * DK;                         // [DK] Lambda_0 = log alpha_0
+  float *rowc = row0 + DK;                             // [DK] Lambda_{C-1}
+  if (I == 0 && lr == 0) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float *d = row0 + 32 * s + 8 * lq;
+      *reinterpret_cast<float4 *>(d) = make_float4(lt[s][0], lt[s][1], lt[s][2], lt[s][3]);
+      *reinterpret_cast<float4 *>(d + 4) = make_float4(lt[s][4], lt[s][5], lt[s][6], lt[s][7]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lt[s][e] = row_prefix16(lt[s][e]);
+  }
+  if (lr == 15) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float *d = off + I * DK + 32 * s + 8 * lq;
+      *reinterpret_cast<float4 *>(d) = make_float4(lt[s][0], lt[s][1], lt[s][2], lt[s][3]);
+      *reinterpret_cast<float4 *>(d + 4) = make_float4(lt[s][4], lt[s][5], lt[s][6], lt[s][7]);
+    }
+  }
+  // flags[kChunkWide]: a positive log alpha (Lambda not monotone) or a span
+  // beyond kPivotRange; the chunk pivot needs neither
+  if (x.tid == 0) x.flags[kChunkWide] = 0;
+  const bool any_rising = __ballot(rising) != 0;
+  __syncthreads();
+  if (lr == 0 && lq == 0 && any_rising) x.flags[kChunkWide] = 1;
+  if (x.tid < DK) {
+    const int ch = x.tid;
+    float run = 0.f;
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      const float t = off[J * DK + ch];
+      off[J * DK + ch] = run;
+      run += t;
+    }
+    rowc[ch] = run;
+    if (!(row0[ch] - run <= kPivotRange)) x.flags[kChunkWide] = 1;   // several threads may store the same 1
+  }
+  __syncthreads();
   if (__builtin_amdgcn_readfirstlane(x.flags[kChunkWide])) {
     if (x.tid == 0) x.gm_row()[0] = kWideMark;         // left to the block-pivot kernel
     return;
   }
-  x.write_gm();
+  if (x.tid < DK) x.gm_row()[x.tid] = __expf(rowc[x.tid]);
+  auto load8 = [&](const float *p, float (&y)[8]) __attribute__((always_inline)) {
+    const float4 u = *reinterpret_cast<const float4 *>(p);
+    const float4 v = *reinterpret_cast<const float4 *>(p + 4);
+    y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w; y[4] = v.x; y[5] = v.y; y[6] = v.z; y[7] = v.w;
+  };
+
+  // ---- row and column operands, scan operands, the diagonal pair
   unsigned char *colop = reinterpret_cast<unsigned char *>(x.ureg);
-  const int tr = 16 * I + lr;
-  const float mt = (x.t0 + tr < x.T) ? 1.f : 0.f;
   Split ak[KS], aq[KS];
   f32x4 dG = {0.f, 0.f, 0.f, 0.f}, dL = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int ch0 = 32 * s + 8 * lq;
-    float xk[8], xq[8], lt[8], l0[8], lc[8];
+    float xk[8], xq[8], l0[8], lc[8], o[8];
     kt[s].to_float(xk);
     qt[s].to_float(xq);
-    x.lam8(tr, ch0, lt);
-    x.lam8(0, ch0, l0);
-    x.lam8(C - 1, ch0, lc);
+    load8(row0 + ch0, l0);
+    load8(rowc + ch0, lc);
+    load8(off + I * DK + ch0, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lt[s][e] += o[e];
     float yk[8], yq[8], yb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float ea = __expf(lt[e] - l0[e]) * mt;     // row side
-      const float eb = __expf(l0[e] - lt[e]) * mt;     // column side
+      const float ea = __expf(lt[s][e] - l0[e]) * mt;  // row side
+      const float eb = __expf(l0[e] - lt[s][e]) * mt;  // column side
       yk[e] = xk[e] * ea;
       yq[e] = xq[e] * ea;
       yb[e] = xk[e] * eb;
@@ -584,14 +693,14 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     mma(dG, ak[s], bk);
     mma(dL, aq[s], bk);
     if (I < NB - 1) lds_put_frag(colop, I * KS + s, bk);
-    x.scan_operands(I, s, xk, xq, lt, lc, mt);
+    x.scan_operands(I, s, xk, xq, lt[s], lc, mt);
   }
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int row = 16 * I + 4 * lq + q4, col = 16 * I + lr;
     IO::put_plain(x.tL, frag_pos(row, col, C), row >= col ? dL[q4] : 0.f);
   }
-  __syncthreads();                                     // column operands complete, Lambda dead
+  __syncthreads();                                     // column operands complete, Lambda rows dead
   float *gsolve = x.smem;
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -629,7 +738,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   using IO = typename X::IO;
   constexpr int NB = X::NB, KS = X::KS;
   constexpr int NR = NB / 4;                           // row blocks per wave
-  X x(a, c, hk, b, smem);
+  X x(a, c, hk, b, smem, prep_region0_floats(C, a.G));
   const int w = x.w, lr = x.lr, lq = x.lq, T = x.T, t0 = x.t0;
   auto own = [&](int r) { return (r & 1) ? 4 * r + 3 - w : 4 * r + w; };
   typename X::LaRegs lar;
@@ -796,11 +905,12 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(block, grid, dim3(256), lds, stream, a);
     return hipGetLastError();
   } else {
-  auto chunk = prep_chunk_kernel<TIn, P, DK>;
+  auto chunk = a.G >= 8 ? prep_chunk_kernel<TIn, P, DK, true> : prep_chunk_kernel<TIn, P, DK, false>;
   auto listed = prep_block_listed_kernel<TIn, P, C, DK>;
-  if ((e = set_lds(chunk, lds)) != hipSuccess) return e;
+  const size_t chunk_lds = prep_chunk_lds_bytes(C, DK);
+  if ((e = set_lds(chunk, chunk_lds)) != hipSuccess) return e;
   if ((e = set_lds(listed, lds)) != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk, grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(chunk, grid, dim3(256), chunk_lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // wide-range chunks, if any: at most 256 items per work group
   const long n = (long)a.N_c * a.H_k * a.B;
