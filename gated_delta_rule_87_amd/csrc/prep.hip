@@ -30,15 +30,16 @@
 // applied before the exponential.  No exponential of a positive Lambda
 // difference on the causal side is ever formed.
 //
-// Chunk pivot.  When the range of Lambda over the whole chunk is within
-// kPivotRange in every channel (true for any chunk of mild decay), the first
-// token of the chunk serves as the pivot of every pair: the row operand
-// K_t (.) exp(Lambda_t - Lambda_0) and the column operand
-// K_j (.) exp(Lambda_0 - Lambda_j) then no longer depend on the pair, each
-// block builds both once, and a pair is MFMA work only.  The factors stay in
-// [exp(-kPivotRange), exp(kPivotRange)], so neither overflows nor underflows
-// in fp32 and every product keeps its relative precision; entries with j > t
-// can be large but are masked.
+// Chunk pivot.  When no log alpha of the chunk is positive and the chunk's
+// total decay -Lambda_{C-1} is within kPivotRange in every channel (true for
+// any chunk of mild decay), the first token of the chunk serves as the pivot
+// of every pair: the row operand K_t (.) exp(Lambda_t - Lambda_0) and the
+// column operand K_j (.) exp(Lambda_0 - Lambda_j) then no longer depend on
+// the pair, each block builds both once, and a pair is MFMA work only.  Every
+// Lambda_t lies in [-kPivotRange, 0], so exp(+-Lambda_t) and all the factors
+// formed from them stay in [exp(-kPivotRange), exp(kPivotRange)]: none
+// overflows or underflows in fp32, every product keeps its relative
+// precision, and entries with j > t can be large but are masked.
 #include <algorithm>
 #include <type_traits>
 
@@ -454,21 +455,11 @@ struct PrepItem {
 
   // The scan operands of channel step s of block I (Systolic Linear
   // Attention, Table 2; lane: token 16 I + lr, channels 32 s + 8 lq ..):
-  // Kbar = K (.) exp(Lambda_t), Qbar = Q (.) exp(Lambda_t), and
-  // Khat = K (.) exp(Lambda_C - Lambda_t), the last transposed through the
-  // wave's LDS buffer into channel-row fragments.  lt, lc: Lambda of the
-  // token and of the last token.
-  __device__ __forceinline__ void scan_operands(int I, int s, const float (&xk)[8], const float (&xq)[8],
-                                                const float (&lt)[8], const float (&lc)[8], float mt) const {
-    float kbar[8], qbar[8], kh[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float d = __expf(lt[e]) * mt;
-      const float h = __expf(lc[e] - lt[e]) * mt;
-      kbar[e] = xk[e] * d;
-      qbar[e] = xq[e] * d;
-      kh[e] = xk[e] * h;
-    }
+  // kbar = K (.) exp(Lambda_t), qbar = Q (.) exp(Lambda_t) and
+  // kh = K (.) exp(Lambda_C - Lambda_t), the last transposed through the
+  // wave's LDS buffer into channel-row fragments.
+  __device__ __forceinline__ void scan_operands(int I, int s, const float (&kbar)[8], const float (&qbar)[8],
+                                                const float (&kh)[8]) const {
     IO::put_plain8(tKB, I * KS + s, l, kbar);
     IO::put_plain8(tQB, I * KS + s, l, qbar);
     // Khat^T: lane (token lr, channels 8 lq ..) writes, lane (channel
@@ -483,6 +474,27 @@ struct PrepItem {
     xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     IO::put_plain8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+  }
+
+  // The 16 x 16 block (I, J) of L from an MFMA accumulator (lane: rows
+  // 4 lq .. 4 lq + 3, column lr), through the wave's LDS buffer, as 32
+  // fragments of 8 columns; on the diagonal block the entries above the
+  // diagonal are zero.
+  __device__ __forceinline__ void store_L_block(int I, int J, const f32x4 &acc) const {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int r = 4 * lq + q4;
+      xb[r * kXbLd + lr] = (I > J || r >= lr) ? acc[q4] : 0.f;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int r = l & 15, h = (l >> 4) & 1;
+    const float4 u0 = *reinterpret_cast<const float4 *>(xb + r * kXbLd + 8 * h);
+    const float4 u1 = *reinterpret_cast<const float4 *>(xb + r * kXbLd + 8 * h + 4);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (l < 32) {
+      const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      IO::put_plain8(tL, I * (C / 32) + J / 2, 16 * (2 * (J & 1) + h) + r, v);
+    }
   }
 
   // L above the diagonal blocks, one fragment (row, 8 columns) per store
@@ -562,7 +574,6 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   using X = PrepItem<TIn, P, C, DK>;
   using Split = typename X::Split;
-  using IO = typename X::IO;
   constexpr int NB = X::NB, KS = X::KS;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw), prep_chunk_region0_floats(C));
@@ -585,7 +596,10 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   x.load_rows(kt, x.kbase, I);
   x.load_rows(qt, x.qbase, I);
 
-  // ---- Lambda of the lane's token: in-block prefix, then block offsets
+  // ---- Lambda of the lane's token in log2 units (log2(e) Lambda): in-block
+  // prefix, then block offsets
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float scale = mt * kLog2e;                     // tokens past T: zero log decay
   float lt[KS][8];
   bool rising = false;                                 // a positive log alpha: Lambda not monotone
 #pragma unroll
@@ -596,11 +610,11 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
       lav[s].to_float(f);
       const int g0 = min(ch0 >> gs, G - 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lt[s][e] = (gs == 0 ? f[e] : pick(f, ((ch0 + e) >> gs) - g0)) * mt;
+      for (int e = 0; e < 8; ++e) lt[s][e] = (gs == 0 ? f[e] : pick(f, ((ch0 + e) >> gs) - g0)) * scale;
     } else {
       // G < 8 < d_k / G: the lane's eight channels share one group
       const int g = ch0 >> gs;
-      const float v = static_cast<float>(g == 0 ? las[0] : g == 1 ? las[1] : g == 2 ? las[2] : las[3]) * mt;
+      const float v = static_cast<float>(g == 0 ? las[0] : g == 1 ? las[1] : g == 2 ? las[2] : las[3]) * scale;
 #pragma unroll
       for (int e = 0; e < 8; ++e) lt[s][e] = v;
     }
@@ -608,10 +622,12 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     for (int e = 0; e < 8; ++e) rising |= lt[s][e] > 0.f;
   }
   // Block totals of log alpha -> LDS; then one thread per channel turns them
-  // into exclusive block offsets and Lambda_{C-1}, and checks the range.
+  // into exclusive block offsets and the per-channel factors
+  // e0 = exp(Lambda_0), e0i = exp(-Lambda_0), gc = exp(Lambda_{C-1}).
   float *off = x.smem;                                 // [NB][DK] block totals, then block offsets
-  float *row0 = off + NB * DK;                         // [DK] Lambda_0 = log alpha_0
-  float *rowc = row0 + DK;                             // [DK] Lambda_{C-1}
+  float *row0 = off + NB * DK;                         // [DK] log2(e) Lambda_0, then e0
+  float *e0i = row0 + DK;                              // [DK]
+  float *gc = e0i + DK;                                // [DK]
   if (I == 0 && lr == 0) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -633,8 +649,10 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
       *reinterpret_cast<float4 *>(d + 4) = make_float4(lt[s][4], lt[s][5], lt[s][6], lt[s][7]);
     }
   }
-  // flags[kChunkWide]: a positive log alpha (Lambda not monotone) or a span
-  // beyond kPivotRange; the chunk pivot needs neither
+  // flags[kChunkWide]: a positive log alpha (Lambda not monotone) or a total
+  // decay -Lambda_{C-1} beyond kPivotRange.  Without either, every Lambda_t
+  // lies in [-kPivotRange, 0] and all the factors below lie in
+  // [exp(-kPivotRange), exp(kPivotRange)].
   if (x.tid == 0) x.flags[kChunkWide] = 0;
   const bool any_rising = __ballot(rising) != 0;
   __syncthreads();
@@ -648,15 +666,18 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
       off[J * DK + ch] = run;
       run += t;
     }
-    rowc[ch] = run;
-    if (!(row0[ch] - run <= kPivotRange)) x.flags[kChunkWide] = 1;   // several threads may store the same 1
+    if (!(-run <= kPivotRange * kLog2e)) x.flags[kChunkWide] = 1;   // several threads may store the same 1
+    const float l0 = row0[ch];
+    row0[ch] = __builtin_amdgcn_exp2f(l0);
+    e0i[ch] = __builtin_amdgcn_exp2f(-l0);
+    gc[ch] = __builtin_amdgcn_exp2f(run);
   }
   __syncthreads();
   if (__builtin_amdgcn_readfirstlane(x.flags[kChunkWide])) {
     if (x.tid == 0) x.gm_row()[0] = kWideMark;         // left to the block-pivot kernel
     return;
   }
-  if (x.tid < DK) x.gm_row()[x.tid] = __expf(rowc[x.tid]);
+  if (x.tid < DK) x.gm_row()[x.tid] = gc[x.tid];
   auto load8 = [&](const float *p, float (&y)[8]) __attribute__((always_inline)) {
     const float4 u = *reinterpret_cast<const float4 *>(p);
     const float4 v = *reinterpret_cast<const float4 *>(p + 4);
@@ -670,22 +691,26 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int ch0 = 32 * s + 8 * lq;
-    float xk[8], xq[8], l0[8], lc[8], o[8];
+    float xk[8], xq[8], f0[8], f0i[8], fc[8], o[8];
     kt[s].to_float(xk);
     qt[s].to_float(xq);
-    load8(row0 + ch0, l0);
-    load8(rowc + ch0, lc);
+    load8(row0 + ch0, f0);
+    load8(e0i + ch0, f0i);
+    load8(gc + ch0, fc);
     load8(off + I * DK + ch0, o);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lt[s][e] += o[e];
-    float yk[8], yq[8], yb[8];
+    float yk[8], yq[8], yb[8], kbar[8], qbar[8], kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float ea = __expf(lt[s][e] - l0[e]) * mt;  // row side
-      const float eb = __expf(l0[e] - lt[s][e]) * mt;  // column side
-      yk[e] = xk[e] * ea;
-      yq[e] = xq[e] * ea;
-      yb[e] = xk[e] * eb;
+      const float l2 = lt[s][e] + o[e];                // log2(e) Lambda_t
+      const float d = __builtin_amdgcn_exp2f(l2);      // exp(Lambda_t)
+      const float u = __builtin_amdgcn_exp2f(-l2);     // exp(-Lambda_t)
+      const float k = xk[e] * mt, q = xq[e] * mt;
+      yk[e] = k * (d * f0i[e]);                        // row side, exp(Lambda_t - Lambda_0)
+      yq[e] = q * (d * f0i[e]);
+      yb[e] = k * (u * f0[e]);                         // column side, exp(Lambda_0 - Lambda_t)
+      kbar[e] = k * d;
+      qbar[e] = q * d;
+      kh[e] = k * (u * fc[e]);                         // exp(Lambda_C - Lambda_t)
     }
     ak[s] = make_frag<Split>(yk);
     aq[s] = make_frag<Split>(yq);
@@ -693,13 +718,9 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     mma(dG, ak[s], bk);
     mma(dL, aq[s], bk);
     if (I < NB - 1) lds_put_frag(colop, I * KS + s, bk);
-    x.scan_operands(I, s, xk, xq, lt[s], lc, mt);
+    x.scan_operands(I, s, kbar, qbar, kh);
   }
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int row = 16 * I + 4 * lq + q4, col = 16 * I + lr;
-    IO::put_plain(x.tL, frag_pos(row, col, C), row >= col ? dL[q4] : 0.f);
-  }
+  x.store_L_block(I, I, dL);
   __syncthreads();                                     // column operands complete, Lambda rows dead
   float *gsolve = x.smem;
 #pragma unroll
@@ -716,11 +737,8 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
       mma(accL, aq[s], bj);
     }
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
-      gsolve[row * (C + 4) + col] = accG[q4];
-      IO::put_plain(x.tL, frag_pos(row, col, C), accL[q4]);
-    }
+    for (int q4 = 0; q4 < 4; ++q4) gsolve[(16 * I + 4 * lq + q4) * (C + 4) + 16 * J + lr] = accG[q4];
+    x.store_L_block(I, J, accL);
   }
   x.zero_upper_L();
   x.solve_store(gsolve, x.ureg);
@@ -735,7 +753,6 @@ template <typename TIn, class P, int C, int DK>
 __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int hk, int b, float *smem) {
   using X = PrepItem<TIn, P, C, DK>;
   using Split = typename X::Split;
-  using IO = typename X::IO;
   constexpr int NB = X::NB, KS = X::KS;
   constexpr int NR = NB / 4;                           // row blocks per wave
   X x(a, c, hk, b, smem, prep_region0_floats(C, a.G));
@@ -764,16 +781,21 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
       x.lam8(tr, ch0, lt);
       x.lam8(piv, ch0, lp);
       x.lam8(C - 1, ch0, lc);
-      float yk[8], yq[8];
+      float yk[8], yq[8], kbar[8], qbar[8], kh[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float ea = __expf(lt[e] - lp[e]) * mt;
+        const float d = __expf(lt[e]) * mt;
+        const float h = __expf(lc[e] - lt[e]) * mt;
         yk[e] = xk[e] * ea;
         yq[e] = xq[e] * ea;
+        kbar[e] = xk[e] * d;
+        qbar[e] = xq[e] * d;
+        kh[e] = xk[e] * h;
       }
       ak[s] = make_frag<Split>(yk);
       aq[s] = make_frag<Split>(yq);
-      x.scan_operands(I, s, xk, xq, lt, lc, mt);
+      x.scan_operands(I, s, kbar, qbar, kh);
     }
     if (r + 1 < NR) {                                  // next owned block's rows
       x.load_rows(kt, x.kbase, own(r + 1));
@@ -826,8 +848,8 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
       for (int q4 = 0; q4 < 4; ++q4) {
         const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
         gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[q4] : 0.f;
-        IO::put_plain(x.tL, frag_pos(row, col, C), (I > J || row >= col) ? accL[q4] : 0.f);
       }
+      x.store_L_block(I, J, accL);
     }
   }
   x.zero_upper_L();

@@ -31,7 +31,7 @@ def _gpu():
 # pivot: 4096 (chunk, key head) items, several per work group of the
 # block-pivot fallback kernel
 MIXED_LONG = Workload("kda_c64_mixed_long", 1, 16384, 16, 16, 128, 128, 64, 128, "bf16",
-                      alpha_mu=0.75, alpha_sigma=2.0, seed=31)
+                      alpha_mu=0.85, alpha_sigma=2.0, seed=31)
 
 
 def sample_units(w, n=3):

@@ -1,10 +1,10 @@
 """Properties of the GPU test inputs themselves (CPU only).
 
-The prep stage takes one of two routes per chunk (chunk-wide pivot when the
-range of the cumulative log-decay over the chunk is at most 64 in every
-decay group, 16-token block pivots otherwise).  The mixed-range cases must
-hold chunks of both kinds in one launch, or they would not test the hand-off
-between the two kernels.
+The prep stage takes one of two routes per chunk: a chunk-wide pivot when no
+log alpha of the chunk is positive and the chunk's total decay
+-Lambda_{C-1} = -sum(log alpha) is at most 64 in every decay group, 16-token
+block pivots otherwise.  The mixed-range cases must hold chunks of both kinds
+in one launch, or they would not test the hand-off between the two kernels.
 """
 import numpy as np
 import pytest
@@ -17,17 +17,17 @@ PIVOT_RANGE = 64.0
 
 
 def wide_fraction(w):
-    """Fraction of (batch, key head, chunk) items whose in-chunk range of
-    Lambda = cumsum(log alpha) exceeds the limit in some decay group (rows
-    past T are zero log-decay)."""
+    """Fraction of (batch, key head, chunk) items that need block pivots: a
+    positive log alpha, or a total decay beyond the limit in some decay group
+    (rows past T are zero log-decay)."""
     la = decode(make_inputs(w)["log_alpha"]).astype(np.float64)   # [B, T, H_k, G]
     B, T, H, G = la.shape
     C = w.chunk
     nc = -(-T // C)
     pad = np.zeros((B, nc * C, H, G))
     pad[:, :T] = la
-    lam = np.cumsum(pad.reshape(B, nc, C, H, G), axis=2)
-    wide = (lam.max(axis=2) - lam.min(axis=2) > PIVOT_RANGE).any(axis=-1)
+    chunks = pad.reshape(B, nc, C, H, G)
+    wide = ((-chunks.sum(axis=2) > PIVOT_RANGE) | (chunks > 0).any(axis=2)).any(axis=-1)
     return float(wide.mean())
 
 
