@@ -66,6 +66,7 @@ struct WaveJobs {
   static constexpr int RPW = kWide ? NBLK / kScanWaves : 1;   // blocks per wave
   static constexpr int WPR = kWide ? 1 : kScanWaves / NBLK;   // waves per block
   static constexpr int TPW = (NT + WPR - 1) / WPR;            // tiles per wave and block
+  static constexpr bool kAllTiles = NT % WPR == 0;             // every (wave, u) names a tile < NT
   __device__ static int blk(int w, int r) { return kWide ? w + kScanWaves * r : w % NBLK; }
   __device__ static int tile(int w, int u) { return (kWide ? 0 : w / NBLK) + WPR * u; }
 };
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int u = 0; u < YNT; ++u) {
           const int n = YS == 1 ? J::tile(w, u) : u;
-          if (n >= NT) continue;
+          if (!(YS == 2 || J::kAllTiles) && n >= NT) continue;
           const Split fs = sT.get(16 * n + lr, 32 * (yh * YKS + s) + 8 * lq);
           mma(accY[u], fkb[r][s], fs);
           mma(accQ[u], fqb[r][s], fs);
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       for (int u = 0; u < J::TPW; ++u) {
         const int n = J::tile(w, u);
         accO[r][u] = accQ[u];
-        if (n >= NT) continue;
+        if (!J::kAllTiles && n >= NT) continue;
         f32x4 y;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     }
     load_y(c1);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);          // keep each phase's work (and waits) in its phase
 
     // ---- E = diag(beta) A Y
 #pragma unroll
@@ -284,22 +286,22 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) accE[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) {
-        if (s * 32 >= 16 * I + 16) continue;   // A_c is lower triangular
+      for (int s = 0; s < CSTEPS; ++s) {        // all steps: A_c is zero above its diagonal blocks
 #pragma unroll
         for (int u = 0; u < J::TPW; ++u) {
           const int n = J::tile(w, u);
-          if (n < NT) mma(accE[u], fa[r][s], yT.get(16 * n + lr, 32 * s + 8 * lq));
+          if (J::kAllTiles || n < NT) mma(accE[u], fa[r][s], yT.get(16 * n + lr, 32 * s + 8 * lq));
         }
       }
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) {
         const int n = J::tile(w, u);
-        if (n < NT) eT.put4(16 * n + lr, 16 * I + 4 * lq, accE[u]);
+        if (J::kAllTiles || n < NT) eT.put4(16 * n + lr, 16 * I + 4 * lq, accE[u]);
       }
     }
     load_a(c1);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- O = Qbar S + L E
     TOut *o_c = at_chunk(op, v_row, c);
@@ -307,19 +309,18 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     for (int r = 0; r < J::RPW; ++r) {
       const int I = J::blk(w, r);
 #pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) {
-        if (s * 32 >= 16 * I + 16) continue;   // L_c is lower triangular
+      for (int s = 0; s < CSTEPS; ++s) {        // all steps: L_c is zero above its diagonal blocks
 #pragma unroll
         for (int u = 0; u < J::TPW; ++u) {
           const int n = J::tile(w, u);
-          if (n < NT) mma(accO[r][u], fl[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
+          if (J::kAllTiles || n < NT) mma(accO[r][u], fl[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
         }
       }
       const unsigned o_off = (16 * I + 4 * lq) * v_row + hv * a.d_v + c0 + lr;
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) {
         const int n = J::tile(w, u);
-        if (n >= NT) continue;
+        if (!J::kAllTiles && n >= NT) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (!kTail || row_ok(c, 16 * I + 4 * lq + e)) st(at(o_c, o_off + e * v_row + 16 * n), accO[r][u][e]);
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       }
     }
     load_l(c1);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- S = F_c S + Khat^T E
 #pragma unroll
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       const int i0 = 16 * SJ::blk(w, r);
 #pragma unroll
       for (int u = 0; u < SJ::TPW; ++u) {
-        if (SJ::tile(w, u) >= NT) continue;
+        if (!SJ::kAllTiles && SJ::tile(w, u) >= NT) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[r][u][e] *= gm[r][e];
       }
@@ -343,19 +345,27 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int u = 0; u < SJ::TPW; ++u) {
           const int n = SJ::tile(w, u);
-          if (n < NT) mma(S[r][u], fkh[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
+          if (SJ::kAllTiles || n < NT) mma(S[r][u], fkh[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
         }
       }
 #pragma unroll
       for (int u = 0; u < SJ::TPW; ++u) {
         const int n = SJ::tile(w, u);
-        if (n < NT) sT.put4(16 * n + lr, i0 + 4 * lq, S[r][u]);
+        if (SJ::kAllTiles || n < NT) sT.put4(16 * n + lr, i0 + 4 * lq, S[r][u]);
       }
     }
     load_s(c1);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  for (int c = 0; c + 1 < a.N_c; ++c) step(c, std::integral_constant<bool, false>());
+  // The first chunk is peeled so the loop is entered from an iteration with
+  // the same memory-instruction order as its own back edge: the compiler's
+  // wait counts at the loop head then allow the whole next-chunk prefetch to
+  // stay in flight.
+  if (a.N_c > 1) {
+    step(0, std::integral_constant<bool, false>());
+    for (int c = 1; c + 1 < a.N_c; ++c) step(c, std::integral_constant<bool, false>());
+  }
   if (a.N_c > 0) step(a.N_c - 1, std::integral_constant<bool, true>());
 
   if (a.hT) {
