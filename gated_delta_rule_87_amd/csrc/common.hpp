@@ -212,6 +212,9 @@ __device__ __forceinline__ void mma(f32x4 &c, const FragS &a, const FragS &b) {
   c = mfma_bf16(a.h, b.l, c);
   c = mfma_bf16(a.h, b.h, c);
 }
+__device__ __forceinline__ void mma(f32x4 &c, const FragH &a, const FragH &b) {
+  c = mfma_f16(a.h, b.h, c);
+}
 __device__ __forceinline__ void mma(f32x4 &c, const FragH &a, const FragHS &b) {
   c = mfma_f16(a.h, b.l, c);
   c = mfma_f16(a.h, b.h, c);
@@ -362,6 +365,33 @@ template <> struct OperandLds<PrecF32> {
     return f;
   }
 };
+
+// LDS storage of the state operand S^T (B fragments, same addressing as
+// OperandLds): one fp16 plane for the fp16 policy -- the state itself stays
+// in fp32 accumulators, only the operand copy of each chunk is rounded once
+// -- and the fp32 plane for the fp32 policy.
+template <class P> struct StateLds;
+template <> struct StateLds<PrecF16> {
+  f16 *v;
+  int ld;
+  __device__ __forceinline__ void init(void *base, int /*n_rows*/, int ld_) {
+    v = reinterpret_cast<f16 *>(base);
+    ld = ld_;
+  }
+  __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
+    typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = static_cast<f16>(x[r]);
+    *reinterpret_cast<f16x4 *>(v + n * ld + k) = h;
+  }
+  __device__ __forceinline__ FragH get(int n, int k) const {
+    FragH f;
+    f.h = *reinterpret_cast<const f16x8 *>(v + n * ld + k);
+    return f;
+  }
+};
+template <> struct StateLds<PrecF32> : OperandLds<PrecF32> {};
 
 // LDS storage of an operand read back as Plain fragments, same addressing as
 // OperandLds: bf16 policy one bf16 plane, fp32 policy one fp32 plane.

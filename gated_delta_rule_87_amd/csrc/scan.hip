@@ -17,11 +17,15 @@
 // workgroups is exact.
 //
 // Operand precision (bf16 inputs): the prepared operands diag(beta) A_c, L_c,
-// Kbar, Qbar and Khat are single fp16 (11 significant bits); the state S and
-// the intermediates Y and E are split fp16 pairs (x = hi + lo, hi = fp16(x)),
-// so every product is two fp16 MFMAs with fp32 accumulation.  bf16 (8 bits)
-// is too coarse for Qbar, Khat, L, S, Y and E: rounding any one of them to
-// bf16 breaks a 1e-2 max-error bar on the per-channel-gate workload.
+// Kbar, Qbar and Khat are single fp16 (11 significant bits), and so is the
+// per-chunk operand copy of the state S (S itself accumulates in fp32
+// registers); the intermediates Y and E are split fp16 pairs (x = hi + lo,
+// hi = fp16(x)), so their products are two fp16 MFMAs with fp32
+// accumulation.  bf16 (8 bits) is too coarse for Qbar, Khat, L, S, Y and E:
+// rounding any one of them to bf16 breaks a 1e-2 max-error bar on the
+// per-channel-gate workload.  Rounding the S operand to single fp16 leaves
+// the error where the split pair had it; rounding Y or E as well would add
+// about a quarter each.
 //
 // Organisation.  Eight waves, two per SIMD, so one wave's memory and LDS
 // latency hides behind the other's arithmetic.  Jobs per chunk: Y, E and O
@@ -84,7 +88,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   using Lay = ScanLayout<C, DK, BV>;
   using IO = TileIO<P>;
   using Plain = typename P::Plain;
-  using Split = typename P::Split;
   constexpr int NB = C / 16;                  // token row blocks
   constexpr int NT = BV / 16;                 // column tiles
   using J = WaveJobs<NB, NT>;                 // Y / E / O jobs
@@ -121,7 +124,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   const int hk = hv / R;
   const int hb = a.beta_per_key_head ? hk : hv;
 
-  OperandLds<P> sT, yT, eT;
+  StateLds<P> sT;
+  OperandLds<P> yT, eT;
   sT.init(smem_raw, BV, Lay::S_LD);
   yT.init(smem_raw + Lay::s_bytes, BV, Lay::Y_LD);
   eT.init(smem_raw + Lay::s_bytes + Lay::y_bytes, BV, Lay::Y_LD);
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         for (int u = 0; u < YNT; ++u) {
           const int n = YS == 1 ? J::tile(w, u) : u;
           if (!(YS == 2 || J::kAllTiles) && n >= NT) continue;
-          const Split fs = sT.get(16 * n + lr, 32 * (yh * YKS + s) + 8 * lq);
+          const auto fs = sT.get(16 * n + lr, 32 * (yh * YKS + s) + 8 * lq);
           mma(accY[u], fkb[r][s], fs);
           mma(accQ[u], fqb[r][s], fs);
         }
