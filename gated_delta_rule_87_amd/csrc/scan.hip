@@ -54,9 +54,9 @@ struct ScanLayout {
   static constexpr int Y_LD = C + 8;    // Y^T, E^T rows
   static constexpr size_t s_bytes = 4 * (size_t)BV * S_LD;
   static constexpr size_t y_bytes = 4 * (size_t)BV * Y_LD;
-  // Y split over channel steps (fewer row blocks than waves, d_k = 256):
+  // Y split over channel steps (fewer row blocks than waves, d_k >= 128):
   // partial Y and Qbar S products exchanged through [C/16][BV/16][2][64] f32x4
-  static constexpr bool kYSplit = (C / 16 < 8) && DK >= 256;
+  static constexpr bool kYSplit = (C / 16 < 8) && DK >= 128;
   static constexpr size_t x_bytes = kYSplit ? (size_t)(C / 16) * (BV / 16) * 2 * 64 * 16 : 0;
   static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes;
 };
@@ -95,12 +95,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   constexpr int KSTEPS = DK / 32;             // contraction steps over channels
   constexpr int CSTEPS = C / 32;              // contraction steps over tokens
   // Y jobs: when two waves share a row block (J::WPR = 2) and the rows are
-  // long (d_k = 256), they split its channel steps (each loads half of the
+  // long (d_k >= 128), they split its channel steps (each loads half of the
   // block's Kbar / Qbar rows and forms partial products for every column
   // tile) instead of loading the same rows twice; the partials are summed
-  // through LDS by the wave that owns the tile.  At d_k <= 128 the extra
-  // barrier costs more than the halved loads save, and the two waves split
-  // the column tiles instead.
+  // through LDS by the wave that owns the tile.  The chunk step is bound by
+  // the issue of its vector memory instructions, so halving them is worth
+  // the extra barrier; at d_k = 64 the two waves split the column tiles.
   constexpr int YS = Lay::kYSplit ? 2 : 1;    // waves splitting a row block's channel steps
   static_assert(!Lay::kYSplit || J::WPR == 2, "channel split needs two waves per row block");
   constexpr int YKS = KSTEPS / YS;            // channel steps per wave in Y
