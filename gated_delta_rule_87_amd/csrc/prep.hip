@@ -934,9 +934,10 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   if ((e = set_lds(listed, lds)) != hipSuccess) return e;
   hipLaunchKernelGGL(chunk, grid, dim3(256), chunk_lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // wide-range chunks, if any: at most 256 items per work group
+  // wide-range chunks, if any: two work groups per CU (the LDS of the block
+  // route allows two), at most 256 items each
   const long n = (long)a.N_c * a.H_k * a.B;
-  const long groups = std::max(std::min(n, 1024L), (n + 255) / 256);
+  const long groups = std::max(std::min(n, 512L), (n + 255) / 256);
   hipLaunchKernelGGL(listed, dim3((unsigned)groups), dim3(256), lds, stream, a);
   return hipGetLastError();
   }
