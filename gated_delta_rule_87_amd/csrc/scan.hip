@@ -242,28 +242,34 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       for (int s = 0; s < YKS; ++s) {
 #pragma unroll
         for (int u = 0; u < YNT; ++u) {
-          const int n = YS == 1 ? J::tile(w, u) : u;
+          // channel split: accumulator 0 is this wave's own tile yh
+          const int n = YS == 1 ? J::tile(w, u) : (yh + u) % NT;
           if (!(YS == 2 || J::kAllTiles) && n >= NT) continue;
           const auto fs = sT.get(16 * n + lr, 32 * (yh * YKS + s) + 8 * lq);
           mma(accY[u], fkb[r][s], fs);
           mma(accQ[u], fqb[r][s], fs);
         }
       }
-      if constexpr (YS == 2) {
-        // hand the partials of the tile the other wave owns to it: tile n is
-        // finished by the wave with yh == n
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (n == yh) continue;
-          f32x4 *slot = xch + ((I * NT + n) * 2) * 64;
-          slot[l] = accY[n];
-          slot[64 + l] = accQ[n];
+      if constexpr (YS == 2 && NT == 2) {
+        // hand the partials of the partner's tile (accumulator 1) to it
+        f32x4 *give = xch + ((I * NT + 1 - yh) * 2) * 64;
+        give[l] = accY[1];
+        give[64 + l] = accQ[1];
+        __syncthreads();
+        const f32x4 *take = xch + ((I * NT + yh) * 2) * 64;
+        accY[0] += take[l];
+        accQ[0] += take[64 + l];
+      } else if constexpr (YS == 2) {
+        // one tile: the yh = 1 wave only contributes its partials
+        f32x4 *slot = xch + (I * NT * 2) * 64;
+        if (yh == 1) {
+          slot[l] = accY[0];
+          slot[64 + l] = accQ[0];
         }
         __syncthreads();
-        if (yh < NT) {
-          const f32x4 *slot = xch + ((I * NT + yh) * 2) * 64;
-          accY[0] = accY[yh] + slot[l];
-          accQ[0] = accQ[yh] + slot[64 + l];
+        if (yh == 0) {
+          accY[0] += slot[l];
+          accQ[0] += slot[64 + l];
         }
       }
 #pragma unroll
