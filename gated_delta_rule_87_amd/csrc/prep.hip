@@ -129,18 +129,21 @@ __device__ __forceinline__ void tile_f32_n(f32x4 &acc, const FX &x, const FY &y,
   for (int u = 0; u < 4 * N; ++u) acc = mfma_f32(xa[u], yb[u], acc);
 }
 
-// Same over [k0, k1), k1 - k0 a multiple of 16 up to 128.
-template <class FX, class FY>
+// Same over [k0, k1), k1 - k0 a multiple of 16 up to 16 NMAX (the longest
+// contraction the caller can reach; the registers of the unrolled loads are
+// sized for it).
+template <int NMAX, class FX, class FY>
 __device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, int k0, int k1) {
+  static_assert(NMAX >= 1 && NMAX <= 8, "contraction of 16 to 128");
   switch ((k1 - k0) >> 4) {
     case 1: tile_f32_n<1>(acc, x, y, k0); break;
-    case 2: tile_f32_n<2>(acc, x, y, k0); break;
-    case 3: tile_f32_n<3>(acc, x, y, k0); break;
-    case 4: tile_f32_n<4>(acc, x, y, k0); break;
-    case 5: tile_f32_n<5>(acc, x, y, k0); break;
-    case 6: tile_f32_n<6>(acc, x, y, k0); break;
-    case 7: tile_f32_n<7>(acc, x, y, k0); break;
-    case 8: tile_f32_n<8>(acc, x, y, k0); break;
+    case 2: if constexpr (NMAX >= 2) tile_f32_n<2>(acc, x, y, k0); break;
+    case 3: if constexpr (NMAX >= 3) tile_f32_n<3>(acc, x, y, k0); break;
+    case 4: if constexpr (NMAX >= 4) tile_f32_n<4>(acc, x, y, k0); break;
+    case 5: if constexpr (NMAX >= 5) tile_f32_n<5>(acc, x, y, k0); break;
+    case 6: if constexpr (NMAX >= 6) tile_f32_n<6>(acc, x, y, k0); break;
+    case 7: if constexpr (NMAX >= 7) tile_f32_n<7>(acc, x, y, k0); break;
+    case 8: if constexpr (NMAX >= 8) tile_f32_n<8>(acc, x, y, k0); break;
     default: break;
   }
 }
@@ -148,14 +151,14 @@ __device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, i
 // ------------------------------------------------------------- exact solve
 // amat <- (I + M)^{-1}, M = gmat diag(bet): 16x16 diagonal blocks by forward
 // substitution (one lane per column), then block-doubling merges
-// A[B,T] = -A[B,B] (M[B,T] A[T,T]) with fp32 MFMA.
+// A[B,T] = -A[B,B] (M[B,T] A[T,T]) with fp32 MFMA.  Only the diagonal and
+// lower 16x16 blocks of amat are written (and read): the blocks above the
+// diagonal are zero by construction and left to the caller.
 template <int C>
 __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  for (int i = tid; i < C * LD; i += blockDim.x) amat[i] = 0.f;
-  __syncthreads();
   if (tid < NB * 16) {
     const int base = 16 * (tid >> 4), cc = tid & 15;
     float bl[16], x[16];
@@ -190,7 +193,7 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
       const int top = 2 * bs * p, bot = top + bs;
       const int r0 = bot + 16 * ti, c0 = top + 16 * tj;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      tile_f32(acc,
+      tile_f32<C / 32>(acc,
                [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
                [&](int k, int j) { return amat[k * LD + c0 + j]; },
                c0, top + bs);                 // A[top,top] is lower: rows k >= column
@@ -206,7 +209,7 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
       const int r0 = bot + 16 * ti;
       const float *X = tmp + p * bs * XLD;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      tile_f32(acc,
+      tile_f32<C / 32>(acc,
                [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
                [&](int k, int j) { return X[(k - bot) * XLD + 16 * tj + j]; },
                bot, r0 + 16);                 // A[bot,bot] is lower: columns k <= row
@@ -243,7 +246,7 @@ __device__ __forceinline__ void solve_neumann(const float *gmat, const float *be
       for (int I = J + w; I < NB; I += nw, ++nt) {
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int r0 = 16 * I;
-        tile_f32(acc[nt], [&](int i, int k) { return Mx(i, k, r0); },
+        tile_f32<C / 16>(acc[nt], [&](int i, int k) { return Mx(i, k, r0); },
                  [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, r0 + 16);
       }
       __syncthreads();
@@ -264,7 +267,7 @@ __device__ __forceinline__ void solve_neumann(const float *gmat, const float *be
       for (int I = J + w; I < NB; I += nw) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const int r0 = 16 * I;
-        tile_f32(acc, [&](int i, int k) { return Mx(i, k, r0); },
+        tile_f32<C / 16>(acc, [&](int i, int k) { return Mx(i, k, r0); },
                  [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, r0 + 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -278,7 +281,7 @@ __device__ __forceinline__ void solve_neumann(const float *gmat, const float *be
       for (int I = J + w; I < NB; I += nw, ++nt) {
         acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int r0 = 16 * I;
-        tile_f32(acc[nt], [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
+        tile_f32<C / 16>(acc[nt], [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
                  [&](int k, int j) { return tmp[k * TLD + j]; }, 16 * J, r0 + 16);
       }
       __syncthreads();
@@ -507,26 +510,38 @@ struct PrepItem {
     }
   }
 
-  // Per beta head: A = (I + G diag(beta))^{-1} from gsolve into asolve (row
-  // stride C + 4 both), then diag(beta) A to the workspace.  beta is loaded
-  // here, into short-lived registers.
-  __device__ __forceinline__ void solve_store(float *gsolve, float *asolve) const {
-    constexpr int NBET = 4;                            // up to 4 * 256 beta values (C * Rb)
-    TIn bets[NBET];
+  // beta of the chunk for every beta head of this key head: element e of
+  // thread tid's register j is e = tid + 256 j = rb * C + t (up to 4 * 256
+  // values, C * Rb)
+  static constexpr int NBET = 4;
+  __device__ __forceinline__ void load_betas(TIn (&bets)[NBET]) const {
 #pragma unroll
     for (int j = 0; j < NBET; ++j) {
-      const int e = min(tid + 256 * j, C * Rb - 1);    // e = rb * C + t
+      const int e = min(tid + 256 * j, C * Rb - 1);
       bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
     }
+  }
+  __device__ __forceinline__ void put_betas(const TIn (&bets)[NBET], int rb) const {
+#pragma unroll
+    for (int j = 0; j < NBET; ++j) {
+      const int e = tid + 256 * j;
+      if (e / C == rb && e < C * Rb) bet[e % C] = (t0 + e % C < T) ? static_cast<float>(bets[j]) : 0.f;
+    }
+  }
+
+  // Per beta head: A = (I + G diag(beta))^{-1} from gsolve into asolve (row
+  // stride C + 4 both), then diag(beta) A to the workspace, the blocks above
+  // the diagonal as zeros.  bet0_ready: the first head's beta is already in
+  // LDS (written before a barrier that precedes the call).
+  __device__ __forceinline__ void solve_store(float *gsolve, float *asolve, const TIn (&bets)[NBET],
+                                              bool bet0_ready) const {
     for (int rb = 0; rb < Rb; ++rb) {
       const int hb = hk * Rb + rb;
       __syncthreads();
-#pragma unroll
-      for (int j = 0; j < NBET; ++j) {
-        const int e = tid + 256 * j;
-        if (e / C == rb && e < C * Rb) bet[e % C] = (t0 + e % C < T) ? static_cast<float>(bets[j]) : 0.f;
+      if (rb > 0 || !bet0_ready) {
+        put_betas(bets, rb);
+        __syncthreads();
       }
-      __syncthreads();
       if (a.solve == 0) {
         solve_exact<C>(gsolve, bet, asolve, tmp);
       } else {
@@ -540,8 +555,11 @@ struct PrepItem {
         const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
         const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
         const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
+        const bool upper = col / 16 > row / 16;             // above the diagonal blocks: never written
         const float bt = bet[row];
-        const float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
+        float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = upper ? 0.f : x[e];
         IO::put_plain8(tA, blk, f, x);
       }
     }
@@ -574,14 +592,16 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   using X = PrepItem<TIn, P, C, DK>;
   using Split = typename X::Split;
-  constexpr int NB = X::NB, KS = X::KS;
+  constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw), prep_chunk_region0_floats(C));
+  const X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw),
+            prep_chunk_region0_floats(C));
   const int I = x.w, lr = x.lr, lq = x.lq, gs = x.gs, G = x.G;
   const int tr = 16 * I + lr;
   const float mt = (x.t0 + tr < x.T) ? 1.f : 0.f;
 
-  // ---- loads: log alpha of the lane's token, then its key and query rows
+  // ---- all loads of the item, issued together: log alpha of the lane's
+  // token, its key and query rows, beta
   const TIn *larow = x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G;
   Raw8<TIn> lav[kVecLa ? KS : 1];
   TIn las[4];
@@ -595,6 +615,9 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   Raw8<TIn> kt[KS], qt[KS];
   x.load_rows(kt, x.kbase, I);
   x.load_rows(qt, x.qbase, I);
+  TIn bets[NBET];
+  x.load_betas(bets);
+
 
   // ---- Lambda of the lane's token in log2 units (log2(e) Lambda): in-block
   // prefix, then block offsets
@@ -656,6 +679,7 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   if (x.tid == 0) x.flags[kChunkWide] = 0;
   const bool any_rising = __ballot(rising) != 0;
   __syncthreads();
+  x.put_betas(bets, 0);                               // the solve's first beta head, read after later barriers
   if (lr == 0 && lq == 0 && any_rising) x.flags[kChunkWide] = 1;
   if (x.tid < DK) {
     const int ch = x.tid;
@@ -673,7 +697,8 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     gc[ch] = __builtin_amdgcn_exp2f(run);
   }
   __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(x.flags[kChunkWide])) {
+  const bool wide = __builtin_amdgcn_readfirstlane(x.flags[kChunkWide]) != 0;
+  if (wide) {
     if (x.tid == 0) x.gm_row()[0] = kWideMark;         // left to the block-pivot kernel
     return;
   }
@@ -683,7 +708,6 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     const float4 v = *reinterpret_cast<const float4 *>(p + 4);
     y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w; y[4] = v.x; y[5] = v.y; y[6] = v.z; y[7] = v.w;
   };
-
   // ---- row and column operands, scan operands, the diagonal pair
   unsigned char *colop = reinterpret_cast<unsigned char *>(x.ureg);
   Split ak[KS], aq[KS];
@@ -703,14 +727,14 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     for (int e = 0; e < 8; ++e) {
       const float l2 = lt[s][e] + o[e];                // log2(e) Lambda_t
       const float d = __builtin_amdgcn_exp2f(l2);      // exp(Lambda_t)
-      const float u = __builtin_amdgcn_exp2f(-l2);     // exp(-Lambda_t)
+      const float ui = __builtin_amdgcn_exp2f(-l2);    // exp(-Lambda_t)
       const float k = xk[e] * mt, q = xq[e] * mt;
       yk[e] = k * (d * f0i[e]);                        // row side, exp(Lambda_t - Lambda_0)
       yq[e] = q * (d * f0i[e]);
-      yb[e] = k * (u * f0[e]);                         // column side, exp(Lambda_0 - Lambda_t)
+      yb[e] = k * (ui * f0[e]);                        // column side, exp(Lambda_0 - Lambda_t)
       kbar[e] = k * d;
       qbar[e] = q * d;
-      kh[e] = k * (u * fc[e]);                         // exp(Lambda_C - Lambda_t)
+      kh[e] = k * (ui * fc[e]);                        // exp(Lambda_C - Lambda_t)
     }
     ak[s] = make_frag<Split>(yk);
     aq[s] = make_frag<Split>(yq);
@@ -741,7 +765,7 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     x.store_L_block(I, J, accL);
   }
   x.zero_upper_L();
-  x.solve_store(gsolve, x.ureg);
+  x.solve_store(gsolve, x.ureg, bets, true);
 }
 
 // Block-pivot route for one chunk: p = first token of the row block; every
@@ -853,7 +877,9 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
     }
   }
   x.zero_upper_L();
-  x.solve_store(gmat, x.smem);
+  TIn bets[X::NBET];                                   // beta loaded here: short-lived registers
+  x.load_betas(bets);
+  x.solve_store(gmat, x.smem, bets, false);
 }
 
 // Grid (N_c, H_k, B), one chunk per work group.
