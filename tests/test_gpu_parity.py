@@ -37,10 +37,20 @@ SMALL = {
                               alpha_mu=0.75, alpha_sigma=2.0, seed=9),
     "gdn_f32_c64_mixed": Workload("gdn_f32_c64_mixed", 2, 450, 2, 2, 64, 64, 64, 1, "f32",
                                   alpha_mu=0.0, alpha_sigma=2.0, seed=10),
+    # grouped gates whose 8-channel lanes span 1 group (G = 16) or 2 (G = 32)
+    # of a d_k = 128 head, per-key-head beta with grouped value heads, both
+    # routes
+    "gva_bkh_mixed": Workload("gva_bkh_mixed", 1, 450, 2, 8, 128, 32, 64, 16, "bf16", alpha_mu=0.5,
+                              alpha_sigma=2.0, beta_per_key_head=True, seed=13),
+    "g32_mixed": Workload("g32_mixed", 2, 333, 2, 2, 128, 48, 64, 32, "bf16", alpha_mu=0.5, alpha_sigma=2.0,
+                          seed=14),
+    # one token; one ragged chunk with 8 groups of 8 channels
+    "t1_bf16": Workload("t1_bf16", 2, 1, 2, 2, 128, 64, 64, 128, "bf16", seed=11),
+    "t63_f32_g8": Workload("t63_f32_g8", 1, 63, 2, 2, 64, 32, 64, 8, "f32", seed=12),
 }
 
 # the cases above with chunks on both sides of the chunk-pivot range limit
-MIXED = ("kda_c64_mixed", "gdn_f32_c64_mixed")
+MIXED = ("kda_c64_mixed", "gdn_f32_c64_mixed", "gva_bkh_mixed", "g32_mixed")
 
 
 def oracle(x, w, h0=None, units=None):
@@ -84,6 +94,7 @@ def test_chunk_fwd_nonzero_h0(name):
 
 
 @pytest.mark.parametrize("name,order,res", [("kda_c128_strong", 4, 1), ("kda_bf16", 2, 1), ("kda_f32_c128", 3, 2),
+                                            ("kda_c64_mixed", 3, 1), ("gdn_f32_c64_mixed", 4, 1),
                                             ("gva_g4_bf16", 1, 0)])
 def test_neumann_small(name, order, res):
     w = SMALL[name].with_(neumann_order=order, neumann_residual=res)
@@ -125,7 +136,8 @@ def expected_operands(x, w):
 
 
 @pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong",
-                                  "dk64_bkh_gva", "dk256_kda_bf16", "kda_c64_mixed", "gdn_f32_c64_mixed"])
+                                  "dk64_bkh_gva", "dk256_kda_bf16", "kda_c64_mixed", "gdn_f32_c64_mixed",
+                                  "gva_bkh_mixed", "g32_mixed", "t63_f32_g8"])
 @pytest.mark.parametrize("solve", ["exact", "neumann"])
 def test_prepared_workspace(name, solve):
     """Every prepared chunk quantity against the fp64 chunk pieces: diag(beta)
