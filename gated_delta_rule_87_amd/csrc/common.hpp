@@ -129,9 +129,6 @@ __device__ __forceinline__ void prefix_column(float *col, int ld) {
 }
 
 // ----------------------------------------------------------------- fragments
-struct FragP {            // plain bf16
-  bf16x8 h;
-};
 struct FragS {            // split bf16 hi + lo
   bf16x8 h, l;
 };
@@ -147,12 +144,6 @@ struct FragHS {           // split fp16 hi + lo
 
 template <class F> __device__ __forceinline__ F make_frag(const float (&x)[8]);
 
-template <> __device__ __forceinline__ FragP make_frag<FragP>(const float (&x)[8]) {
-  FragP f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.h[e] = to_bf16(x[e]);
-  return f;
-}
 template <> __device__ __forceinline__ FragS make_frag<FragS>(const float (&x)[8]) {
   FragS f;
 #pragma unroll
@@ -196,17 +187,6 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void mma(f32x4 &c, const FragP &a, const FragP &b) {
-  c = mfma_bf16(a.h, b.h, c);
-}
-__device__ __forceinline__ void mma(f32x4 &c, const FragP &a, const FragS &b) {
-  c = mfma_bf16(a.h, b.l, c);
-  c = mfma_bf16(a.h, b.h, c);
-}
-__device__ __forceinline__ void mma(f32x4 &c, const FragS &a, const FragP &b) {
-  c = mfma_bf16(a.l, b.h, c);
-  c = mfma_bf16(a.h, b.h, c);
-}
 __device__ __forceinline__ void mma(f32x4 &c, const FragS &a, const FragS &b) {
   c = mfma_bf16(a.l, b.h, c);
   c = mfma_bf16(a.h, b.l, c);
@@ -225,9 +205,9 @@ __device__ __forceinline__ void mma(f32x4 &c, const FragF &a, const FragF &b) {
 }
 
 // Precision policies.  Each kernel names, per operand, whether it needs the
-// Split kind; the fp32 policy maps every kind to FragF.
+// Split kind; the fp32 policy maps every kind to FragF.  Split bf16 pairs
+// (bf16 range, about 16 significant bits) for the Gram of the prep kernels.
 struct PrecBF16 {
-  using Plain = FragP;
   using Split = FragS;
   static constexpr bool kF32 = false;
 };
@@ -247,66 +227,9 @@ struct PrecF16 {
 
 // LDS storage of an operand that is read back as B fragments: element (n, k)
 // of an N x K operand (column n of the B matrix, contraction index k) lives at
-// n * ld + k, so a fragment is eight consecutive values.  bf16 policy: hi and
+// n * ld + k, so a fragment is eight consecutive values.  fp16 policy: hi and
 // lo planes; fp32 policy: one fp32 plane (same bytes).
 template <class P> struct OperandLds;
-
-template <> struct OperandLds<PrecBF16> {
-  bf16 *hi;
-  bf16 *lo;
-  int ld;
-  static constexpr int kBytesPerElem = 4;
-  __device__ __forceinline__ void init(void *base, int n_rows, int ld_) {
-    hi = reinterpret_cast<bf16 *>(base);
-    lo = hi + n_rows * ld_;
-    ld = ld_;
-  }
-  __device__ __forceinline__ void put(int n, int k, float x) {
-    const bf16 h = to_bf16(x);
-    hi[n * ld + k] = h;
-    lo[n * ld + k] = to_bf16(x - static_cast<float>(h));
-  }
-  // four consecutive k for one n (D-layout rows of one column)
-  __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
-    typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 h, l;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      h[r] = to_bf16(x[r]);
-      l[r] = to_bf16(x[r] - static_cast<float>(h[r]));
-    }
-    *reinterpret_cast<bf16x4 *>(hi + n * ld + k) = h;
-    *reinterpret_cast<bf16x4 *>(lo + n * ld + k) = l;
-  }
-  // eight consecutive k for one n
-  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
-    bf16x8 h, l;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      h[r] = to_bf16(x[r]);
-      l[r] = to_bf16(x[r] - static_cast<float>(h[r]));
-    }
-    *reinterpret_cast<bf16x8 *>(hi + n * ld + k) = h;
-    *reinterpret_cast<bf16x8 *>(lo + n * ld + k) = l;
-  }
-  // two consecutive k for one n (one dword per plane)
-  __device__ __forceinline__ void put2(int n, int k, float x0, float x1) {
-    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 h, l;
-    h[0] = to_bf16(x0);
-    h[1] = to_bf16(x1);
-    l[0] = to_bf16(x0 - static_cast<float>(h[0]));
-    l[1] = to_bf16(x1 - static_cast<float>(h[1]));
-    *reinterpret_cast<bf16x2 *>(hi + n * ld + k) = h;
-    *reinterpret_cast<bf16x2 *>(lo + n * ld + k) = l;
-  }
-  __device__ __forceinline__ FragS get(int n, int k) const {
-    FragS f;
-    f.h = *reinterpret_cast<const bf16x8 *>(hi + n * ld + k);
-    f.l = *reinterpret_cast<const bf16x8 *>(lo + n * ld + k);
-    return f;
-  }
-};
 
 template <> struct OperandLds<PrecF16> {
   f16 *hi;
@@ -345,16 +268,9 @@ template <> struct OperandLds<PrecF32> {
     v = reinterpret_cast<float *>(base);
     ld = ld_;
   }
-  __device__ __forceinline__ void put(int n, int k, float x) { v[n * ld + k] = x; }
+  // four consecutive k for one n (D-layout rows of one column)
   __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
     *reinterpret_cast<f32x4 *>(v + n * ld + k) = x;
-  }
-  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
-    *reinterpret_cast<float4 *>(v + n * ld + k) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(v + n * ld + k + 4) = make_float4(x[4], x[5], x[6], x[7]);
-  }
-  __device__ __forceinline__ void put2(int n, int k, float x0, float x1) {
-    *reinterpret_cast<float2 *>(v + n * ld + k) = make_float2(x0, x1);
   }
   __device__ __forceinline__ FragF get(int n, int k) const {
     FragF f;
@@ -393,53 +309,6 @@ template <> struct StateLds<PrecF16> {
 };
 template <> struct StateLds<PrecF32> : OperandLds<PrecF32> {};
 
-// LDS storage of an operand read back as Plain fragments, same addressing as
-// OperandLds: bf16 policy one bf16 plane, fp32 policy one fp32 plane.
-template <class P> struct PlainLds;
-
-template <> struct PlainLds<PrecBF16> {
-  bf16 *v;
-  int ld;
-  static constexpr int kBytesPerElem = 2;
-  __device__ __forceinline__ void init(void *base, int ld_) {
-    v = reinterpret_cast<bf16 *>(base);
-    ld = ld_;
-  }
-  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
-    bf16x8 h;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) h[r] = to_bf16(x[r]);
-    *reinterpret_cast<bf16x8 *>(v + n * ld + k) = h;
-  }
-  __device__ __forceinline__ FragP get(int n, int k) const {
-    FragP f;
-    f.h = *reinterpret_cast<const bf16x8 *>(v + n * ld + k);
-    return f;
-  }
-};
-
-template <> struct PlainLds<PrecF32> {
-  float *v;
-  int ld;
-  static constexpr int kBytesPerElem = 4;
-  __device__ __forceinline__ void init(void *base, int ld_) {
-    v = reinterpret_cast<float *>(base);
-    ld = ld_;
-  }
-  __device__ __forceinline__ void put8(int n, int k, const float (&x)[8]) {
-    *reinterpret_cast<float4 *>(v + n * ld + k) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(v + n * ld + k + 4) = make_float4(x[4], x[5], x[6], x[7]);
-  }
-  __device__ __forceinline__ FragF get(int n, int k) const {
-    FragF f;
-    const float4 a = *reinterpret_cast<const float4 *>(v + n * ld + k);
-    const float4 b = *reinterpret_cast<const float4 *>(v + n * ld + k + 4);
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-  }
-};
-
 // ------------------------------------------------------------ workspace tiles
 // Fragment-major tiles: an R x K tile (R a multiple of 16, K of 32) is stored
 // as (R/16) x (K/32) blocks in row-block-major order; block (i, j) holds its
@@ -448,13 +317,6 @@ template <> struct PlainLds<PrecF32> {
 // operand lane f of a 16x16x32 MFMA reads, so a wave loads a block as one
 // contiguous run.  fp16 tiles: 1 KiB blocks, fragment f at byte 16 f; fp32
 // tiles: 2 KiB blocks, fragment f at byte 32 f.
-struct FragPos {
-  int blk, f, e;   // block, fragment, element within the fragment
-};
-__device__ __forceinline__ FragPos frag_pos(int r, int k, int K) {
-  return FragPos{(r >> 4) * (K >> 5) + (k >> 5), 16 * ((k & 31) >> 3) + (r & 15), k & 7};
-}
-
 template <class P> struct TileIO;
 
 // fp16 tiles (operands prepared from bf16 inputs): plain only, 1 KiB blocks.
@@ -467,9 +329,6 @@ template <> struct TileIO<PrecF16> {
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = static_cast<f16>(x[e]);
     *reinterpret_cast<f16x8 *>(at(t, blk, f)) = h;
-  }
-  __device__ static void put_plain(void *t, FragPos p, float x) {
-    reinterpret_cast<f16 *>(at(t, p.blk, p.f))[p.e] = static_cast<f16>(x);
   }
   __device__ static FragH get_plain(const void *t, int blk, int f) {
     FragH v;
@@ -487,9 +346,6 @@ template <> struct TileIO<PrecF32> {
     *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
   }
-  __device__ static void put_split8(void *t, int blk, int f, const float (&x)[8]) { put_plain8(t, blk, f, x); }
-  __device__ static void put_split(void *t, FragPos p, float x) { at(t, p.blk, p.f)[p.e] = x; }
-  __device__ static void put_plain(void *t, FragPos p, float x) { at(t, p.blk, p.f)[p.e] = x; }
   __device__ static FragF get_plain(const void *t, int blk, int f) {
     const float *p = at(const_cast<void *>(t), blk, f);
     const float4 a = *reinterpret_cast<const float4 *>(p);
@@ -499,7 +355,6 @@ template <> struct TileIO<PrecF32> {
     v.v[4] = b.x; v.v[5] = b.y; v.v[6] = b.z; v.v[7] = b.w;
     return v;
   }
-  __device__ static FragF get_split(const void *t, int blk, int f) { return get_plain(t, blk, f); }
 };
 
 }  // namespace gdr

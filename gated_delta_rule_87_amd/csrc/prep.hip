@@ -7,16 +7,19 @@
 // bf16 inputs, fp32 for fp32 inputs): diag(beta) A_c, L_c, Kbar_c, Qbar_c,
 // Khat_c^T, and exp(Lambda_C).
 //
-// Systolic Linear Attention (paperpeel 2611.06828):
+// Systolic Linear Attention: Co-Designing Tile-Grouped Gated Delta Attention
+// for TPUs:
 //  - cumulative log-decay Lambda and the chunk matrices: Table 2;
 //  - the Gram entries M_{t,j} = 1[t>j] beta_j sum_i exp(Lambda_{t,i} -
 //    Lambda_{j,i}) k_{t,i} k_{j,i}: section 2.2, "Bottleneck 2";
 //  - exp(+-Lambda) leaves fp32 once |Lambda| > 88.7: section 2.4.2;
 //  - the exact inverse by recursive block doubling: section 2.4.3.
-// Muir (ai.info 2611.08376), "Key Contributions" item 4: relative decays are
-// split at chunk-internal boundaries instead of dividing by cumulative decay.
-// Multiplication-only inversion paper (pith.science JIMYX2Z6): truncated
-// Neumann series with residual correction.
+// Muir: Linear Attention with Sensitivity-Allocated Gating and Matched-Filter
+// Readout, "Key Contributions": relative decays are split at chunk-internal
+// boundaries instead of dividing by cumulative decay.
+// When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
+// Approximation for Quantized Gated DeltaNet: truncated Neumann series with
+// residual correction.
 //
 // Division-free decay with block pivots.  The chunk is cut into 16-token
 // blocks.  For a block pair (I, J), I >= J, every t in I and j in J satisfy

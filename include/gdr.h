@@ -2,8 +2,8 @@
  * gdr.h -- C ABI of libgdr.so: chunkwise gated delta-rule forward on AMD
  * MI355X (gfx950).
  *
- * The operation (Systolic Linear Attention, paperpeel 2611.06828, section
- * 2.1, Eq. (2)): for every batch b and value head h, with key head
+ * The operation ("Systolic Linear Attention: Co-Designing Tile-Grouped Gated
+ * Delta Attention for TPUs", section 2.1, Eq. (2)): for every batch b and value head h, with key head
  * h_k = h / (H_v / H_k) and S_0 = h0 (or 0), for t = 1..T
  *
  *     S_t = (I - beta_t k_t k_t^T) F_t S_{t-1} + beta_t k_t v_t^T,
@@ -19,8 +19,9 @@
  * Table 2 and section 2.4.2): per chunk of C tokens it builds the strictly
  * lower-triangular Gram M_c and the score matrix L_c with division-free
  * relative decay, solves A_c = (I + M_c)^{-1} (exactly, or by the truncated
- * Neumann series with residual correction of the multiplication-only
- * inversion paper, pith.science JIMYX2Z6), and carries the d_k x d_v state
+ * Neumann series with residual correction of "When Good Enough Is Optimal:
+ * Multiplication-Only Matrix Inversion Approximation for Quantized Gated
+ * DeltaNet"), and carries the d_k x d_v state
  * across chunks.  gdr_recurrent_step runs the token recurrence directly (the
  * stateful step-by-step decoding of section 2.4.3).
  *

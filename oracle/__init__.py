@@ -11,7 +11,8 @@ used as a fallback for it.
   tile-grouped packed WY equivalence in section 2.4.2) in fp64 numpy, with the
   in-chunk inverse taken exactly, by recursive block doubling (section 2.4.3),
   or by the truncated Neumann series with residual correction (the
-  multiplication-only inversion paper, pith.science JIMYX2Z6).  It is the
+  paper "When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
+  Approximation for Quantized Gated DeltaNet").  It is the
   parity oracle for the Neumann mode and for per-stage checks.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``

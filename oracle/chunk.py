@@ -1,6 +1,7 @@
 """Chunkwise WY form of the gated delta rule in fp64 -- TEST INFRASTRUCTURE ONLY.
 
-Written from Systolic Linear Attention (paperpeel 2611.06828):
+Written from "Systolic Linear Attention: Co-Designing Tile-Grouped Gated Delta
+Attention for TPUs":
 
 * Table 2 (notation) defines, per chunk of C tokens and one key head:
   the in-chunk cumulative log-decay Lambda_{t,i} = sum_{s<=t} log f_{s,i};
@@ -26,8 +27,8 @@ In-chunk inverses:
   2.4.3 (merge two diagonal-block inverses with two products per merge).
   Exact algebra, pinned against ``exact_inverse``.
 * :func:`neumann_inverse` is the truncated Neumann series of the
-  multiplication-only inversion paper (pith.science JIMYX2Z6, core claim and
-  Fig. 5): X = sum_{s=0}^{m} (-M)^s ("order m" keeps powers 0..m, the reading
+  paper "When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
+  Approximation for Quantized Gated DeltaNet" (core claim and Fig. 5): X = sum_{s=0}^{m} (-M)^s ("order m" keeps powers 0..m, the reading
   under which ||A||^{m+1}/(1-||A||) bounds the tail), followed by r parallel
   residual corrections X <- X + X (I - (I + M) X).
 * :func:`block_neumann_inverse` is the block-Jacobi form of section 2.4.3's

@@ -1,6 +1,7 @@
 """Token-by-token fp64 gated delta rule -- TEST INFRASTRUCTURE ONLY.
 
-Follows Systolic Linear Attention (paperpeel 2611.06828), section 2.1,
+Follows "Systolic Linear Attention: Co-Designing Tile-Grouped Gated Delta
+Attention for TPUs", section 2.1,
 Eq. (2): per token, decay the state by the diagonal gate F_t, take the
 prediction error u_t = v_t - (F_t S_{t-1})^T k_t, write S_t = F_t S_{t-1} +
 beta_t k_t u_t^T, and read out o_t = S_t^T q_t after the update.
