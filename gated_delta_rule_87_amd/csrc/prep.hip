@@ -589,8 +589,11 @@ __device__ __forceinline__ float pick(const float (&f)[8], int i) {
 // through LDS.  Lambda never goes through LDS whole: each lane holds log
 // alpha of its token for its channels, the in-block prefix runs over the
 // 16 lanes of a DPP row, and only the block totals and the first token's
-// values are exchanged.  kVecLa: G >= 8 (log alpha read as 8-element vectors).
-template <typename TIn, class P, int DK, bool kVecLa>
+// values are exchanged.  kGate: how log alpha maps onto a lane's eight
+// channels (one value per channel, one 8-vector of groups, or at most four
+// groups read as scalars).
+enum GateMode { kGatePerChannel, kGateGroupsVec, kGateGroupsFew };
+template <typename TIn, class P, int DK, int kGate>
 __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   using X = PrepItem<TIn, P, C, DK>;
@@ -606,6 +609,7 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   // ---- all loads of the item, issued together: log alpha of the lane's
   // token, its key and query rows, beta
   const TIn *larow = x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G;
+  constexpr bool kVecLa = kGate != kGateGroupsFew;      // G >= 8: log alpha read as 8-element vectors
   Raw8<TIn> lav[kVecLa ? KS : 1];
   TIn las[4];
   if constexpr (kVecLa) {
@@ -631,12 +635,23 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int ch0 = 32 * s + 8 * lq;
-    if constexpr (kVecLa) {
+    if constexpr (kGate == kGatePerChannel) {
+      float f[8];
+      lav[s].to_float(f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lt[s][e] = f[e] * scale;
+    } else if constexpr (kGate == kGateGroupsVec) {
       float f[8];
       lav[s].to_float(f);
       const int g0 = min(ch0 >> gs, G - 8);
+      if (gs >= 3) {                                     // one group for the lane's eight channels
+        const float v = pick(f, (ch0 >> gs) - g0) * scale;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lt[s][e] = (gs == 0 ? f[e] : pick(f, ((ch0 + e) >> gs) - g0)) * scale;
+        for (int e = 0; e < 8; ++e) lt[s][e] = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lt[s][e] = pick(f, ((ch0 + e) >> gs) - g0) * scale;
+      }
     } else {
       // G < 8 < d_k / G: the lane's eight channels share one group
       const int g = ch0 >> gs;
@@ -731,7 +746,7 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
       const float l2 = lt[s][e] + o[e];                // log2(e) Lambda_t
       const float d = __builtin_amdgcn_exp2f(l2);      // exp(Lambda_t)
       const float ui = __builtin_amdgcn_exp2f(-l2);    // exp(-Lambda_t)
-      const float k = xk[e] * mt, q = xq[e] * mt;
+      const float k = xk[e] * mt, q = xq[e] * mt;       // tokens past T: zero rows
       yk[e] = k * (d * f0i[e]);                        // row side, exp(Lambda_t - Lambda_0)
       yq[e] = q * (d * f0i[e]);
       yb[e] = k * (ui * f0[e]);                        // column side, exp(Lambda_0 - Lambda_t)
@@ -956,7 +971,9 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(block, grid, dim3(256), lds, stream, a);
     return hipGetLastError();
   } else {
-  auto chunk = a.G >= 8 ? prep_chunk_kernel<TIn, P, DK, true> : prep_chunk_kernel<TIn, P, DK, false>;
+  auto chunk = a.G == DK  ? prep_chunk_kernel<TIn, P, DK, kGatePerChannel>
+               : a.G >= 8 ? prep_chunk_kernel<TIn, P, DK, kGateGroupsVec>
+                          : prep_chunk_kernel<TIn, P, DK, kGateGroupsFew>;
   auto listed = prep_block_listed_kernel<TIn, P, C, DK>;
   const size_t chunk_lds = prep_chunk_lds_bytes(C, DK);
   if ((e = set_lds(chunk, chunk_lds)) != hipSuccess) return e;
