@@ -58,7 +58,32 @@ struct ScanLayout {
   // partial Y and Qbar S products exchanged through [C/16][BV/16][2][64] f32x4
   static constexpr bool kYSplit = (C / 16 < 8) && DK >= 128;
   static constexpr size_t x_bytes = kYSplit ? (size_t)(C / 16) * (BV / 16) * 2 * 64 * 16 : 0;
-  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes;
+  // Row-major staging of one chunk's v tile and o tile (C x BV elements of
+  // up to 4 bytes, rows padded by 16 bytes).
+  static constexpr size_t st_bytes = (size_t)C * (4 * BV + 16);
+  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes + 2 * st_bytes;
+};
+
+// One thread's share when all 64 * kScanWaves threads move a row-major C x BV
+// tile of E-byte elements between HBM and LDS: NREP pieces of SW bytes, piece
+// k of thread t at byte (k * threads + t) * SW of the unpadded tile.  A wave
+// then covers whole rows with 8- or 16-byte accesses instead of one element
+// per lane in the MFMA layout (four rows of 16 elements per instruction).
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <int C, int BV, int E>
+struct RowSegs {
+  static constexpr int kThreads = 64 * kScanWaves;
+  static constexpr int BYTES = C * BV * E / kThreads;
+  static constexpr int SW = BYTES < 16 ? BYTES : 16;
+  static constexpr int NREP = BYTES / SW;
+  static constexpr int ROWB = BV * E;         // bytes of one tile row
+  static constexpr int PITCH = ROWB + 16;     // bytes of one staged row
+  static_assert(BYTES >= 4 && BYTES % SW == 0 && ROWB % SW == 0, "row pieces");
+  using Vec = typename std::conditional<SW == 4, unsigned,
+              typename std::conditional<SW == 8, u32x2, u32x4>::type>::type;
+  __device__ static int row(int t, int k) { return (k * kThreads + t) * SW / ROWB; }
+  __device__ static int colb(int t, int k) { return (k * kThreads + t) * SW % ROWB; }
 };
 
 // Distribution of (block, tile) jobs over the eight waves: with at least
@@ -130,6 +155,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   yT.init(smem_raw + Lay::s_bytes, BV, Lay::Y_LD);
   eT.init(smem_raw + Lay::s_bytes + Lay::y_bytes, BV, Lay::Y_LD);
   f32x4 *xch = reinterpret_cast<f32x4 *>(smem_raw + Lay::s_bytes + 2 * Lay::y_bytes);
+  using VS = RowSegs<C, BV, (int)sizeof(TIn)>;
+  using OS = RowSegs<C, BV, (int)sizeof(TOut)>;
+  unsigned char *vst = smem_raw + Lay::s_bytes + 2 * Lay::y_bytes + Lay::x_bytes;   // v_c, row-major
+  unsigned char *ost = vst + Lay::st_bytes;                                           // o_c, row-major
+  const int tid = threadIdx.x;
   const int yh = YS == 1 ? 0 : w / NB;        // this wave's half of the channel steps (YS = 2)
 
   const TIn *vp = reinterpret_cast<const TIn *>(a.v);
@@ -147,7 +177,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   Plain fl[J::RPW][CSTEPS];           // L_c rows
   Plain fkh[SJ::RPW][CSTEPS];         // Khat^T rows (channels) of each S block
   f32x4 gm[SJ::RPW];                  // exp(Lambda_C) of the block's rows of S
-  TIn vr[J::RPW][J::TPW][4];          // v entries (D layout)
+  typename VS::Vec vseg[VS::NREP];    // this thread's pieces of the v tile
 
   auto load_y = [&](int c) __attribute__((always_inline)) {
     const void *tkb = tile(kWsKB, a.H_k, hk, c), *tqb = tile(kWsQB, a.H_k, hk, c);
@@ -159,13 +189,36 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         fkb[r][s] = IO::get_plain(tkb, I * KSTEPS + yh * YKS + s, l);
         fqb[r][s] = IO::get_plain(tqb, I * KSTEPS + yh * YKS + s, l);
       }
+    }
+  };
+  // v_c: rows clamped to the last token (the tail's extra rows are masked
+  // where they are used); staged in LDS by put_v
+  auto load_v = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < J::TPW; ++u) {
-        const int col = min(c0 + 16 * J::tile(w, u) + lr, a.d_v - 1);
+    for (int k = 0; k < VS::NREP; ++k) {
+      const int t = VS::row(tid, k);
+      vseg[k] = *reinterpret_cast<const typename VS::Vec *>(
+          at(at_chunk(vp, v_row, c), crow(c, t) * v_row + hv * a.d_v + c0 + VS::colb(tid, k) / (int)sizeof(TIn)));
+    }
+  };
+  auto put_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vr[r][u][e] = *at(at_chunk(vp, v_row, c), crow(c, 16 * I + 4 * lq + e) * v_row + hv * a.d_v + col);
-      }
+    for (int k = 0; k < VS::NREP; ++k)
+      *reinterpret_cast<typename VS::Vec *>(vst + VS::row(tid, k) * VS::PITCH + VS::colb(tid, k)) = vseg[k];
+  };
+  auto v_at = [&](int t, int col) -> float {
+    return static_cast<float>(*reinterpret_cast<const TIn *>(vst + t * VS::PITCH + col * (int)sizeof(TIn)));
+  };
+  // o_c from its LDS staging, whole rows per wave
+  auto store_o = [&](int c, auto tail_tag) __attribute__((always_inline)) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    TOut *o_c = at_chunk(op, v_row, c);
+#pragma unroll
+    for (int k = 0; k < OS::NREP; ++k) {
+      const int t = OS::row(tid, k);
+      const auto val = *reinterpret_cast<const typename OS::Vec *>(ost + t * OS::PITCH + OS::colb(tid, k));
+      if (!kTail || row_ok(c, t))
+        *reinterpret_cast<typename OS::Vec *>(at(o_c, t * v_row + hv * a.d_v + c0 + OS::colb(tid, k) / (int)sizeof(TOut))) = val;
     }
   };
   auto load_a = [&](int c) __attribute__((always_inline)) {
@@ -217,9 +270,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   }
   if (a.N_c > 0) {
     load_y(0);
+    load_v(0);
     load_a(0);
     load_l(0);
     load_s(0);
+    put_v();
   }
   __syncthreads();
 
@@ -280,11 +335,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         f32x4 y;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          y[e] = (!kTail || row_ok(c, 16 * I + 4 * lq + e) ? static_cast<float>(vr[r][u][e]) : 0.f) - accY[u][e];
+          y[e] = (!kTail || row_ok(c, 16 * I + 4 * lq + e) ? v_at(16 * I + 4 * lq + e, 16 * n + lr) : 0.f) - accY[u][e];
         yT.put4(16 * n + lr, 16 * I + 4 * lq, y);
       }
     }
     load_y(c1);
+    load_v(c1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);          // keep each phase's work (and waits) in its phase
 
@@ -313,8 +369,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- O = Qbar S + L E
-    TOut *o_c = at_chunk(op, v_row, c);
+    // ---- O = Qbar S + L E (staged in LDS; stored after the chunk's last barrier)
 #pragma unroll
     for (int r = 0; r < J::RPW; ++r) {
       const int I = J::blk(w, r);
@@ -326,15 +381,13 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
           if (J::kAllTiles || n < NT) mma(accO[r][u], fl[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
         }
       }
-      const unsigned o_off = (16 * I + 4 * lq) * v_row + hv * a.d_v + c0 + lr;
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) {
         const int n = J::tile(w, u);
         if (!J::kAllTiles && n >= NT) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (!kTail || row_ok(c, 16 * I + 4 * lq + e)) st(at(o_c, o_off + e * v_row + 16 * n), accO[r][u][e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          st(reinterpret_cast<TOut *>(ost + (16 * I + 4 * lq + e) * OS::PITCH) + 16 * n + lr, accO[r][u][e]);
       }
     }
     load_l(c1);
@@ -365,8 +418,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       }
     }
     load_s(c1);
+    put_v();                                    // v_{c+1}: the Y phase above was the last reader of v_c
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
+    store_o(c, tail_tag);                       // the next O phase rewrites the staging after two barriers
   };
   // The first chunk is peeled so the loop is entered from an iteration with
   // the same memory-instruction order as its own back edge: the compiler's
