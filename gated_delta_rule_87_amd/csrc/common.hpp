@@ -99,6 +99,11 @@ template <int N>
 __device__ __forceinline__ float dpp_row_shr(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + N, 0xf, 0xf, true));
 }
+// Lane N of each DPP row (16 lanes) broadcast to the whole row.
+template <int N>
+__device__ __forceinline__ float dpp_row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf, false));
+}
 // Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16 r .. 16 r + 15).
 __device__ __forceinline__ float row_prefix16(float v) {
   v += dpp_row_shr<1>(v);

@@ -48,7 +48,18 @@ namespace gdr {
 constexpr int kScanWaves = 8;
 constexpr int kXcds = 8;   // accelerator complex dies of the MI355X, each with its own L2
 
-template <int C, int DK, int BV>
+// The chunk operands diag(beta) A_c and L_c are lower triangular: of their
+// 16 x 32 operand blocks (I, s) (row block I, contraction step s) only those
+// with s <= I / 2 are nonzero.  Their number, and the position of block
+// (I, s) among them in row-major order.
+__host__ __device__ constexpr int tri_blocks(int nb) { return (nb / 2) * (nb / 2 + 1); }
+__device__ __forceinline__ int tri_index(int I, int s) {
+  const int m = I >> 1;
+  return ((I & 1) ? (m + 1) * (m + 1) : m * (m + 1)) + s;
+}
+
+// FB: bytes of one 16 x 32 operand block in the workspace (fp16 1 KiB, fp32 2 KiB).
+template <int C, int DK, int BV, int FB>
 struct ScanLayout {
   static constexpr int S_LD = DK + 8;   // S^T rows (elements), 16-byte pad per bf16 plane
   static constexpr int Y_LD = C + 8;    // Y^T, E^T rows
@@ -61,7 +72,10 @@ struct ScanLayout {
   // Row-major staging of one chunk's v tile and o tile (C x BV elements of
   // up to 4 bytes, rows padded by 16 bytes).
   static constexpr size_t st_bytes = (size_t)C * (4 * BV + 16);
-  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes + 2 * st_bytes;
+  // nonzero blocks of diag(beta) A_c, then of L_c, each followed by one zero block
+  static constexpr int NZ = tri_blocks(C / 16);
+  static constexpr size_t al_bytes = 2 * (size_t)(NZ + 1) * FB;
+  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes + 2 * st_bytes + al_bytes;
 };
 
 // One thread's share when all 64 * kScanWaves threads move a row-major C x BV
@@ -110,7 +124,8 @@ __device__ __forceinline__ T *at(T *base, unsigned off) {
 
 template <typename TIn, typename TOut, class P, int C, int DK, int BV>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
-  using Lay = ScanLayout<C, DK, BV>;
+  constexpr int FB = P::kF32 ? 2048 : 1024;
+  using Lay = ScanLayout<C, DK, BV, FB>;
   using IO = TileIO<P>;
   using Plain = typename P::Plain;
   constexpr int NB = C / 16;                  // token row blocks
@@ -159,7 +174,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   using OS = RowSegs<C, BV, (int)sizeof(TOut)>;
   unsigned char *vst = smem_raw + Lay::s_bytes + 2 * Lay::y_bytes + Lay::x_bytes;   // v_c, row-major
   unsigned char *ost = vst + Lay::st_bytes;                                           // o_c, row-major
+  unsigned char *alA = ost + Lay::st_bytes;                                           // diag(beta) A_c blocks
+  unsigned char *alL = alA + (Lay::NZ + 1) * FB;                                      // L_c blocks
   const int tid = threadIdx.x;
+  // LDS block of (I, s): its compacted position, or the zero block
+  auto al_slot = [&](int I, int s) { return s <= I / 2 ? tri_index(I, s) : Lay::NZ; };
   const int yh = YS == 1 ? 0 : w / NB;        // this wave's half of the channel steps (YS = 2)
 
   const TIn *vp = reinterpret_cast<const TIn *>(a.v);
@@ -173,11 +192,35 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   // ---------------------------------------------------- prefetch registers
   Plain fkb[J::RPW][YKS];             // Kbar rows of each row block (this wave's channel steps)
   Plain fqb[J::RPW][YKS];             // Qbar rows
-  Plain fa[J::RPW][CSTEPS];           // diag(beta) A_c rows
-  Plain fl[J::RPW][CSTEPS];           // L_c rows
   Plain fkh[SJ::RPW][CSTEPS];         // Khat^T rows (channels) of each S block
-  f32x4 gm[SJ::RPW];                  // exp(Lambda_C) of the block's rows of S
+  float gm[SJ::RPW];                  // exp(Lambda_C) of S row i0 + 4 lq + (lane & 3) of each block
   typename VS::Vec vseg[VS::NREP];    // this thread's pieces of the v tile
+
+  // The nonzero blocks of diag(beta) A_c and L_c, 2 NZ FB bytes, are loaded
+  // by all threads in pieces of AW bytes (piece p at byte AW p of the A
+  // blocks followed by the L blocks) during chunk c-1 and staged in LDS in
+  // the Y phase of chunk c, where no wave reads either.
+  constexpr int AL_BYTES = 2 * Lay::NZ * FB / (64 * kScanWaves);
+  constexpr int AW = AL_BYTES % 16 == 0 ? 16 : 8;
+  constexpr int ANREP = AL_BYTES / AW;
+  static_assert(AL_BYTES % AW == 0 && FB % AW == 0, "operand block pieces");
+  using AVec = typename std::conditional<AW == 8, u32x2, u32x4>::type;
+  AVec alseg[ANREP];
+  unsigned al_src[ANREP], al_dst[ANREP];   // byte offsets in the chunk's A or L tile / in LDS
+  bool al_isl[ANREP];
+#pragma unroll
+  for (int k = 0; k < ANREP; ++k) {
+    const int byte = (k * 64 * kScanWaves + tid) * AW;
+    int j = byte / FB;
+    const int off = byte % FB;
+    al_isl[k] = j >= Lay::NZ;
+    if (al_isl[k]) j -= Lay::NZ;
+    int I = 0;
+#pragma unroll
+    for (int i = 1; i < NB; ++i) I = tri_index(i, 0) <= j ? i : I;
+    al_src[k] = (I * CSTEPS + (j - tri_index(I, 0))) * FB + off;
+    al_dst[k] = (al_isl[k] ? (Lay::NZ + 1) * FB : 0) + j * FB + off;
+  }
 
   auto load_y = [&](int c) __attribute__((always_inline)) {
     const void *tkb = tile(kWsKB, a.H_k, hk, c), *tqb = tile(kWsQB, a.H_k, hk, c);
@@ -221,22 +264,16 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         *reinterpret_cast<typename OS::Vec *>(at(o_c, t * v_row + hv * a.d_v + c0 + OS::colb(tid, k) / (int)sizeof(TOut))) = val;
     }
   };
-  auto load_a = [&](int c) __attribute__((always_inline)) {
-    const void *ta = tile(kWsA, a.H_beta, hb, c);
+  auto load_al = [&](int c) __attribute__((always_inline)) {
+    const unsigned char *ta = static_cast<const unsigned char *>(tile(kWsA, a.H_beta, hb, c));
+    const unsigned char *tl = static_cast<const unsigned char *>(tile(kWsL, a.H_k, hk, c));
 #pragma unroll
-    for (int r = 0; r < J::RPW; ++r) {
-#pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) fa[r][s] = IO::get_plain(ta, J::blk(w, r) * CSTEPS + s, l);
-    }
+    for (int k = 0; k < ANREP; ++k)
+      alseg[k] = *reinterpret_cast<const AVec *>((al_isl[k] ? tl : ta) + al_src[k]);
   };
-  auto load_l = [&](int c) __attribute__((always_inline)) {
-    const void *tl = tile(kWsL, a.H_k, hk, c);
+  auto put_al = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < J::RPW; ++r) {
-#pragma unroll
-      for (int s = 0; s < CSTEPS; ++s)
-        fl[r][s] = IO::get_plain(tl, J::blk(w, r) * CSTEPS + s, l);
-    }
+    for (int k = 0; k < ANREP; ++k) *reinterpret_cast<AVec *>(alA + al_dst[k]) = alseg[k];
   };
   auto load_s = [&](int c) __attribute__((always_inline)) {
     const void *tkh = tile(kWsKH, a.H_k, hk, c);
@@ -246,7 +283,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       const int i0 = 16 * SJ::blk(w, r);
 #pragma unroll
       for (int s = 0; s < CSTEPS; ++s) fkh[r][s] = IO::get_plain(tkh, SJ::blk(w, r) * CSTEPS + s, l);
-      gm[r] = *reinterpret_cast<const f32x4 *>(tgm + i0 + 4 * lq);
+      gm[r] = tgm[i0 + 4 * lq + (lr & 3)];
     }
   };
 
@@ -268,11 +305,15 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       sT.put4(16 * n + lr, i0 + 4 * lq, S[r][u]);
     }
   }
+  // the zero blocks that stand for the blocks above the diagonal
+  for (int i = tid; i < FB / 16; i += 64 * kScanWaves) {
+    reinterpret_cast<u32x4 *>(alA + Lay::NZ * FB)[i] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4 *>(alL + Lay::NZ * FB)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
   if (a.N_c > 0) {
     load_y(0);
     load_v(0);
-    load_a(0);
-    load_l(0);
+    load_al(0);
     load_s(0);
     put_v();
   }
@@ -339,6 +380,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         yT.put4(16 * n + lr, 16 * I + 4 * lq, y);
       }
     }
+    put_al();                                   // A_c, L_c: the last readers of A_{c-1}, L_{c-1} were before the previous barrier
     load_y(c1);
     load_v(c1);
     __syncthreads();
@@ -352,11 +394,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
       for (int u = 0; u < J::TPW; ++u) accE[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) {        // all steps: A_c is zero above its diagonal blocks
+      for (int s = 0; s < CSTEPS; ++s) {        // all steps: blocks above the diagonal read the zero block
+        const Plain fa = IO::get_plain(alA, al_slot(I, s), l);
 #pragma unroll
         for (int u = 0; u < J::TPW; ++u) {
           const int n = J::tile(w, u);
-          if (J::kAllTiles || n < NT) mma(accE[u], fa[r][s], yT.get(16 * n + lr, 32 * s + 8 * lq));
+          if (J::kAllTiles || n < NT) mma(accE[u], fa, yT.get(16 * n + lr, 32 * s + 8 * lq));
         }
       }
 #pragma unroll
@@ -365,7 +408,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         if (J::kAllTiles || n < NT) eT.put4(16 * n + lr, 16 * I + 4 * lq, accE[u]);
       }
     }
-    load_a(c1);
+    load_al(c1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -374,11 +417,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     for (int r = 0; r < J::RPW; ++r) {
       const int I = J::blk(w, r);
 #pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) {        // all steps: L_c is zero above its diagonal blocks
+      for (int s = 0; s < CSTEPS; ++s) {        // all steps: blocks above the diagonal read the zero block
+        const Plain fl = IO::get_plain(alL, al_slot(I, s), l);
 #pragma unroll
         for (int u = 0; u < J::TPW; ++u) {
           const int n = J::tile(w, u);
-          if (J::kAllTiles || n < NT) mma(accO[r][u], fl[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
+          if (J::kAllTiles || n < NT) mma(accO[r][u], fl, eT.get(16 * n + lr, 32 * s + 8 * lq));
         }
       }
 #pragma unroll
@@ -390,18 +434,20 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
           st(reinterpret_cast<TOut *>(ost + (16 * I + 4 * lq + e) * OS::PITCH) + 16 * n + lr, accO[r][u][e]);
       }
     }
-    load_l(c1);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- S = F_c S + Khat^T E
 #pragma unroll
     for (int r = 0; r < SJ::RPW; ++r) {
       const int i0 = 16 * SJ::blk(w, r);
+      // row 4 lq + e of the block: held by lane e of DPP row lq
+      const float g[4] = {dpp_row_bcast<0>(gm[r]), dpp_row_bcast<1>(gm[r]), dpp_row_bcast<2>(gm[r]),
+                          dpp_row_bcast<3>(gm[r])};
 #pragma unroll
       for (int u = 0; u < SJ::TPW; ++u) {
         if (!SJ::kAllTiles && SJ::tile(w, u) >= NT) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[r][u][e] *= gm[r][e];
+        for (int e = 0; e < 4; ++e) S[r][u][e] *= g[e];
       }
 #pragma unroll
       for (int s = 0; s < CSTEPS; ++s) {
@@ -451,9 +497,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   }
 }
 
-static size_t scan_lds_bytes(int C, int d_k, int BV) {
+static size_t scan_lds_bytes(int C, int d_k, int BV, int fb) {
 #define GDR_CASE(c_, dk_, bv_) \
-  if (C == c_ && d_k == dk_ && BV == bv_) return ScanLayout<c_, dk_, bv_>::total;
+  if (C == c_ && d_k == dk_ && BV == bv_) \
+    return fb == 1024 ? ScanLayout<c_, dk_, bv_, 1024>::total : ScanLayout<c_, dk_, bv_, 2048>::total;
   GDR_CASE(64, 64, 16) GDR_CASE(64, 64, 32) GDR_CASE(64, 128, 16) GDR_CASE(64, 128, 32)
   GDR_CASE(64, 256, 16) GDR_CASE(64, 256, 32) GDR_CASE(128, 64, 16) GDR_CASE(128, 64, 32)
   GDR_CASE(128, 128, 16) GDR_CASE(128, 128, 32) GDR_CASE(128, 256, 16) GDR_CASE(128, 256, 32)
@@ -465,11 +512,11 @@ static size_t scan_lds_bytes(int C, int d_k, int BV) {
 // (256 of them), else 16 for more parallelism; 0 if the shape is not
 // supported.
 int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16) {
-  (void)in_bf16;
+  const int fb = in_bf16 ? 1024 : 2048;
   if (!(C == 64 || C == 128) || !(d_k == 64 || d_k == 128 || d_k == 256) || d_v % 16 != 0) return 0;
   const size_t cap = 160 * 1024;
-  const bool fit32 = d_v % 32 == 0 && scan_lds_bytes(C, d_k, 32) <= cap;
-  const bool fit16 = scan_lds_bytes(C, d_k, 16) <= cap;
+  const bool fit32 = d_v % 32 == 0 && scan_lds_bytes(C, d_k, 32, fb) <= cap;
+  const bool fit16 = scan_lds_bytes(C, d_k, 16, fb) <= cap;
   const long n32 = (long)B * H_v * (d_v / 32);
   if (fit32 && (n32 >= 256 || !fit16)) return 32;
   return fit16 ? 16 : 0;
@@ -477,7 +524,7 @@ int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16) {
 
 template <typename TIn, typename TOut, class P, int C, int DK, int BV>
 static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream) {
-  const size_t lds = ScanLayout<C, DK, BV>::total;
+  const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024>::total;
   auto kern = scan_kernel<TIn, TOut, P, C, DK, BV>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
