@@ -194,7 +194,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   Plain fqb[J::RPW][YKS];             // Qbar rows
   Plain fkh[SJ::RPW][CSTEPS];         // Khat^T rows (channels) of each S block
   float gm[SJ::RPW];                  // exp(Lambda_C) of S row i0 + 4 lq + (lane & 3) of each block
-  typename VS::Vec vseg[VS::NREP];    // this thread's pieces of the v tile
+  // this thread's pieces of the v tile: v_{c+1} (staged in LDS during chunk
+  // c) and v_{c+2} (requested during chunk c: v comes from HBM, so it is
+  // fetched a chunk further ahead than the operand tiles, most of which the
+  // other column tiles of the head have already brought into L2)
+  typename VS::Vec vseg[VS::NREP], vnext[VS::NREP];
 
   // The nonzero blocks of diag(beta) A_c and L_c, 2 NZ FB bytes, are loaded
   // by all threads in pieces of AW bytes (piece p at byte AW p of the A
@@ -236,11 +240,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   };
   // v_c: rows clamped to the last token (the tail's extra rows are masked
   // where they are used); staged in LDS by put_v
-  auto load_v = [&](int c) __attribute__((always_inline)) {
+  auto load_v = [&](typename VS::Vec (&dst)[VS::NREP], int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < VS::NREP; ++k) {
       const int t = VS::row(tid, k);
-      vseg[k] = *reinterpret_cast<const typename VS::Vec *>(
+      dst[k] = *reinterpret_cast<const typename VS::Vec *>(
           at(at_chunk(vp, v_row, c), crow(c, t) * v_row + hv * a.d_v + c0 + VS::colb(tid, k) / (int)sizeof(TIn)));
     }
   };
@@ -312,7 +316,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   }
   if (a.N_c > 0) {
     load_y(0);
-    load_v(0);
+    load_v(vseg, 0);
+    load_v(vnext, min(1, a.N_c - 1));
     load_al(0);
     load_s(0);
     put_v();
@@ -382,7 +387,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     }
     put_al();                                   // A_c, L_c: the last readers of A_{c-1}, L_{c-1} were before the previous barrier
     load_y(c1);
-    load_v(c1);
+#pragma unroll
+    for (int k = 0; k < VS::NREP; ++k) vseg[k] = vnext[k];
+    load_v(vnext, min(c + 2, a.N_c - 1));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);          // keep each phase's work (and waits) in its phase
 
