@@ -504,12 +504,14 @@ struct PrepItem {
   }
 
   // L above the diagonal blocks, one fragment (row, 8 columns) per store
+  // The upper half of each 16 x 32 block of L_c that straddles the diagonal;
+  // blocks wholly above it (2 kb > rb) are never read and not written.
   __device__ __forceinline__ void zero_upper_L() const {
     const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int u = tid; u < (C / 16) * (C / 32) * 64; u += blockDim.x) {
       const int blk = u >> 6, f = u & 63;
       const int rb = blk / (C / 32), kb = blk % (C / 32);
-      if (2 * kb + (f >> 5) > rb) IO::put_plain8(tL, blk, f, z);   // column block 2 kb + (f >> 4) / 2
+      if (2 * kb + (f >> 5) > rb && 2 * kb <= rb) IO::put_plain8(tL, blk, f, z);   // column block 2 kb + (f >> 5)
     }
   }
 
@@ -555,10 +557,11 @@ struct PrepItem {
       void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
       for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
         const int blk = u >> 6, f = u & 63;
+        if (2 * (blk % (C / 32)) > blk / (C / 32)) continue;   // block wholly above the diagonal: not written
         const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
         const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
         const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
-        const bool upper = col / 16 > row / 16;             // above the diagonal blocks: never written
+        const bool upper = col / 16 > row / 16;             // the half of a straddling block above the diagonal
         const float bt = bet[row];
         float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
 #pragma unroll

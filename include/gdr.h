@@ -103,7 +103,10 @@ typedef struct {
  * MFMA operands are read: an R x K tile is (R/16) x (K/32) blocks,
  * row-block-major; a block is 64 fragments of 8 consecutive columns,
  * fragment f = 16 q + r holding row r, columns 8 q .. 8 q + 7 of the block,
- * at byte 16 f (fp16, 1 KiB blocks) or 32 f (fp32, 2 KiB blocks).  Token rows
+ * at byte 16 f (fp16, 1 KiB blocks) or 32 f (fp32, 2 KiB blocks).  A and L
+ * are lower triangular: their blocks wholly above the diagonal (block
+ * (i, j) with 32 j > 16 i + 15) are neither written nor read, and hold
+ * whatever the buffer held.  Token rows
  * (columns of KH) of a short final chunk past T are zero and its gate values
  * are those of its last real token.  Region
  * offsets: gdr_chunk_workspace_layout.

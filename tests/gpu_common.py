@@ -77,9 +77,18 @@ def decode_workspace(ws, p):
         x = x.transpose(0, 1, 4, 2, 3, 5).reshape(n_tiles, R, K)
         return x.reshape((p.B, heads, nc, R, K))
 
+    def lower_blocks(x):
+        # 16 x 32 blocks wholly above the diagonal are not written (include/gdr.h)
+        x = x.copy()
+        for i in range(C // 16):
+            for j in range(C // 32):
+                if 32 * j > 16 * i + 15:
+                    x[..., 16 * i:16 * i + 16, 32 * j:32 * j + 32] = 0.0
+        return x
+
     return {
-        "A": region("A", hb, (C, C)),
-        "L": region("L", p.H_k, (C, C)),
+        "A": lower_blocks(region("A", hb, (C, C))),
+        "L": lower_blocks(region("L", p.H_k, (C, C))),
         "KB": region("KB", p.H_k, (C, dk)),
         "QB": region("QB", p.H_k, (C, dk)),
         "KH": region("KH", p.H_k, (dk, C)),
