@@ -4,6 +4,7 @@ and the fp64 CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--solve exact|neumann]   (defaults 200, 400, 2)
     python bench.py --copy-calibration BYTES      # plain copy, for rocprofv3 --pmc scaling
+    python bench.py --decode [--config 2]         # the recurrent step, one token per sequence
 
 One step is one full forward over the workload's synthetic batch, inputs
 already resident in HBM: the chunk-prep kernel then the scan/output kernel
@@ -130,6 +131,67 @@ def copy_calibration(nbytes, steps):
                       "GBs_read_plus_write": 2 * n * 4 / dt / 1e9}), flush=True)
 
 
+def decode_bench(w, args, q, k, v, beta, la):
+    """Decoding: gdr_recurrent_step on token t of every sequence (t runs over
+    the workload's first 64 tokens), the fp32 state [B, H_v, d_k, d_v]
+    resident and updated in place.  A step is one launch, short enough that
+    the host's call overhead would be what the wall clock measures, so the
+    64 steps are captured once in a HIP graph and the graph is replayed; one
+    replay is checked against the same steps run eagerly.  The step reads and
+    writes the state once; that dominates its HBM traffic."""
+    import torch
+    from gated_delta_rule_87_amd import binding as gb
+
+    n_tok = min(w.T, 64)
+    toks = [tuple(x[:, t:t + 1].contiguous() for x in (q, k, v, beta, la)) for t in range(n_tok)]
+    state = torch.zeros((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, 1, w.H_v, w.d_v), dtype=torch.float32, device="cuda")
+
+    def steps():
+        for tq, tk, tv, tb, tl in toks:
+            gb.gdr_recurrent_step(tq, tk, tv, tb, tl, state, o=o)
+
+    steps()                                     # eager reference from the zero state
+    torch.cuda.synchronize()
+    ref = state.clone()
+    state.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    state.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    replay_diff = float((state - ref).abs().max().item())
+    reps = max(1, args.steps // n_tok)
+    for _ in range(max(1, args.warmup // n_tok)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * n_tok)
+    es = 2 if w.dtype == "bf16" else 4
+    state_bytes = 4 * w.B * w.H_v * w.d_k * w.d_v
+    io_bytes = w.B * (es * (2 * w.H_k * w.d_k + w.H_v * w.d_v + w.H_beta + w.H_k * w.G) + 4 * w.H_v * w.d_v)
+    achieved = (2 * state_bytes + io_bytes) / (ms_step * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "decode tokens/s (recurrent step, one token per sequence), 1 GPU",
+        "value": w.B / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": reps * n_tok,
+        "warmup": max(1, args.warmup // n_tok) * n_tok, "ms_per_step": ms_step, "higher_is_better": True,
+        "dtype": "f32 state, " + w.dtype + " inputs", "data": "synthetic", "timing": "HIP graph of 64 steps",
+        "graph_replay_max_abs_diff_vs_eager": replay_diff,
+        "config": {"workload": w.name + "_decode", "B": w.B, "T": 1, "H_k": w.H_k, "H_v": w.H_v,
+                   "d_k": w.d_k, "d_v": w.d_v, "gate_groups": w.G},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "kernel": "step", "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +205,8 @@ def main():
     ap.add_argument("--solve", default=None, choices=["exact", "neumann"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--decode", action="store_true",
+                    help="time gdr_recurrent_step on one token per sequence (its own metric)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -172,6 +236,9 @@ def main():
         return torch.from_numpy(a).cuda()
 
     q, k, v, beta, la = (dev(raw[n]) for n in ("q", "k", "v", "beta", "log_alpha"))
+    if args.decode:
+        decode_bench(w, args, q, k, v, beta, la)
+        return
     p = gb.make_problem(q, v, la, beta, chunk=w.chunk, solve=solve, neumann_order=w.neumann_order,
                         neumann_residual_steps=w.neumann_residual)
     ws = torch.empty(gb.gdr_chunk_fwd_workspace_size(p) // 4, dtype=torch.float32, device="cuda")
