@@ -324,6 +324,11 @@ template <> struct StateLds<PrecF32> : OperandLds<PrecF32> {};
 // tiles: 2 KiB blocks, fragment f at byte 32 f.
 template <class P> struct TileIO;
 
+// Tiles are written with non-temporal stores.  The scan reads them from HBM
+// right after prep: with ordinary stores, prep leaves the L2 full of dirty
+// workspace lines, and the scan's start competes with their write-back
+// (measured: the scan runs 4 % faster on the per-channel workload and 12 %
+// on the scalar-gate one).
 // fp16 tiles (operands prepared from bf16 inputs): plain only, 1 KiB blocks.
 template <> struct TileIO<PrecF16> {
   __device__ static unsigned char *at(void *t, int blk, int f) {
@@ -333,7 +338,7 @@ template <> struct TileIO<PrecF16> {
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = static_cast<f16>(x[e]);
-    *reinterpret_cast<f16x8 *>(at(t, blk, f)) = h;
+    __builtin_nontemporal_store(h, reinterpret_cast<f16x8 *>(at(t, blk, f)));
   }
   __device__ static FragH get_plain(const void *t, int blk, int f) {
     FragH v;
@@ -348,8 +353,8 @@ template <> struct TileIO<PrecF32> {
   }
   __device__ static void put_plain8(void *t, int blk, int f, const float (&x)[8]) {
     float *p = at(t, blk, f);
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4 *>(p + 4));
   }
   __device__ static FragF get_plain(const void *t, int blk, int f) {
     const float *p = at(const_cast<void *>(t), blk, f);
