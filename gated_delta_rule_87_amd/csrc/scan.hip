@@ -265,7 +265,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       const int t = OS::row(tid, k);
       const auto val = *reinterpret_cast<const typename OS::Vec *>(ost + t * OS::PITCH + OS::colb(tid, k));
       if (!kTail || row_ok(c, t))
-        *reinterpret_cast<typename OS::Vec *>(at(o_c, t * v_row + hv * a.d_v + c0 + OS::colb(tid, k) / (int)sizeof(TOut))) = val;
+        __builtin_nontemporal_store(   // written once, read by no later launch of this pass
+            val, reinterpret_cast<typename OS::Vec *>(at(o_c, t * v_row + hv * a.d_v + c0 + OS::colb(tid, k) / (int)sizeof(TOut))));
     }
   };
   auto load_al = [&](int c) __attribute__((always_inline)) {
