@@ -186,39 +186,44 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
     }
   }
   __syncthreads();
+  // One job per (pair p, column tile tj): a wave forms the column tile of
+  // X_p = M[bot, top] A[top, top] and then the same column of
+  // A[bot, top] = -A[bot, bot] X_p, which needs only that column of X_p, so
+  // the two products meet through the wave's own LDS writes, with no
+  // workgroup barrier between them.
   for (int bs = 16; bs < C; bs *= 2) {
     const int tpb = bs / 16;                  // tiles per block side
     const int XLD = bs + 4;
-    const int jobs = (C / (2 * bs)) * tpb * tpb;
-    // X_p = M[bot, top] * A[top, top] -> tmp (pair p at tmp + p * bs * XLD)
+    const int jobs = (C / (2 * bs)) * tpb;
     for (int job = w; job < jobs; job += blockDim.x / kWave) {
-      const int p = job / (tpb * tpb), ti = (job / tpb) % tpb, tj = job % tpb;
+      const int p = job / tpb, tj = job % tpb;
       const int top = 2 * bs * p, bot = top + bs;
-      const int r0 = bot + 16 * ti, c0 = top + 16 * tj;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      tile_f32<C / 32>(acc,
-               [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
-               [&](int k, int j) { return amat[k * LD + c0 + j]; },
-               c0, top + bs);                 // A[top,top] is lower: rows k >= column
-      float *X = tmp + p * bs * XLD;
+      const int c0 = top + 16 * tj;
+      float *X = tmp + p * bs * XLD;          // pair p's X at tmp + p * bs * XLD
+      for (int ti = 0; ti < tpb; ++ti) {
+        const int r0 = bot + 16 * ti;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_f32<C / 32>(acc,
+                 [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
+                 [&](int k, int j) { return amat[k * LD + c0 + j]; },
+                 c0, top + bs);               // A[top,top] is lower: rows k >= column
 #pragma unroll
-      for (int r = 0; r < 4; ++r) X[(16 * ti + 4 * (l >> 4) + r) * XLD + 16 * tj + (l & 15)] = acc[r];
-    }
-    __syncthreads();
-    // A[bot, top] = -A[bot, bot] * X_p
-    for (int job = w; job < jobs; job += blockDim.x / kWave) {
-      const int p = job / (tpb * tpb), ti = (job / tpb) % tpb, tj = job % tpb;
-      const int top = 2 * bs * p, bot = top + bs;
-      const int r0 = bot + 16 * ti;
-      const float *X = tmp + p * bs * XLD;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      tile_f32<C / 32>(acc,
-               [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
-               [&](int k, int j) { return X[(k - bot) * XLD + 16 * tj + j]; },
-               bot, r0 + 16);                 // A[bot,bot] is lower: columns k <= row
+        for (int r = 0; r < 4; ++r) X[(16 * ti + 4 * (l >> 4) + r) * XLD + 16 * tj + (l & 15)] = acc[r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // this wave's X column before its reads
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int ti = 0; ti < tpb; ++ti) {
+        const int r0 = bot + 16 * ti;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_f32<C / 32>(acc,
+                 [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
+                 [&](int k, int j) { return X[(k - bot) * XLD + 16 * tj + j]; },
+                 bot, r0 + 16);               // A[bot,bot] is lower: columns k <= row
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        amat[(r0 + 4 * (l >> 4) + r) * LD + top + 16 * tj + (l & 15)] = -acc[r];
+        for (int r = 0; r < 4; ++r)
+          amat[(r0 + 4 * (l >> 4) + r) * LD + top + 16 * tj + (l & 15)] = -acc[r];
+      }
     }
     __syncthreads();
   }
