@@ -231,10 +231,16 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
 
 // ----------------------------------------------------------- Neumann solve
 // X = sum_{s=0}^{m} (-M)^s by Horner (X <- I - M X, m times), then r residual
-// corrections X <- X + X (I - (I + M) X).  Both products are evaluated one
-// 16-column block of the result at a time, so X is updated in place: a column
-// block of M X needs only the same column block of X, and X Rm[:, J] needs the
-// columns of X at and right of J, which are still the old ones.
+// corrections X <- X + X (I - (I + M) X).  Horner steps update X in place by
+// 16-column blocks, one wave per block: tile (I, J) of M X contracts over
+// k in [16 J, 16 I + 16) (X is lower triangular), that is over the tiles of
+// column block J at and above row block I, so a wave that goes up its column
+// from the bottom overwrites only tiles nothing later in the column reads.
+// One barrier per step.  The residual products go one 16-column block of
+// the result at a time, X updated in place: (I + M) X[:, J] needs only
+// column block J of X, and X Rm[:, J] needs the columns of X at and right of
+// J, which are still the old ones.
+constexpr int kPrepWaves = 4;                 // the prep kernels run 256 threads
 template <int C>
 __device__ __forceinline__ void solve_neumann(const float *gmat, const float *bet, float *amat, float *tmp, int order,
                               int residual) {
@@ -247,27 +253,25 @@ __device__ __forceinline__ void solve_neumann(const float *gmat, const float *be
   for (int i = tid; i < C * LD; i += blockDim.x) amat[i] = ((i / LD) == (i % LD)) ? 1.f : 0.f;
   __syncthreads();
   auto Mx = [&](int i, int k, int r0) { return gmat[(r0 + i) * LD + k] * bet[k]; };
+  // column blocks J and NB - 1 - J share a wave: long and short columns paired
+  auto owner = [](int J) { return (J < NB / 2 ? J : NB - 1 - J) % kPrepWaves; };
   for (int it = 0; it < order; ++it) {
+#pragma unroll 1
     for (int J = 0; J < NB; ++J) {
-      f32x4 acc[kMaxTiles];
-      int nt = 0;
-      for (int I = J + w; I < NB; I += nw, ++nt) {
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r0 = 16 * I;
-        tile_f32<C / 16>(acc[nt], [&](int i, int k) { return Mx(i, k, r0); },
-                 [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, r0 + 16);
-      }
-      __syncthreads();
-      nt = 0;
-      for (int I = J + w; I < NB; I += nw, ++nt) {
+      if (owner(J) != w) continue;
+#pragma unroll 1
+      for (int I = NB - 1; I >= J; --I) {       // one tile's operands live at a time
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_f32<C / 16>(acc, [&](int i, int k) { return Mx(i, k, 16 * I); },
+                 [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, 16 * I + 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          amat[row * LD + col] = ((row == col) ? 1.f : 0.f) - acc[nt][r];
+          amat[row * LD + col] = ((row == col) ? 1.f : 0.f) - acc[r];
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
   }
   for (int it = 0; it < residual; ++it) {
     for (int J = 0; J < NB; ++J) {
