@@ -47,6 +47,12 @@ SMALL = {
     # one token; one ragged chunk with 8 groups of 8 channels
     "t1_bf16": Workload("t1_bf16", 2, 1, 2, 2, 128, 64, 64, 128, "bf16", seed=11),
     "t63_f32_g8": Workload("t63_f32_g8", 1, 63, 2, 2, 64, 32, 64, 8, "f32", seed=12),
+    # enough (batch, value head, 32-column) tiles for 32-column scan
+    # workgroups (B H_v d_v / 32 >= 256): C = 128 with bf16 inputs, and fp32
+    # inputs at C = 64
+    "c128_bv32_bf16": Workload("c128_bv32_bf16", 1, 260, 64, 64, 128, 128, 128, 128, "bf16", alpha_mu=2.0,
+                               seed=15),
+    "f32_bv32": Workload("f32_bv32", 2, 150, 64, 64, 64, 64, 64, 1, "f32", seed=16),
 }
 
 # the cases above with chunks on both sides of the chunk-pivot range limit
