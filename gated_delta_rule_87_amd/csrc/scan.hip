@@ -30,11 +30,14 @@
 // Organisation.  Eight waves, two per SIMD, so one wave's memory and LDS
 // latency hides behind the other's arithmetic.  Jobs per chunk: Y, E and O
 // over (16-token row block, 16-column tile), S over (16-channel block,
-// tile); a wave that owns several tiles of one block loads the block's A
-// fragments once.  The state and the intermediate Y and E live in LDS as
-// split B operands between phases.  Every operand tile of chunk c+1 is
-// requested while chunk c computes: each prefetch register set is refilled
-// right after its last use, and all loads of a non-final chunk are
+// tile).  The state and the intermediate Y and E live in LDS as B operands
+// between phases.  The step is bound by the bytes each CU moves through its
+// vector memory path, so every tile is fetched once per workgroup, in wide
+// pieces: each wave loads only its own K̄, Q̄ and K̂ᵀ rows into registers;
+// the nonzero blocks of diag(beta) A_c and L_c, v_c and o_c move through
+// LDS as whole-row pieces shared by all threads.  Every operand of chunk
+// c+1 (v: c+2) is requested while chunk c computes, right after the last
+// use of the registers it goes to, and all loads of a non-final chunk are
 // unconditional (indices clamped to the last chunk) so the compiler's
 // memory-wait counts stay exact across iterations; the final, possibly
 // ragged chunk is peeled.
