@@ -33,9 +33,9 @@
 // tile).  The state and the intermediate Y and E live in LDS as B operands
 // between phases.  The step is bound by the bytes each CU moves through its
 // vector memory path, so every tile is fetched once per workgroup, in wide
-// pieces: each wave loads only its own K̄, Q̄ and K̂ᵀ rows into registers;
-// the nonzero blocks of diag(beta) A_c and L_c, v_c and o_c move through
-// LDS as whole-row pieces shared by all threads.  Every operand of chunk
+// pieces: each wave loads only its own Kbar, Qbar and Khat^T rows into
+// registers; the nonzero blocks of diag(beta) A_c and L_c, v_c and o_c move
+// through LDS as whole-row pieces shared by all threads.  Every operand of chunk
 // c+1 (v: c+2) is requested while chunk c computes, right after the last
 // use of the registers it goes to, and all loads of a non-final chunk are
 // unconditional (indices clamped to the last chunk) so the compiler's
