@@ -263,6 +263,12 @@ template <> struct OperandLds<PrecF16> {
     f.l = *reinterpret_cast<const f16x8 *>(lo + n * ld + k);
     return f;
   }
+  // the hi plane only: the operand rounded once to fp16
+  __device__ __forceinline__ FragH get_hi(int n, int k) const {
+    FragH f;
+    f.h = *reinterpret_cast<const f16x8 *>(hi + n * ld + k);
+    return f;
+  }
 };
 
 template <> struct OperandLds<PrecF32> {
@@ -277,6 +283,7 @@ template <> struct OperandLds<PrecF32> {
   __device__ __forceinline__ void put4(int n, int k, const f32x4 &x) {
     *reinterpret_cast<f32x4 *>(v + n * ld + k) = x;
   }
+  __device__ __forceinline__ FragF get_hi(int n, int k) const { return get(n, k); }   // fp32: the operand itself
   __device__ __forceinline__ FragF get(int n, int k) const {
     FragF f;
     const float4 a = *reinterpret_cast<const float4 *>(v + n * ld + k);

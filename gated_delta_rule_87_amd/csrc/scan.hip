@@ -19,13 +19,15 @@
 // Operand precision (bf16 inputs): the prepared operands diag(beta) A_c, L_c,
 // Kbar, Qbar and Khat are single fp16 (11 significant bits), and so is the
 // per-chunk operand copy of the state S (S itself accumulates in fp32
-// registers); the intermediates Y and E are split fp16 pairs (x = hi + lo,
-// hi = fp16(x)), so their products are two fp16 MFMAs with fp32
-// accumulation.  bf16 (8 bits) is too coarse for Qbar, Khat, L, S, Y and E:
-// rounding any one of them to bf16 breaks a 1e-2 max-error bar on the
-// per-channel-gate workload.  Rounding the S operand to single fp16 leaves
-// the error where the split pair had it; rounding Y or E as well would add
-// about a quarter each.
+// registers); the intermediates Y and E are kept in LDS as split fp16 pairs
+// (x = hi + lo, hi = fp16(x)).  E = diag(beta) A Y and the readout L E use
+// both halves (two fp16 MFMAs, fp32 accumulation); the state update
+// Khat^T E uses hi alone.  bf16 (8 bits) is too coarse for Qbar, Khat, L,
+// S, Y and E: rounding any one of them to bf16 breaks a 1e-2 max-error bar
+// on the per-channel-gate workload.  Measured at full size: the single fp16
+// E in the state update leaves the error of o where it was and doubles that
+// of the final state (at most 4.3e-3, C = 128 stress workload); single fp16
+// Y and E everywhere would raise the error of o to 9e-3 there.
 //
 // Organisation.  Eight waves, two per SIMD, so one wave's memory and LDS
 // latency hides behind the other's arithmetic.  Jobs per chunk: Y, E and O
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int u = 0; u < SJ::TPW; ++u) {
           const int n = SJ::tile(w, u);
-          if (SJ::kAllTiles || n < NT) mma(S[r][u], fkh[r][s], eT.get(16 * n + lr, 32 * s + 8 * lq));
+          if (SJ::kAllTiles || n < NT) mma(S[r][u], fkh[r][s], eT.get_hi(16 * n + lr, 32 * s + 8 * lq));
         }
       }
 #pragma unroll
