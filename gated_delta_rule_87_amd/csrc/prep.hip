@@ -512,9 +512,9 @@ struct PrepItem {
     }
   }
 
-  // L above the diagonal blocks, one fragment (row, 8 columns) per store
-  // The upper half of each 16 x 32 block of L_c that straddles the diagonal;
-  // blocks wholly above it (2 kb > rb) are never read and not written.
+  // Zeros in the upper half of each 16 x 32 block of L_c that straddles the
+  // diagonal, one fragment (row, 8 columns) per store; blocks wholly above
+  // it (2 kb > rb) are never read and not written.
   __device__ __forceinline__ void zero_upper_L() const {
     const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int u = tid; u < (C / 16) * (C / 32) * 64; u += blockDim.x) {
@@ -544,9 +544,10 @@ struct PrepItem {
   }
 
   // Per beta head: A = (I + G diag(beta))^{-1} from gsolve into asolve (row
-  // stride C + 4 both), then diag(beta) A to the workspace, the blocks above
-  // the diagonal as zeros.  bet0_ready: the first head's beta is already in
-  // LDS (written before a barrier that precedes the call).
+  // stride C + 4 both), then diag(beta) A to the workspace: the upper half of
+  // a 16 x 32 block that straddles the diagonal as zeros, blocks wholly above
+  // it not at all.  bet0_ready: the first head's beta is already in LDS
+  // (written before a barrier that precedes the call).
   __device__ __forceinline__ void solve_store(float *gsolve, float *asolve, const TIn (&bets)[NBET],
                                               bool bet0_ready) const {
     for (int rb = 0; rb < Rb; ++rb) {
