@@ -55,6 +55,10 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
                        (double)(p->d_k > p->d_v ? p->d_k : p->d_v);
   if (elems > 9.0e15 || (double)p->B * p->T > 2147483647.0)
     return fail(GDR_ERR_INVALID_ARG, "problem too large (B*T=%lld)", (long long)p->B * p->T);
+  // Launch geometry: the batch and head indices are grid dimensions z and y
+  // (at most 65535 each), and no grid dimension may count 2^32 work items.
+  if (p->B > 65535 || p->H_v > 65535)
+    return fail(GDR_ERR_UNSUPPORTED, "B=%d H_v=%d: at most 65535 each", p->B, p->H_v);
   if (!(p->d_k == 64 || p->d_k == 128 || p->d_k == 256))
     return fail(GDR_ERR_UNSUPPORTED, "d_k=%d: this build supports d_k in {64, 128, 256}", p->d_k);
   if (p->d_v % 16 != 0) return fail(GDR_ERR_UNSUPPORTED, "d_v=%d: must be a multiple of 16", p->d_v);
@@ -72,6 +76,12 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
     }
     if (!(p->chunk == 64 || p->chunk == 128))
       return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: this build supports chunk in {64, 128}", p->chunk);
+    // prep: one 256-thread workgroup per chunk along x; scan: one 512-thread
+    // workgroup per (batch, value head, tile of at least 16 value columns)
+    const long long n_c = ((long long)p->T + p->chunk - 1) / p->chunk;
+    const long long scan_units = (long long)p->B * p->H_v * (p->d_v / 16);
+    if (n_c * 256 >= (1LL << 32) || scan_units * 512 >= (1LL << 32))
+      return fail(GDR_ERR_UNSUPPORTED, "T=%d chunks or B*H_v*d_v/16=%lld tiles exceed a launch", p->T, scan_units);
     const int beta_heads_per_key = p->beta_per_key_head ? 1 : p->H_v / p->H_k;
     if (p->chunk * beta_heads_per_key > 1024)
       return fail(GDR_ERR_UNSUPPORTED, "chunk * (H_v / H_k) = %d: at most 1024 beta values per chunk",

@@ -132,7 +132,9 @@ gdr_status gdr_chunk_workspace_layout(const gdr_problem *p, size_t *offsets);
  *               bytes, 256-byte aligned; its contents on return are the
  *               per-chunk quantities documented there.
  * Supported here: in_dtype bf16 or f32, chunk 64 or 128, d_k in {64,128,256},
- * d_v a multiple of 16, G a divisor of d_k; beyond that GDR_ERR_UNSUPPORTED.
+ * d_v a multiple of 16, G a divisor of d_k, B and H_v at most 65535, fewer
+ * than 2^24 chunks per sequence and B H_v d_v / 16 below 2^23; beyond that
+ * GDR_ERR_UNSUPPORTED.
  */
 gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v,
                          const void *beta, const void *log_alpha, const float *h0, void *o,
@@ -166,7 +168,8 @@ gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, 
  * Token recurrence, p->T tokens in order (Systolic Linear Attention, section
  * 2.1, Eq. (2)), updating `state` in place (fp32 [B,H_v,d_k,d_v], read and
  * written) and writing o [B,T,H_v,d_v].  chunk / solve fields are ignored.
- * Supported here: d_k in {64,128,256}, d_v a multiple of 16.
+ * Supported here: d_k in {64,128,256}, d_v a multiple of 16, B and H_v at
+ * most 65535.
  */
 gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k, const void *v,
                               const void *beta, const void *log_alpha, float *state, void *o,

@@ -120,6 +120,10 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, la=FAKE, h0=None, o=FAKE, hT=
     (dict(chunk=32), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=128, d_k=256, gate_groups=256), gb.GDR_ERR_UNSUPPORTED),
     (dict(B=1 << 20, T=1 << 20), gb.GDR_ERR_INVALID_ARG),
+    (dict(B=70000), gb.GDR_ERR_UNSUPPORTED),
+    (dict(H_k=70000, H_v=70000), gb.GDR_ERR_UNSUPPORTED),
+    (dict(B=1, T=(1 << 30) + 1), gb.GDR_ERR_UNSUPPORTED),
+    (dict(B=128, H_k=4096, H_v=4096, d_v=256), gb.GDR_ERR_UNSUPPORTED),
 ])
 def test_invalid_problems(kw, status):
     assert call_fwd(problem(**kw)) == status
