@@ -38,11 +38,13 @@
 // pieces: each wave loads only its own Kbar, Qbar and Khat^T rows into
 // registers; the nonzero blocks of diag(beta) A_c and L_c, v_c and o_c move
 // through LDS as whole-row pieces shared by all threads.  Every operand of chunk
-// c+1 (v: c+2) is requested while chunk c computes, right after the last
-// use of the registers it goes to, and all loads of a non-final chunk are
-// unconditional (indices clamped to the last chunk) so the compiler's
-// memory-wait counts stay exact across iterations; the final, possibly
-// ragged chunk is peeled.
+// c+1 (v: c+2) is requested while chunk c computes: Kbar, Qbar and Khat^T
+// right after the last use of the registers they go to (they need most of a
+// chunk to arrive), the A and L blocks at the end of the E phase, one phase
+// after their registers free up (requested together with Kbar and Qbar they
+// slow the chunk down).  All loads of a non-final chunk are unconditional
+// (indices clamped to the last chunk) so the compiler's memory-wait counts
+// stay exact across iterations; the final, possibly ragged chunk is peeled.
 #include <type_traits>
 
 #include "common.hpp"
