@@ -60,7 +60,7 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
   if (p->B > 65535 || p->H_v > 65535)
     return fail(GDR_ERR_UNSUPPORTED, "B=%d H_v=%d: at most 65535 each", p->B, p->H_v);
   if (!(p->d_k == 64 || p->d_k == 128 || p->d_k == 256))
-    return fail(GDR_ERR_UNSUPPORTED, "d_k=%d: this build supports d_k in {64, 128, 256}", p->d_k);
+    return fail(GDR_ERR_UNSUPPORTED, "d_k=%d: libgdr supports d_k in {64, 128, 256}", p->d_k);
   if (p->d_v % 16 != 0) return fail(GDR_ERR_UNSUPPORTED, "d_v=%d: must be a multiple of 16", p->d_v);
   if (chunked) {
     if (p->chunk <= 0) return fail(GDR_ERR_INVALID_ARG, "chunk=%d must be > 0", p->chunk);
@@ -75,7 +75,7 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
                     p->neumann_residual_steps);
     }
     if (!(p->chunk == 64 || p->chunk == 128))
-      return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: this build supports chunk in {64, 128}", p->chunk);
+      return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: libgdr supports chunk in {64, 128}", p->chunk);
     // prep: one 256-thread workgroup per chunk along x; scan: one 512-thread
     // workgroup per (batch, value head, tile of at least 16 value columns)
     const long long n_c = ((long long)p->T + p->chunk - 1) / p->chunk;

@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   GDR_OK = 0,
   GDR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent heads */
-  GDR_ERR_UNSUPPORTED = 2, /* valid problem outside the shapes this build compiles */
+  GDR_ERR_UNSUPPORTED = 2, /* valid problem outside the shapes the library is compiled for */
   GDR_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the queried size  */
   GDR_ERR_HIP = 4          /* a HIP launch failed; gdr_last_error() has the text  */
 } gdr_status;
