@@ -74,9 +74,35 @@ def load_traffic(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, o_gpu, target_s=10.0):
+def host_cpu():
+    """The host's logical CPUs, physical cores and CPU model (from /proc/cpuinfo)."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return {"logical_cpus": os.cpu_count(), "physical_cores": len(cores) or None, "model": model}
+
+
+def cpu_baseline(w, x, o_gpu, target_s=10.0, target_1t_s=3.0):
     """The fp64 oracle on a bounded sample of (batch, value head) units over the
-    full sequence, on this host's cores; also the GPU's error on that sample."""
+    full sequence, on this host's cores (at most 16 threads, the CPU share of
+    one GPU), and on one thread; also the GPU's error on the sample."""
     import numpy as np
     from oracle.recurrence import recurrence_c   # test infrastructure: baseline leg only
 
@@ -98,6 +124,12 @@ def cpu_baseline(w, x, o_gpu, target_s=10.0):
                             beta_per_key_head=w.beta_per_key_head, units=units, nthreads=threads)
     dt = time.perf_counter() - t
     tokens_equiv = n_units * w.T / w.H_v          # whole-job tokens (all heads) the sample is worth
+    # one thread, on the first units of the same sample
+    n1 = max(1, min(len(units), int(target_1t_s / max(per_token_head * w.T, 1e-9))))
+    t = time.perf_counter()
+    recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], beta_per_key_head=w.beta_per_key_head,
+                 units=units[:n1], nthreads=1)
+    dt1 = time.perf_counter() - t
     err = None
     if o_gpu is not None:
         num, den = 0.0, 0.0
@@ -107,10 +139,15 @@ def cpu_baseline(w, x, o_gpu, target_s=10.0):
             num = max(num, float(np.max(np.abs(o_gpu[b, :, h] - ref))))
             den += float(np.sum(ref ** 2))
         err = num / (den / (n_units * w.T * w.d_v)) ** 0.5
+    host = host_cpu()
     return {
         "value": tokens_equiv / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": f"{n_units} of {units_all} (batch, value head) units x all {w.T} tokens, "
-                  f"fp64 token recurrence in C, {dt:.1f} s",
+                  f"fp64 token recurrence in C on {threads} threads, {dt:.2f} s; one thread: {n1} units, "
+                  f"{dt1:.2f} s",
+        "value_1thread": n1 * w.T / w.H_v / dt1,
+        "host_logical_cpus": host["logical_cpus"], "host_physical_cores": host["physical_cores"],
+        "cpu_model": host["model"],
     }, err
 
 
@@ -195,12 +232,13 @@ def decode_bench(w, args, q, k, v, beta, la):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU needs roughly 0.1-0.3 s of sustained work before its clocks
-    # settle (timings of the first few hundred steps drift down by 10-15 %):
-    # the default warm-up covers that, and the timed steps stay well under a
-    # second.
+    # The GPU needs a few tenths of a second of sustained work before its
+    # clocks settle (timings of the first few hundred steps drift down by
+    # 10-25 %): warm-up runs at least --warmup steps and at least
+    # --warmup-seconds of work, whichever is longer.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--warmup-seconds", type=float, default=0.6)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: per-channel-gate KDA)")
     ap.add_argument("--solve", default=None, choices=["exact", "neumann"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -257,9 +295,14 @@ def main():
         if evs:
             evs[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(10):
+            step()
+        n_warm += 10
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -295,6 +338,7 @@ def main():
         "metric": METRIC, "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "warmup_steps_run": n_warm, "warmup_s": round(warm_s, 3),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H_k": w.H_k, "H_v": w.H_v, "d_k": w.d_k,
                    "d_v": w.d_v, "chunk": w.chunk, "gate_groups": w.G, "solve": solve,
                    "in_dtype": w.dtype, "out_dtype": "f32", "parallelism": "single-gpu"},

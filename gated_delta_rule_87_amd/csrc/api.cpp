@@ -6,7 +6,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 
 #include "gdr.h"
 #include "kernels.hpp"
@@ -82,6 +85,12 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
     const long long scan_units = (long long)p->B * p->H_v * (p->d_v / 16);
     if (n_c * 256 >= (1LL << 32) || scan_units * 512 >= (1LL << 32))
       return fail(GDR_ERR_UNSUPPORTED, "T=%d chunks or B*H_v*d_v/16=%lld tiles exceed a launch", p->T, scan_units);
+    // The scan addresses the rows of v and o within one chunk with 32-bit
+    // byte offsets from the chunk's first row: C rows of H_v * d_v elements
+    // of at most 4 bytes must stay below 4 GiB.
+    if ((long long)p->chunk * p->H_v * p->d_v * 4 >= (1LL << 32))
+      return fail(GDR_ERR_UNSUPPORTED, "chunk * H_v * d_v = %lld: one chunk of v or o must stay below 2^30 elements",
+                  (long long)p->chunk * p->H_v * p->d_v);
     const int beta_heads_per_key = p->beta_per_key_head ? 1 : p->H_v / p->H_k;
     if (p->chunk * beta_heads_per_key > 1024)
       return fail(GDR_ERR_UNSUPPORTED, "chunk * (H_v / H_k) = %d: at most 1024 beta values per chunk",
@@ -139,6 +148,23 @@ gdr_status launched(hipError_t e, const char *what) {
 }
 
 }  // namespace
+
+namespace gdr {
+
+hipError_t allow_full_lds(const void *kernel) {
+  static std::mutex mu;
+  static std::set<std::pair<const void *, int>> done;   // (kernel, device) pairs already raised
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
+
+}  // namespace gdr
 
 extern "C" {
 

@@ -76,6 +76,10 @@ hipError_t launch_prep(const ChunkArgs &a, bool in_bf16, hipStream_t stream);
 hipError_t launch_scan(const ChunkArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 
+// Raise a kernel's dynamic LDS limit to the CU's 160 KiB, once per kernel and
+// device (each launch then passes its own size); later calls return at once.
+hipError_t allow_full_lds(const void *kernel);
+
 // Whether a shape is compiled in (the API layer reports GDR_ERR_UNSUPPORTED otherwise).
 bool prep_supported(int C, int d_k, int G);
 int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16);

@@ -968,9 +968,8 @@ bool prep_supported(int C, int d_k, int G) {
 }
 
 template <class K>
-static hipError_t set_lds(K kern, size_t lds) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)lds);
+static hipError_t set_lds(K kern, size_t /*lds*/) {
+  return allow_full_lds(reinterpret_cast<const void *>(kern));
 }
 
 template <typename TIn, class P, int C, int DK>

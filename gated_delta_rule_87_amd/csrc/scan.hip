@@ -541,8 +541,7 @@ template <typename TIn, typename TOut, class P, int C, int DK, int BV>
 static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream) {
   const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024>::total;
   auto kern = scan_kernel<TIn, TOut, P, C, DK, BV>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
   if (e != hipSuccess) return e;
   dim3 grid((a.d_v / BV) * a.H_v * a.B);
   hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), lds, stream, a);

@@ -11,7 +11,9 @@ C order, drawn in this order):
 1. q_raw [B, T, H_k, d_k] ~ N(0, 1), then L2-normalised over d_k (fp64, no eps);
 2. k_raw likewise;
 3. v [B, T, H_v, d_v] ~ N(0, 1);
-4. beta logits [B, T, H_beta] ~ N(0, 1), beta = sigmoid(logit);
+4. beta logits [B, T, H_beta] ~ N(0, 1), beta = s_beta * sigmoid(logit)
+   (s_beta = 1 for the Gated DeltaNet / KDA gate; 2 for the Systolic Linear
+   Attention write gate, section 2.3 and Table 2: beta in (0, 2));
 5. decay logits [B, T, H_k, G] ~ N(mu, sigma) (sigma a standard deviation),
    log_alpha = logsigmoid(logit) = -log1p(exp(-logit)).
 
@@ -46,6 +48,7 @@ class Workload:
     alpha_mu: float = 3.0
     alpha_sigma: float = 1.0
     beta_per_key_head: bool = False
+    beta_scale: float = 1.0   # s_beta: beta = s_beta * sigmoid(logit)
     solves: tuple = ("exact",)
     neumann_order: int = 4
     neumann_residual: int = 1
@@ -119,7 +122,7 @@ def make_inputs(w: Workload, seed=None, T=None, B=None):
     v = rng.standard_normal((B, T, w.H_v, w.d_v))
     beta_logit = rng.standard_normal((B, T, w.H_beta))
     alpha_logit = rng.normal(w.alpha_mu, w.alpha_sigma, (B, T, w.H_k, w.G))
-    beta = 1.0 / (1.0 + np.exp(-beta_logit))
+    beta = w.beta_scale / (1.0 + np.exp(-beta_logit))
     log_alpha = -np.log1p(np.exp(-alpha_logit))
     return {
         "q": encode(q, w.dtype),

@@ -30,7 +30,8 @@
  * - All tensor pointers are DEVICE pointers (HBM), row-major, contiguous, and
  *   16-byte aligned.  The caller allocates and frees every buffer; the
  *   library never allocates device memory, never synchronises the stream and
- *   keeps no global state other than a thread-local error message.
+ *   keeps no global state other than a thread-local error message and a
+ *   record of the kernels whose LDS limit it has raised on each device.
  * - Layouts:   q, k       [B, T, H_k, d_k]          in_dtype
  *              v          [B, T, H_v, d_v]          in_dtype
  *              beta       [B, T, H_v]  ([B, T, H_k] if beta_per_key_head)  in_dtype
@@ -133,7 +134,8 @@ gdr_status gdr_chunk_workspace_layout(const gdr_problem *p, size_t *offsets);
  *               per-chunk quantities documented there.
  * Supported here: in_dtype bf16 or f32, chunk 64 or 128, d_k in {64,128,256},
  * d_v a multiple of 16, G a divisor of d_k, B and H_v at most 65535, fewer
- * than 2^24 chunks per sequence and B H_v d_v / 16 below 2^23; beyond that
+ * than 2^24 chunks per sequence, B H_v d_v / 16 below 2^23 and
+ * chunk H_v d_v below 2^30 (one chunk of v or o within 4 GiB); beyond that
  * GDR_ERR_UNSUPPORTED.
  */
 gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v,

@@ -16,12 +16,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU test")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests need a visible device; on a CPU-only machine they are skipped
-    # rather than failed, but only when the run did not select them explicitly.
-    pass
-
-
 @pytest.fixture(scope="session")
 def oracle_lib():
     from oracle import build

@@ -130,6 +130,21 @@ def test_invalid_problems(kw, status):
     assert gb.last_error() != ""
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=1, T=256, chunk=128, H_k=256, H_v=32768, d_v=256, beta_per_key_head=1),
+    dict(B=1, T=256, chunk=64, H_k=1024, H_v=32768, d_v=512, beta_per_key_head=1),
+])
+def test_chunk_of_v_or_o_beyond_4gib(kw):
+    """The scan addresses the rows of one chunk of v and o with 32-bit byte
+    offsets: C * H_v * d_v * 4 bytes must stay below 2^32."""
+    p = problem(**kw)
+    assert p.chunk * p.H_v * p.d_v * 4 >= 1 << 32
+    assert call_fwd(p) == gb.GDR_ERR_UNSUPPORTED
+    assert "2^30" in gb.last_error()
+    # the same heads at half the value width pass this check
+    assert (p.chunk * p.H_v * (p.d_v // 2) * 4) < 1 << 32
+
+
 def test_null_problem():
     assert call_fwd(None) == gb.GDR_ERR_INVALID_ARG
 

@@ -6,8 +6,9 @@ hT, grouped value heads == replicated heads, extreme decay, empty input.
 Statistic per sample: max |o_gpu - o_ref| / rms(o_ref) over the sampled
 units (and the same for hT); bar 1e-2 (bf16 inputs) / 1e-4 (fp32 inputs).
 The Neumann run of the strong-decay workload is held to the bar against the
-fp64 chunk form with the same truncated series; its distance to the exact
-recurrence is printed (the pages bound it for trained layers only).
+fp64 chunk form with the same truncated series, for o and hT on four units;
+its distance to the exact recurrence is printed (the pages bound it for
+trained layers only).
 """
 import numpy as np
 import pytest
@@ -34,9 +35,13 @@ MIXED_LONG = Workload("kda_c64_mixed_long", 1, 16384, 16, 16, 128, 128, 64, 128,
                       alpha_mu=0.85, alpha_sigma=2.0, seed=31)
 
 
-def sample_units(w, n=3):
+def sample_units(w):
+    """Eight (batch, value head) units spread over the batch and the heads
+    (all of them when there are at most eight)."""
     total = w.B * w.H_v
-    return sorted({0, total // 2, total - 1} if n == 3 else set(range(min(n, total))))
+    if total <= 8:
+        return list(range(total))
+    return sorted({0, 1, total // 4 + 3, total // 2 - 1, total // 2, 3 * total // 4 + 1, total - 2, total - 1})
 
 
 def unit_err(o, o_ref, w, units):
@@ -89,20 +94,23 @@ def test_strong_decay_neumann():
     o_n, h_n = run_chunk(dev, w, solve="neumann")
     o_e, _ = run_chunk(dev, w, solve="exact")
     o_n, h_n, o_e = o_n.cpu().numpy(), h_n.cpu().numpy(), o_e.cpu().numpy()
-    units = [0, 9]
+    units = [0, 5, 9, 15]
     o_ref_n, h_ref_n = och.chunk_forward(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], chunk=w.chunk,
                                          solve="neumann", order=w.neumann_order,
                                          residual_steps=w.neumann_residual, units=units)
     o_ref, _ = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], units=units)
     e_parity = unit_err(o_n, o_ref_n, w, units)
+    e_state = rel_err(np.stack([h_n[u // w.H_v, u % w.H_v] for u in units]),
+                      np.stack([h_ref_n[u // w.H_v, u % w.H_v] for u in units]))
     e_vs_oracle = unit_err(o_n, o_ref, w, units)
     e_vs_exact = rel_err(o_n, o_e)
     e_oracle_trunc = unit_err(o_ref_n, o_ref, w, units)
-    print(f"  neumann GPU vs fp64 neumann chunk form: {e_parity:.3e}; GPU neumann vs exact recurrence: "
+    print(f"  neumann GPU vs fp64 neumann chunk form: o {e_parity:.3e} hT {e_state:.3e}; "
+          f"GPU neumann vs exact recurrence: "
           f"{e_vs_oracle:.3e}; fp64 neumann vs exact recurrence: {e_oracle_trunc:.3e}; "
           f"GPU neumann vs GPU exact (all units): {e_vs_exact:.3e}", flush=True)
     assert np.all(np.isfinite(o_n))
-    assert e_parity <= TOL[w.dtype]
+    assert e_parity <= TOL[w.dtype] and e_state <= TOL[w.dtype]
 
 
 SMALL_KDA = Workload("inv_kda", 2, 640, 2, 4, 128, 64, 64, 128, "bf16", seed=31)
