@@ -18,7 +18,8 @@ GDR_F32, GDR_BF16 = 0, 1
 GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
 
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_workspace_layout", "gdr_chunk_prepare",
-           "gdr_chunk_scan", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error")
+           "gdr_chunk_scan", "gdr_chunk_fwd_noalloc", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
 # Workspace regions, in order (include/gdr.h, gdr_chunk_fwd_workspace_size).
 WS_REGIONS = ("A", "L", "KB", "QB", "KH", "GM")
 
@@ -57,6 +58,8 @@ def load():
         lib.gdr_chunk_workspace_layout.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_prepare.restype = ctypes.c_int
         lib.gdr_chunk_prepare.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
         lib.gdr_recurrent_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
@@ -195,6 +198,23 @@ def gdr_chunk_fwd(q, k, v, beta, log_alpha, h0=None, *, chunk=64, solve="exact",
     return it holds the prepared chunk quantities (gdr_chunk_workspace_layout)."""
     return _chunk_call("gdr_chunk_fwd", q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order,
                        neumann_residual_steps, out_dtype, o, hT, return_final_state, workspace, stream)
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, beta, log_alpha, h0, o, hT, *, chunk=64, solve="exact", neumann_order=4,
+                          neumann_residual_steps=1, stream=None):
+    """gdr_chunk_fwd into caller-provided ``o`` (and ``hT``, or None) with the
+    library's static per-device scratch instead of a workspace: neither this
+    call nor the library allocates.  Calls that overlap on one device race."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, chunk=chunk, solve=solve, neumann_order=neumann_order,
+                     neumann_residual_steps=neumann_residual_steps, out_dtype=o.dtype)
+    state_shape = (p.B, p.H_v, p.d_k, p.d_v)
+    _check(lib.gdr_chunk_fwd_noalloc(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
+        _ptr(h0, "h0", torch.float32, state_shape), _ptr(o, "o", o.dtype, (p.B, p.T, p.H_v, p.d_v)),
+        _ptr(hT, "hT", torch.float32, state_shape), _stream(stream)))
+    return o, hT
 
 
 def gdr_chunk_scan(q, k, v, beta, log_alpha, h0=None, *, workspace, chunk=64, solve="exact", neumann_order=4,

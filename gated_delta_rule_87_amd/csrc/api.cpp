@@ -201,9 +201,12 @@ gdr_status gdr_chunk_prepare(const gdr_problem *p, const void *q, const void *k,
   return launched(gdr::launch_prep(a, p->in_dtype == GDR_BF16, static_cast<hipStream_t>(stream)), "prep kernel");
 }
 
-namespace {
+}  // extern "C"
 
-// Shared by gdr_chunk_fwd (prepare + scan) and gdr_chunk_scan (scan only).
+namespace gdr {
+
+// Shared by gdr_chunk_fwd (prepare + scan), gdr_chunk_scan (scan only) and
+// the entry point that brings its own scratch (noalloc.hip).
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
                          size_t workspace_bytes, void *stream, bool prepare) {
@@ -241,18 +244,29 @@ gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, con
   return launched(gdr::launch_scan(a, in_bf16, out_bf16, st), "scan kernel");
 }
 
-}  // namespace
+gdr_status workspace_bytes_of(const gdr_problem *p, size_t *bytes) {
+  gdr_status s = check_problem(p, true);
+  if (s != GDR_OK) return s;
+  *bytes = ws_bytes(p);
+  return GDR_OK;
+}
+
+gdr_status set_error(gdr_status s, const char *text) { return fail(s, "%s", text); }
+
+}  // namespace gdr
+
+extern "C" {
 
 gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, void *workspace,
                          size_t workspace_bytes, void *stream) {
-  return chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true);
+  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true);
 }
 
 gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, void *o, float *hT,
                           const void *workspace, size_t workspace_bytes, void *stream) {
-  return chunk_forward(p, nullptr, nullptr, v, nullptr, nullptr, h0, o, hT, workspace, workspace_bytes, stream,
-                       false);
+  return gdr::chunk_forward(p, nullptr, nullptr, v, nullptr, nullptr, h0, o, hT, workspace, workspace_bytes, stream,
+                            false);
 }
 
 gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,

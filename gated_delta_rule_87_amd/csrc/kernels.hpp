@@ -76,6 +76,22 @@ hipError_t launch_prep(const ChunkArgs &a, bool in_bf16, hipStream_t stream);
 hipError_t launch_scan(const ChunkArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 
+}  // namespace gdr
+
+#include "gdr.h"
+
+namespace gdr {
+
+// The chunk forward behind gdr_chunk_fwd (prepare = true) and gdr_chunk_scan
+// (prepare = false): validation, then the launches.  api.cpp.
+gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                         const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
+                         size_t workspace_bytes, void *stream, bool prepare);
+// Workspace bytes of a valid problem (else the validation status).
+gdr_status workspace_bytes_of(const gdr_problem *p, size_t *bytes);
+// Record `text` as this thread's gdr_last_error() and return s.
+gdr_status set_error(gdr_status s, const char *text);
+
 // Raise a kernel's dynamic LDS limit to the CU's 160 KiB, once per kernel and
 // device (each launch then passes its own size); later calls return at once.
 hipError_t allow_full_lds(const void *kernel);

@@ -167,6 +167,26 @@ gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, 
                           const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdr_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  The per-chunk quantities go to a static
+ * device array of GDR_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds
+ * on each device it runs on until the process ends; the array of the current
+ * device (hipGetDevice) is used, so `stream` must belong to that device.
+ * Problems whose gdr_chunk_fwd_workspace_size exceeds the array return
+ * GDR_ERR_UNSUPPORTED with nothing enqueued.  No memory is allocated or
+ * freed and nothing in the array needs clearing (the prep kernels write
+ * every byte the scan reads).  Every call on one device shares its array:
+ * calls that overlap in time on one device (two streams, two threads) race
+ * and produce wrong results; the caller must serialise them.  Other
+ * arguments, results and errors as for gdr_chunk_fwd.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem *p, const void *q, const void *k, const void *v,
+                                 const void *beta, const void *log_alpha, const float *h0, void *o,
+                                 float *hT, void *stream);
+
+/*
  * Token recurrence, p->T tokens in order (Systolic Linear Attention, section
  * 2.1, Eq. (2)), updating `state` in place (fp32 [B,H_v,d_k,d_v], read and
  * written) and writing o [B,T,H_v,d_v].  chunk / solve fields are ignored.
