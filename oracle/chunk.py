@@ -34,6 +34,18 @@ In-chunk inverses:
 * :func:`block_neumann_inverse` is the block-Jacobi form of section 2.4.3's
   block-Neumann factorisation, sum_{s<terms} (-N)^s D_blk^{-1}.
 
+Document resets and chunk-boundary momentum (Table 2: Z_c, mu, kappa_c;
+section 2.3, "Why chunk-level momentum"): a reset at token t discards the
+state carried into t.  Within a chunk the tokens then fall into segments
+(segment of t = number of resets at or before t in the chunk); Lambda is
+cumulated from the start of each token's segment; pairs (t, j) of different
+segments get no decay factor (their Gram and score entries are zero); only
+segment 0 sees the chunk-entry state (rows of Qbar and Kbar of later
+segments are zero); only the last segment carries into the chunk's end (rows
+of Khat before it are zero); F_c is zero when the chunk holds a reset, and
+so is kappa_c.  Momentum then acts on the increment Delta S_c = Khat^T E_c:
+Z_c = mu kappa_c Z_{c-1} + Delta S_c, S_c = F_c S_{c-1} + Z_c.
+
 Everything is fp64 numpy; exponentials are only taken of Lambda_t - Lambda_j
 on the causal side t >= j (masked before exp), i.e. of non-positive numbers.
 """
@@ -107,30 +119,41 @@ def invert(M, solve="exact", order=4, residual_steps=1):
 
 
 # ------------------------------------------------------------ chunk pieces
-def chunk_pieces(q, k, beta, la):
+def chunk_pieces(q, k, beta, la, reset=None):
     """Per-chunk quantities of Table 2 for one key head and one chunk.
 
     q, k: [n, d_k]; beta: [n]; la: [n, d_k] per-channel log decay (groups
-    already broadcast).  Returns a dict with Lambda, Qbar, Kbar, Khat, gamma
-    (= diag of F_c), G (the beta-free strictly lower Gram), M = G diag(beta)
-    and L.
+    already broadcast); reset: [n] or None, nonzero where a token starts a new
+    document.  Returns a dict with Lambda, Qbar, Kbar, Khat, gamma (= diag of
+    F_c), kappa, G (the beta-free strictly lower Gram), M = G diag(beta) and L.
     """
     n = q.shape[0]
-    Lam = np.cumsum(la, axis=0)
+    rs = np.zeros(n, bool) if reset is None else np.asarray(reset) != 0
+    seg = np.cumsum(rs)                                         # segment of each token
+    Lam = np.zeros_like(np.asarray(la, np.float64))
+    run = np.zeros(la.shape[1])
+    for t in range(n):                                          # cumulated within the segment
+        run = (0.0 if rs[t] else run) + la[t]
+        Lam[t] = run
     t_idx = np.arange(n)
-    causal = t_idx[:, None] >= t_idx[None, :]                   # t >= j
+    same = seg[:, None] == seg[None, :]
+    causal = (t_idx[:, None] >= t_idx[None, :]) & same          # t >= j, same document
     diff = Lam[:, None, :] - Lam[None, :, :]                    # Lambda_t - Lambda_j
     P = np.where(causal[:, :, None], np.exp(np.where(causal[:, :, None], diff, 0.0)), 0.0)
     kk = np.einsum("ti,ji,tji->tj", k, k, P)
     qk = np.einsum("ti,ji,tji->tj", q, k, P)
-    strict = t_idx[:, None] > t_idx[None, :]
+    strict = (t_idx[:, None] > t_idx[None, :]) & same
     G = np.where(strict, kk, 0.0)
+    first = (seg == 0)[:, None]                                 # tokens that see the chunk-entry state
+    last = (seg == seg[-1])[:, None] if n else first           # tokens that carry into the chunk's end
+    kappa = not rs.any()
     return {
         "Lambda": Lam,
-        "Qbar": q * np.exp(Lam),
-        "Kbar": k * np.exp(Lam),
-        "Khat": k * np.exp(Lam[-1][None, :] - Lam),
-        "gamma": np.exp(Lam[-1]),
+        "Qbar": np.where(first, q * np.exp(np.where(first, Lam, 0.0)), 0.0),
+        "Kbar": np.where(first, k * np.exp(np.where(first, Lam, 0.0)), 0.0),
+        "Khat": np.where(last, k * np.exp(np.where(last, Lam[-1][None, :] - Lam, 0.0)), 0.0),
+        "gamma": np.exp(Lam[-1]) if kappa else np.zeros(la.shape[1]),
+        "kappa": kappa,
         "G": G,
         "M": G * beta[None, :],
         "L": np.where(causal, qk, 0.0),
@@ -150,35 +173,48 @@ def _expand(q, k, log_alpha, beta, beta_per_key_head, b, hv, Hv, Hk):
 
 
 def chunk_forward(q, k, v, beta, log_alpha, h0=None, chunk=64, solve="exact",
-                  order=4, residual_steps=1, beta_per_key_head=False, units=None):
+                  order=4, residual_steps=1, beta_per_key_head=False, units=None,
+                  reset=None, momentum=0.0, z0=None, return_z=False):
     """Chunkwise WY forward in fp64 with the chosen in-chunk inverse.
 
     Shapes as in :mod:`oracle.recurrence`; a final chunk shorter than
-    ``chunk`` is processed at its own length.  Returns (o, hT) in float64;
-    with ``units`` only those b * H_v + h_v entries are filled.
+    ``chunk`` is processed at its own length.  ``reset`` [B, T] marks tokens
+    that start a new document; ``momentum`` is mu of the chunk-boundary
+    momentum, ``z0`` its initial buffer.  Returns (o, hT), or (o, hT, zT) with
+    ``return_z``, in float64; with ``units`` only those b * H_v + h_v entries
+    are filled.
     """
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     o = np.zeros((B, T, Hv, dv))
     hT = np.zeros((B, Hv, dk, dv))
+    zT = np.zeros((B, Hv, dk, dv))
     todo = range(B * Hv) if units is None else units
     for u in todo:
         b, hv = divmod(int(u), Hv)
         qh, kh, la, bh = _expand(q, k, log_alpha, beta, beta_per_key_head, b, hv, Hv, Hk)
         vh = np.asarray(v[b, :, hv], np.float64)
+        rb = None if reset is None else np.asarray(reset[b])
         S = np.zeros((dk, dv)) if h0 is None else np.array(h0[b, hv], np.float64)
+        Z = np.zeros((dk, dv)) if z0 is None else np.array(z0[b, hv], np.float64)
         for s in range(0, T, chunk):
             e = min(s + chunk, T)
-            pc = chunk_pieces(qh[s:e], kh[s:e], bh[s:e], la[s:e])
+            pc = chunk_pieces(qh[s:e], kh[s:e], bh[s:e], la[s:e], None if rb is None else rb[s:e])
             A = invert(pc["M"], solve, order, residual_steps)
             Bd = bh[s:e][:, None]
             U = Bd * (A @ vh[s:e])                 # U_c = diag(beta) A_c V_c
             W = Bd * (A @ pc["Kbar"])              # W_c = diag(beta) A_c Kbar_c
             E = U - W @ S                          # E_c = U_c - W_c S_{c-1}
             o[b, s:e, hv] = pc["Qbar"] @ S + pc["L"] @ E
-            S = pc["gamma"][:, None] * S + pc["Khat"].T @ E
+            dS = pc["Khat"].T @ E                  # Delta S_c
+            if momentum != 0.0:
+                Z = momentum * (Z if pc["kappa"] else 0.0) + dS
+                S = pc["gamma"][:, None] * S + Z
+            else:
+                S = pc["gamma"][:, None] * S + dS
         hT[b, hv] = S
-    return o, hT
+        zT[b, hv] = Z
+    return (o, hT, zT) if return_z else (o, hT)
 
 
 def chunk_stage_matrices(q, k, beta, log_alpha, chunk, solve="exact", order=4,

@@ -39,6 +39,27 @@
  * units: optional list of n_units indices u = b * H_v + h_v to evaluate (the
  * others are left untouched); NULL evaluates every (b, h_v).
  * Returns 0 on success, -1 on a malformed problem.
+ *
+ * oracle_gdr_layer adds the two sequence-level features of the Systolic
+ * Linear Attention layer (Table 2, the symbols Z_c, mu and kappa_c; section
+ * 2.3, "Why chunk-level momentum"):
+ *
+ *   Document resets.  reset [B, T] (bytes, NULL = none): reset[b, t] != 0
+ *   means token t starts a new document, so the state carried into it is
+ *   discarded: S_{t-1} <- 0 before the step above.
+ *
+ *   Chunk-boundary momentum.  With chunk C > 0 and coefficient mu, the
+ *   sequence is cut into chunks of C tokens from its first token (the last
+ *   one may be shorter).  Over chunk c the state evolves token by token from
+ *   the chunk-entry state S_{c-1} as above (outputs are read from it, token
+ *   by token) to S~_c.  At the chunk's end, with F_c the product of the
+ *   chunk's decays and kappa_c = 0 when any reset falls inside the chunk
+ *   (else 1):
+ *     carry = kappa_c F_c S_{c-1}        (cross-document carry discarded)
+ *     Z_c   = mu kappa_c Z_{c-1} + (S~_c - carry)
+ *     S_c   = carry + Z_c.
+ *   Z_0 = z0 (NULL = zero); zT = Z after the last chunk.  mu = 0 skips the
+ *   chunk-end step, so the result is the plain recurrence bit for bit.
  */
 #include <math.h>
 #include <pthread.h>
@@ -49,8 +70,11 @@
 typedef struct {
   int B, T, Hk, Hv, dk, dv, G, beta_per_key_head;
   const float *q, *k, *v, *beta, *log_alpha;
-  const double *h0;
-  double *o, *hT;
+  const unsigned char *reset;
+  const double *h0, *z0;
+  int chunk;
+  double momentum;
+  double *o, *hT, *zT;
   const int *units;
   int n_units;
   int next; /* work counter, guarded by mu */
@@ -66,14 +90,34 @@ static void run_unit(const job_t *j, int u) {
   double *kv = (double *)malloc(sizeof(double) * (size_t)dk);
   double *qv = (double *)malloc(sizeof(double) * (size_t)dk);
   double *uu = (double *)malloc(sizeof(double) * (size_t)dv);
-  const size_t state_off = ((size_t)b * Hv + hv) * (size_t)dk * dv;
+  const size_t nS = (size_t)dk * dv;
+  const int mom = j->chunk > 0 && j->momentum != 0.0;
+  double *S_in = (double *)malloc(sizeof(double) * nS);  /* chunk-entry state S_{c-1} */
+  double *Z = (double *)malloc(sizeof(double) * nS);     /* momentum buffer Z_{c-1} */
+  double *Fc = (double *)malloc(sizeof(double) * (size_t)dk);  /* product of the chunk's decays */
+  int kappa = 1;
+  const size_t state_off = ((size_t)b * Hv + hv) * nS;
   if (j->h0) {
-    memcpy(S, j->h0 + state_off, sizeof(double) * (size_t)dk * dv);
+    memcpy(S, j->h0 + state_off, sizeof(double) * nS);
   } else {
-    memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    memset(S, 0, sizeof(double) * nS);
+  }
+  if (j->z0) {
+    memcpy(Z, j->z0 + state_off, sizeof(double) * nS);
+  } else {
+    memset(Z, 0, sizeof(double) * nS);
   }
   for (int t = 0; t < T; ++t) {
     const size_t bt = (size_t)b * T + t;
+    if (mom && t % j->chunk == 0) { /* chunk entry */
+      memcpy(S_in, S, sizeof(double) * nS);
+      for (int i = 0; i < dk; ++i) Fc[i] = 1.0;
+      kappa = 1;
+    }
+    if (j->reset && j->reset[bt]) { /* a new document: discard the carried state */
+      memset(S, 0, sizeof(double) * nS);
+      kappa = 0;
+    }
     const float *kt = j->k + (bt * Hk + hk) * (size_t)dk;
     const float *qt = j->q + (bt * Hk + hk) * (size_t)dk;
     const float *vt = j->v + (bt * Hv + hv) * (size_t)dv;
@@ -83,6 +127,7 @@ static void run_unit(const job_t *j, int u) {
       f[i] = exp((double)lat[i / group_width]);
       kv[i] = (double)kt[i];
       qv[i] = (double)qt[i];
+      if (mom) Fc[i] *= f[i];
     }
     /* decay: S <- F_t S */
     for (int i = 0; i < dk; ++i) {
@@ -108,8 +153,23 @@ static void run_unit(const job_t *j, int u) {
       const double *row = S + (size_t)i * dv;
       for (int c = 0; c < dv; ++c) ot[c] += row[c] * qv[i];
     }
+    if (mom && (t % j->chunk == j->chunk - 1 || t == T - 1)) { /* chunk end */
+      for (int i = 0; i < dk; ++i) {
+        const double fk = kappa ? Fc[i] : 0.0;
+        for (int c = 0; c < dv; ++c) {
+          const size_t e = (size_t)i * dv + c;
+          const double carry = fk * S_in[e];
+          Z[e] = j->momentum * (kappa ? Z[e] : 0.0) + (S[e] - carry);
+          S[e] = carry + Z[e];
+        }
+      }
+    }
   }
-  if (j->hT) memcpy(j->hT + state_off, S, sizeof(double) * (size_t)dk * dv);
+  if (j->hT) memcpy(j->hT + state_off, S, sizeof(double) * nS);
+  if (j->zT) memcpy(j->zT + state_off, Z, sizeof(double) * nS);
+  free(S_in);
+  free(Z);
+  free(Fc);
   free(S);
   free(f);
   free(kv);
@@ -129,17 +189,18 @@ static void *worker(void *arg) {
   return NULL;
 }
 
-int oracle_gdr_recurrence(int B, int T, int Hk, int Hv, int dk, int dv, int G,
-                          int beta_per_key_head, const float *q, const float *k,
-                          const float *v, const float *beta, const float *log_alpha,
-                          const double *h0, double *o, double *hT, const int *units,
-                          int n_units, int nthreads) {
+int oracle_gdr_layer(int B, int T, int Hk, int Hv, int dk, int dv, int G, int beta_per_key_head,
+                     const float *q, const float *k, const float *v, const float *beta,
+                     const float *log_alpha, const unsigned char *reset, const double *h0,
+                     const double *z0, int chunk, double momentum, double *o, double *hT,
+                     double *zT, const int *units, int n_units, int nthreads) {
   if (B < 0 || T < 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || G <= 0) return -1;
-  if (Hv % Hk != 0 || dk % G != 0) return -1;
+  if (Hv % Hk != 0 || dk % G != 0 || chunk < 0) return -1;
   job_t j;
   j.B = B; j.T = T; j.Hk = Hk; j.Hv = Hv; j.dk = dk; j.dv = dv; j.G = G;
   j.beta_per_key_head = beta_per_key_head;
   j.q = q; j.k = k; j.v = v; j.beta = beta; j.log_alpha = log_alpha;
+  j.reset = reset; j.z0 = z0; j.chunk = chunk; j.momentum = momentum; j.zT = zT;
   j.h0 = h0; j.o = o; j.hT = hT;
   j.units = units;
   j.n_units = units ? n_units : B * Hv;
@@ -158,4 +219,13 @@ int oracle_gdr_recurrence(int B, int T, int Hk, int Hv, int dk, int dv, int G,
   free(th);
   pthread_mutex_destroy(&j.mu);
   return 0;
+}
+
+int oracle_gdr_recurrence(int B, int T, int Hk, int Hv, int dk, int dv, int G,
+                          int beta_per_key_head, const float *q, const float *k,
+                          const float *v, const float *beta, const float *log_alpha,
+                          const double *h0, double *o, double *hT, const int *units,
+                          int n_units, int nthreads) {
+  return oracle_gdr_layer(B, T, Hk, Hv, dk, dv, G, beta_per_key_head, q, k, v, beta, log_alpha, NULL,
+                          h0, NULL, 0, 0.0, o, hT, NULL, units, n_units, nthreads);
 }
