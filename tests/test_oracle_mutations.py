@@ -95,8 +95,8 @@ def test_mutation_is_caught(mutation):
 def _chunk_with(mutation):
     orig = ch.chunk_pieces
 
-    def pieces(q, k, beta, la):
-        pc = orig(q, k, beta, la)
+    def pieces(q, k, beta, la, reset=None):
+        pc = orig(q, k, beta, la, reset)
         n = q.shape[0]
         if mutation == "L_without_diagonal":
             pc["L"] = np.tril(pc["L"], -1)
