@@ -18,7 +18,8 @@ GDR_F32, GDR_BF16 = 0, 1
 GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
 
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_workspace_layout", "gdr_chunk_prepare",
-           "gdr_chunk_scan", "gdr_chunk_fwd_noalloc", "gdr_recurrent_step", "gdr_status_string", "gdr_last_error")
+           "gdr_chunk_scan", "gdr_chunk_fwd_noalloc", "gdr_chunk_fwd_ex", "gdr_gated_rmsnorm", "gdr_recurrent_step",
+           "gdr_status_string", "gdr_last_error")
 NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
 # Workspace regions, in order (include/gdr.h, gdr_chunk_fwd_workspace_size).
 WS_REGIONS = ("A", "L", "KB", "QB", "KH", "GM")
@@ -28,6 +29,11 @@ class GdrProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "B", "T", "H_k", "H_v", "d_k", "d_v", "chunk", "gate_groups", "beta_per_key_head",
         "in_dtype", "out_dtype", "solve", "neumann_order", "neumann_residual_steps")]
+
+
+class GdrLayerOpts(ctypes.Structure):
+    _fields_ = [("reset", ctypes.c_void_p), ("momentum", ctypes.c_float), ("z0", ctypes.c_void_p),
+                ("zT", ctypes.c_void_p)]
 
 
 class GdrError(RuntimeError):
@@ -58,6 +64,11 @@ def load():
         lib.gdr_chunk_workspace_layout.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         lib.gdr_chunk_prepare.restype = ctypes.c_int
         lib.gdr_chunk_prepare.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_fwd_ex.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_ex.argtypes = [P, ctypes.POINTER(GdrLayerOpts), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
+        lib.gdr_gated_rmsnorm.restype = ctypes.c_int
+        lib.gdr_gated_rmsnorm.argtypes = [P, vp, vp, vp, ctypes.c_float, vp, vp]
         lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.gdr_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
@@ -198,6 +209,71 @@ def gdr_chunk_fwd(q, k, v, beta, log_alpha, h0=None, *, chunk=64, solve="exact",
     return it holds the prepared chunk quantities (gdr_chunk_workspace_layout)."""
     return _chunk_call("gdr_chunk_fwd", q, k, v, beta, log_alpha, h0, chunk, solve, neumann_order,
                        neumann_residual_steps, out_dtype, o, hT, return_final_state, workspace, stream)
+
+
+def gdr_chunk_fwd_ex(q, k, v, beta, log_alpha, h0=None, *, reset=None, momentum=0.0, z0=None, zT=None,
+                     return_momentum_state=False, chunk=64, solve="exact", neumann_order=4, neumann_residual_steps=1,
+                     out_dtype=torch.float32, o=None, hT=None, return_final_state=True, workspace=None, stream=None):
+    """Chunk forward with the layer options: ``reset`` (uint8/bool [B, T],
+    nonzero where a token starts a new document), chunk-boundary ``momentum``
+    (mu) with buffer ``z0`` in and ``zT`` out (fp32 [B, H_v, d_k, d_v]).
+    Returns (o, hT) or, with ``return_momentum_state`` (or a given zT),
+    (o, hT, zT)."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, chunk=chunk, solve=solve, neumann_order=neumann_order,
+                     neumann_residual_steps=neumann_residual_steps, out_dtype=out_dtype)
+    dev = q.device
+    state_shape = (p.B, p.H_v, p.d_k, p.d_v)
+    if o is None:
+        o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=dev)
+    if hT is None and return_final_state:
+        hT = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    want_z = return_momentum_state or zT is not None
+    if zT is None and want_z:
+        zT = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    if reset is not None:
+        if tuple(reset.shape) != (p.B, p.T):
+            raise ValueError(f"reset has shape {tuple(reset.shape)}, expected {(p.B, p.T)}")
+        reset = reset.to(torch.uint8) if reset.dtype != torch.uint8 else reset
+    opts = GdrLayerOpts()
+    opts.reset = _ptr(reset, "reset", torch.uint8)
+    opts.momentum = float(momentum)
+    opts.z0 = _ptr(z0, "z0", torch.float32, state_shape)
+    opts.zT = _ptr(zT, "zT", torch.float32, state_shape)
+    ws_bytes = gdr_chunk_fwd_workspace_size(p)
+    if ws_bytes == 0 and p.B * p.T > 0:
+        _check(lib.gdr_chunk_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.gdr_chunk_fwd_ex(
+        ctypes.byref(p), ctypes.byref(opts), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"),
+        _ptr(log_alpha, "log_alpha"), _ptr(h0, "h0", torch.float32, state_shape),
+        _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _ptr(hT, "hT", torch.float32, state_shape),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (o, hT, zT) if want_z else (o, hT)
+
+
+def gdr_gated_rmsnorm(o, z, *, weight=None, eps=1e-6, y=None, stream=None):
+    """y = sigmoid(z) * o / sqrt(mean(o^2 over d_v) + eps) * weight, per
+    (batch, token, value head) row; o, y [B, T, H_v, d_v] (fp32 or bf16, y
+    like o unless given), z [B, T, H_v, d_v] (fp32 or bf16), weight fp32
+    [d_v] or None.  y may be o itself."""
+    lib = load()
+    if o.dim() != 4 or tuple(z.shape) != tuple(o.shape):
+        raise ValueError(f"o {tuple(o.shape)} and z {tuple(z.shape)} must both be [B, T, H_v, d_v]")
+    if y is None:
+        y = torch.empty_like(o)
+    B, T, Hv, dv = o.shape
+    p = GdrProblem()
+    p.B, p.T, p.H_k, p.H_v, p.d_k, p.d_v = B, T, Hv, Hv, 64, dv
+    p.chunk, p.gate_groups = 64, 1
+    p.in_dtype = _DT[z.dtype]
+    p.out_dtype = _DT[o.dtype]
+    _check(lib.gdr_gated_rmsnorm(ctypes.byref(p), _ptr(o, "o"), _ptr(z, "z"),
+                                 _ptr(weight, "weight", torch.float32, (dv,)), float(eps),
+                                 _ptr(y, "y", o.dtype, tuple(o.shape)), _stream(stream)))
+    return y
 
 
 def gdr_chunk_fwd_noalloc(q, k, v, beta, log_alpha, h0, o, hT, *, chunk=64, solve="exact", neumann_order=4,

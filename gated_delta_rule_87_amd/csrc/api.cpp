@@ -3,6 +3,7 @@
 // memory or synchronises; every check runs before the first launch.
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -209,20 +210,30 @@ namespace gdr {
 // the entry point that brings its own scratch (noalloc.hip).
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
-                         size_t workspace_bytes, void *stream, bool prepare) {
+                         size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts) {
   gdr_status s = check_problem(p, true);
   if (s != GDR_OK) return s;
   if ((s = check_ptr(h0, "h0", false)) || (s = check_ptr(hT, "hT", false))) return s;
+  const bool mom = opts && opts->momentum != 0.f;
+  if (opts && !std::isfinite(opts->momentum))
+    return fail(GDR_ERR_INVALID_ARG, "momentum=%g is not finite", (double)opts->momentum);
+  if (mom && ((s = check_ptr(opts->z0, "z0", false)) || (s = check_ptr(opts->zT, "zT", false)))) return s;
   if (p->B == 0) return GDR_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool in_bf16 = p->in_dtype == GDR_BF16, out_bf16 = p->out_dtype == GDR_BF16;
   if (p->T == 0) {
     // No tokens: the final state is the initial one.  The scan kernel over
-    // zero chunks writes hT from h0 (or zeros) and touches nothing else.
-    if (!hT) return GDR_OK;
+    // zero chunks writes hT from h0 (and zT from z0, or zeros) and touches
+    // nothing else.
+    if (!hT && !(mom && opts->zT)) return GDR_OK;
     gdr::ChunkArgs a = make_chunk_args(p, nullptr);
     a.h0 = h0;
     a.hT = hT;
+    if (mom) {
+      a.momentum = opts->momentum;
+      a.z0 = opts->z0;
+      a.zT = opts->zT;
+    }
     return launched(gdr::launch_scan(a, in_bf16, out_bf16, st), "scan kernel");
   }
   if ((s = check_ptr(q, "q", prepare)) || (s = check_ptr(k, "k", prepare)) || (s = check_ptr(v, "v", true)) ||
@@ -240,6 +251,14 @@ gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, con
   a.h0 = h0;
   a.o = o;
   a.hT = hT;
+  if (opts) {
+    a.reset = opts->reset;
+    if (mom) {
+      a.momentum = opts->momentum;
+      a.z0 = opts->z0;
+      a.zT = opts->zT;
+    }
+  }
   if (prepare && (s = launched(gdr::launch_prep(a, in_bf16, st), "prep kernel")) != GDR_OK) return s;
   return launched(gdr::launch_scan(a, in_bf16, out_bf16, st), "scan kernel");
 }
@@ -260,13 +279,37 @@ extern "C" {
 gdr_status gdr_chunk_fwd(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, void *workspace,
                          size_t workspace_bytes, void *stream) {
-  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true);
+  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true,
+                            nullptr);
+}
+
+gdr_status gdr_chunk_fwd_ex(const gdr_problem *p, const gdr_layer_opts *opts, const void *q, const void *k,
+                            const void *v, const void *beta, const void *log_alpha, const float *h0, void *o,
+                            float *hT, void *workspace, size_t workspace_bytes, void *stream) {
+  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true,
+                            opts);
+}
+
+gdr_status gdr_gated_rmsnorm(const gdr_problem *p, const void *o, const void *z, const float *weight, float eps,
+                             void *y, void *stream) {
+  gdr_status s = check_problem(p, false);
+  if (s != GDR_OK) return s;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(GDR_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", (double)eps);
+  if (p->B == 0 || p->T == 0) return GDR_OK;
+  if ((s = check_ptr(o, "o", true)) || (s = check_ptr(z, "z", true)) || (s = check_ptr(y, "y", true)) ||
+      (s = check_ptr(weight, "weight", false, 4)))
+    return s;
+  const long long rows = (long long)p->B * p->T * p->H_v;
+  if ((rows + 3) / 4 >= (1LL << 31)) return fail(GDR_ERR_UNSUPPORTED, "B*T*H_v=%lld rows exceed a launch", rows);
+  return launched(gdr::launch_gated_rmsnorm(o, z, weight, eps, y, rows, p->d_v, p->out_dtype == GDR_BF16,
+                                            p->in_dtype == GDR_BF16, static_cast<hipStream_t>(stream)),
+                  "gated rmsnorm kernel");
 }
 
 gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, void *o, float *hT,
                           const void *workspace, size_t workspace_bytes, void *stream) {
   return gdr::chunk_forward(p, nullptr, nullptr, v, nullptr, nullptr, h0, o, hT, workspace, workspace_bytes, stream,
-                            false);
+                            false, nullptr);
 }
 
 gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,

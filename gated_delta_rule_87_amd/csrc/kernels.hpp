@@ -55,6 +55,12 @@ struct ChunkArgs {
   int N_c;
   int beta_per_key_head;
   int solve, order, residual;
+  // Layer options (nullable / 0 = off): document resets [B, T] (nonzero =
+  // the token starts a new document) and chunk-boundary momentum.
+  const unsigned char *reset;
+  float momentum;
+  const float *z0;
+  float *zT;
 };
 
 // Tile of region r for (batch b, head, chunk c).
@@ -74,6 +80,8 @@ struct StepArgs {
 // status.  `in_bf16`/`out_bf16` select the element types.
 hipError_t launch_prep(const ChunkArgs &a, bool in_bf16, hipStream_t stream);
 hipError_t launch_scan(const ChunkArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const void *o, const void *z, const float *weight, float eps, void *y,
+                                long long rows, int d_v, bool o_bf16, bool z_bf16, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 
 }  // namespace gdr
@@ -82,11 +90,12 @@ hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream
 
 namespace gdr {
 
-// The chunk forward behind gdr_chunk_fwd (prepare = true) and gdr_chunk_scan
-// (prepare = false): validation, then the launches.  api.cpp.
+// The chunk forward behind gdr_chunk_fwd and gdr_chunk_fwd_ex (prepare =
+// true) and gdr_chunk_scan (prepare = false): validation, then the launches.
+// opts may be NULL.  api.cpp.
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
-                         size_t workspace_bytes, void *stream, bool prepare);
+                         size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts);
 // Workspace bytes of a valid problem (else the validation status).
 gdr_status workspace_bytes_of(const gdr_problem *p, size_t *bytes);
 // Record `text` as this thread's gdr_last_error() and return s.

@@ -66,5 +66,5 @@ extern "C" gdr_status gdr_chunk_fwd_noalloc(const gdr_problem *p, const void *q,
   if (p->B > 0 && p->T > 0 && (s = device_scratch(&ws)) != GDR_OK) return s;
   // Nothing in the scratch needs clearing: the prep kernels write every byte
   // the scan kernel then reads.
-  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, ws, kScratchBytes, stream, true);
+  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, ws, kScratchBytes, stream, true, nullptr);
 }

@@ -66,6 +66,7 @@ __host__ __device__ inline int prep_tmp_floats(int C) {
 
 constexpr int kXbLd = 20;   // row stride (floats) of the per-wave transpose buffers
 constexpr int kChunkWide = 8;  // flags slot: the chunk's decay range exceeds kPivotRange
+constexpr int kHasReset = 9;   // flags slot: a document starts inside the chunk
 
 // Chunk-pivot column operands of blocks 0 .. NB - 2 (split fragments, two
 // 1 KiB planes per block and channel step); only C = 64 (one row block per
@@ -81,9 +82,11 @@ __host__ __device__ inline int prep_union_floats(int C, int DK) {
   return solve > colop ? solve : colop;
 }
 
+// The block-pivot route also keeps each token's document segment (C bytes,
+// after the transpose buffers).
 size_t prep_lds_bytes(int C, int DK, int G) {
   return sizeof(float) * (size_t)(prep_region0_floats(C, G) + prep_union_floats(C, DK) + C) +
-         sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd;
+         sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd + C;
 }
 // The chunk-pivot kernel keeps Lambda in registers: region 0 holds the
 // block totals of Lambda during the build and G after it.
@@ -342,8 +345,9 @@ struct PrepItem {
   // the union region.  The solve's scratch follows C (C + 4) floats into the
   // union region on both routes.
   float *const smem, *const lam, *const ureg, *const tmp, *const bet;
-  int *const flags;                                    // [NB] block ranges, [kChunkWide]
+  int *const flags;                                    // [NB] block ranges, [kChunkWide], [kHasReset]
   float *const xb;                                     // this wave's transpose buffer [32 channels][kXbLd]
+  unsigned char *const seg;                            // [C] document segment of each token (block route)
   const TIn *const la, *const bp, *const kbase, *const qbase;
   const size_t row_stride, la_row;                     // token strides of q / k and of log alpha
   void *const tKB, *const tQB, *const tKH, *const tL;
@@ -356,6 +360,7 @@ struct PrepItem {
         ureg(smem_ + region0), tmp(ureg + C * prep_ld(C)),
         bet(ureg + prep_union_floats(C, DK)), flags(reinterpret_cast<int *>(bet + C)),
         xb(reinterpret_cast<float *>(flags + 16) + wave_id() * 32 * kXbLd),
+        seg(reinterpret_cast<unsigned char *>(reinterpret_cast<float *>(flags + 16) + 4 * 32 * kXbLd)),
         la(reinterpret_cast<const TIn *>(a_.log_alpha)), bp(reinterpret_cast<const TIn *>(a_.beta)),
         kbase(reinterpret_cast<const TIn *>(a_.k) + (size_t)hk_ * DK),
         qbase(reinterpret_cast<const TIn *>(a_.q) + (size_t)hk_ * DK), row_stride((size_t)a_.H_k * DK),
@@ -395,7 +400,11 @@ struct PrepItem {
 
   // Lambda = in-chunk prefix sum of log alpha per decay group (Systolic
   // Linear Attention, Table 2), and the decay range flags: per 16-token block
-  // and over the chunk.  Ends with a barrier.
+  // and over the chunk.  With document resets (the same paper, Table 2,
+  // kappa_c) the sum restarts at each token that starts a document, seg[t]
+  // becomes the number of documents started at or before t in the chunk, a
+  // block holding a reset is flagged (its diagonal pairs are then formed
+  // entry by entry) and flags[kHasReset] is set.  Ends with a barrier.
   __device__ __forceinline__ void lambda(const LaRegs &r) {
     if (G >= 8) {
 #pragma unroll
@@ -420,9 +429,25 @@ struct PrepItem {
       }
     }
     if (tid < 16) flags[tid] = 0;
+    if (tid < C) seg[tid] = (a.reset && t0 + tid < T) ? (a.reset[(size_t)b * T + t0 + tid] != 0) : 0;
     __syncthreads();
-    for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
+    if (a.reset) {
+      for (int g = tid; g < G; g += blockDim.x) prefix_column_restart<C>(lam + g, G, seg);
+    } else {
+      for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
+    }
     __syncthreads();
+    if (a.reset && tid == blockDim.x - 1) {            // reset marks -> segment numbers
+      int n = 0;
+      for (int t = 0; t < C; ++t) {
+        if (seg[t]) {
+          flags[t >> 4] = 1;
+          flags[kHasReset] = 1;
+          ++n;
+        }
+        seg[t] = n;
+      }
+    }
     // several threads may store the same 1
     for (int g = tid; g < G; g += blockDim.x) {
       float clo = lam[g], chi = clo;
@@ -447,8 +472,12 @@ struct PrepItem {
   __device__ __forceinline__ float *gm_row() const {
     return reinterpret_cast<float *>(ws_tile(a, kWsGM, a.H_k, hk, b, c));
   }
+  // exp(Lambda_C) per channel; -0 in every channel when a document starts in
+  // the chunk (nothing is carried across the chunk, and the sign tells the
+  // scan that kappa_c = 0 for the momentum buffer).  Reads flags[kHasReset],
+  // so it runs after lambda().
   __device__ __forceinline__ void write_gm() const {
-    if (tid < DK) gm_row()[tid] = __expf(lam[(C - 1) * G + (tid >> gs)]);
+    if (tid < DK) gm_row()[tid] = flags[kHasReset] ? -0.f : __expf(lam[(C - 1) * G + (tid >> gs)]);
   }
 
   // Lambda of row t for eight consecutive channels (vector reads per channel,
@@ -637,6 +666,8 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   x.load_rows(qt, x.qbase, I);
   TIn bets[NBET];
   x.load_betas(bets);
+  // a document starting in the chunk sends it to the block-pivot kernel
+  const bool reset_here = a.reset && mt > 0.f && a.reset[x.tok(tr)] != 0;
 
 
   // ---- Lambda of the lane's token in log2 units (log2(e) Lambda): in-block
@@ -644,7 +675,7 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   constexpr float kLog2e = 1.4426950408889634f;
   const float scale = mt * kLog2e;                     // tokens past T: zero log decay
   float lt[KS][8];
-  bool rising = false;                                 // a positive log alpha: Lambda not monotone
+  bool rising = reset_here;                            // a positive log alpha (Lambda not monotone) or a reset
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int ch0 = 32 * s + 8 * lq;
@@ -822,10 +853,17 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   x.lambda(lar);
   x.write_gm();
   float *gmat = x.ureg;
+  // Document segments (all 0 without resets): only segment 0 sees the
+  // chunk-entry state (Kbar, Qbar rows), only the last one carries to the
+  // chunk's end (Khat rows), and pairs of different segments are zero.  Every
+  // mask is a select, so an infinite factor of a pair across a reset (whose
+  // Lambda values belong to different documents) never reaches a kept entry.
+  const int seg_last = x.seg[C - 1];
   for (int r = 0; r < NR; ++r) {
     const int I = own(r);
     const int tr = 16 * I + lr, piv = 16 * I;
     const float mt = (t0 + tr < T) ? 1.f : 0.f;
+    const bool sees_entry = x.seg[tr] == 0, carries = x.seg[tr] == seg_last;
     Split ak[KS], aq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -844,9 +882,9 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
         const float h = __expf(lc[e] - lt[e]) * mt;
         yk[e] = xk[e] * ea;
         yq[e] = xq[e] * ea;
-        kbar[e] = xk[e] * d;
-        qbar[e] = xq[e] * d;
-        kh[e] = xk[e] * h;
+        kbar[e] = sees_entry ? xk[e] * d : 0.f;
+        qbar[e] = sees_entry ? xq[e] * d : 0.f;
+        kh[e] = carries ? xk[e] * h : 0.f;
       }
       ak[s] = make_frag<Split>(yk);
       aq[s] = make_frag<Split>(yq);
@@ -885,7 +923,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
         for (int q4 = 0; q4 < 4; ++q4) {
           const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
           float sg = 0.f, sl = 0.f;
-          if (row >= col && t0 + row < T) {
+          if (row >= col && t0 + row < T && x.seg[row] == x.seg[col]) {
             const size_t rrow = x.tok(row) * x.row_stride, rcol = x.tok(col) * x.row_stride;
             for (int ch = 0; ch < DK; ++ch) {
               const int g = ch >> x.gs;
@@ -902,7 +940,9 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
-        gmat[row * (C + 4) + col] = (I > J || row > col) ? accG[q4] : 0.f;
+        const bool same = x.seg[row] == x.seg[col];
+        gmat[row * (C + 4) + col] = ((I > J || row > col) && same) ? accG[q4] : 0.f;
+        accL[q4] = same ? accL[q4] : 0.f;
       }
       x.store_L_block(I, J, accL);
     }

@@ -45,6 +45,13 @@
 // slow the chunk down).  All loads of a non-final chunk are unconditional
 // (indices clamped to the last chunk) so the compiler's memory-wait counts
 // stay exact across iterations; the final, possibly ragged chunk is peeled.
+//
+// Chunk-boundary momentum (kMom; Systolic Linear Attention, Table 2, Z_c,
+// mu, kappa_c, and section 2.3): the increment Delta S_c = Khat_c^T E_c goes
+// to its own accumulator, the momentum buffer Z (fp32 accumulators shaped
+// like S) becomes Z = mu kappa_c Z + Delta S_c, and S = F_c S + Z.  kappa_c is
+// 0 when a document starts inside the chunk, which the prep kernels mark by
+// writing F_c as -0 (an exponential never yields it).
 #include <type_traits>
 
 #include "common.hpp"
@@ -129,7 +136,7 @@ __device__ __forceinline__ T *at(T *base, unsigned off) {
   return reinterpret_cast<T *>(reinterpret_cast<B *>(base) + off * (unsigned)sizeof(T));
 }
 
-template <typename TIn, typename TOut, class P, int C, int DK, int BV>
+template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   constexpr int FB = P::kF32 ? 2048 : 1024;
   using Lay = ScanLayout<C, DK, BV, FB>;
@@ -301,6 +308,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 
   // ---------------------------------------------------- state and prologue
   f32x4 S[SJ::RPW][SJ::TPW];
+  f32x4 Z[SJ::RPW][SJ::TPW];          // momentum buffer (kMom)
   const size_t sbase = ((size_t)b * a.H_v + hv) * DK * a.d_v;
 #pragma unroll
   for (int r = 0; r < SJ::RPW; ++r) {
@@ -313,6 +321,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int i = i0 + 4 * lq + e, col = c0 + 16 * n + lr;
         S[r][u][e] = a.h0 ? a.h0[sbase + (size_t)i * a.d_v + col] : 0.f;
+        if constexpr (kMom) Z[r][u][e] = a.z0 ? a.z0[sbase + (size_t)i * a.d_v + col] : 0.f;
       }
       sT.put4(16 * n + lr, i0 + 4 * lq, S[r][u]);
     }
@@ -464,12 +473,37 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[r][u][e] *= g[e];
       }
+      if constexpr (kMom) {
+        // Delta S_c in its own accumulator; Z = mu kappa_c Z + Delta S_c; S += Z
+        const float mk = __builtin_signbit(gm[r]) ? 0.f : a.momentum;
+        f32x4 D[SJ::TPW];
 #pragma unroll
-      for (int s = 0; s < CSTEPS; ++s) {
+        for (int u = 0; u < SJ::TPW; ++u) D[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < CSTEPS; ++s) {
+#pragma unroll
+          for (int u = 0; u < SJ::TPW; ++u) {
+            const int n = SJ::tile(w, u);
+            if (SJ::kAllTiles || n < NT) mma(D[u], fkh[r][s], eT.get_hi(16 * n + lr, 32 * s + 8 * lq));
+          }
+        }
 #pragma unroll
         for (int u = 0; u < SJ::TPW; ++u) {
-          const int n = SJ::tile(w, u);
-          if (SJ::kAllTiles || n < NT) mma(S[r][u], fkh[r][s], eT.get_hi(16 * n + lr, 32 * s + 8 * lq));
+          if (!SJ::kAllTiles && SJ::tile(w, u) >= NT) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            Z[r][u][e] = mk * Z[r][u][e] + D[u][e];
+            S[r][u][e] += Z[r][u][e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < CSTEPS; ++s) {
+#pragma unroll
+          for (int u = 0; u < SJ::TPW; ++u) {
+            const int n = SJ::tile(w, u);
+            if (SJ::kAllTiles || n < NT) mma(S[r][u], fkh[r][s], eT.get_hi(16 * n + lr, 32 * s + 8 * lq));
+          }
         }
       }
 #pragma unroll
@@ -510,6 +544,22 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
       }
     }
   }
+  if (kMom && a.zT) {
+#pragma unroll
+    for (int r = 0; r < SJ::RPW; ++r) {
+      const int i0 = 16 * SJ::blk(w, r);
+#pragma unroll
+      for (int u = 0; u < SJ::TPW; ++u) {
+        const int n = SJ::tile(w, u);
+        if (n >= NT) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + 4 * lq + e, col = c0 + 16 * n + lr;
+          a.zT[sbase + (size_t)i * a.d_v + col] = Z[r][u][e];
+        }
+      }
+    }
+  }
 }
 
 static size_t scan_lds_bytes(int C, int d_k, int BV, int fb) {
@@ -540,7 +590,8 @@ int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16) {
 template <typename TIn, typename TOut, class P, int C, int DK, int BV>
 static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream) {
   const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024>::total;
-  auto kern = scan_kernel<TIn, TOut, P, C, DK, BV>;
+  auto kern = a.momentum != 0.f ? scan_kernel<TIn, TOut, P, C, DK, BV, true>
+                                : scan_kernel<TIn, TOut, P, C, DK, BV, false>;
   hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
   if (e != hipSuccess) return e;
   dim3 grid((a.d_v / BV) * a.H_v * a.B);

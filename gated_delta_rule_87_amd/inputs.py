@@ -133,6 +133,25 @@ def make_inputs(w: Workload, seed=None, T=None, B=None):
     }
 
 
+def make_resets(B, T, mean_doc_len, seed, extra=()):
+    """Document starts for packed sequences: uint8 [B, T], 1 where a token
+    starts a new document.  Document lengths are drawn from a geometric
+    distribution with the given mean (numpy Generator(PCG64(seed))); ``extra``
+    lists (b, t) positions that are also marked (to place starts on chunk
+    edges, on token 0 or twice in one 16-token block)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    r = np.zeros((B, T), np.uint8)
+    for b in range(B):
+        t = int(rng.geometric(1.0 / mean_doc_len))
+        while t < T:
+            r[b, t] = 1
+            t += int(rng.geometric(1.0 / mean_doc_len))
+    for b, t in extra:
+        if 0 <= t < T:
+            r[b, t] = 1
+    return r
+
+
 def decoded(inputs):
     """All five arrays as fp32 (exact decode)."""
     return {name: decode(a) for name, a in inputs.items()}

@@ -187,6 +187,59 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_problem *p, const void *q, const void
                                  float *hT, void *stream);
 
 /*
+ * Layer options of the chunk path: the sequence-level features of the
+ * Systolic Linear Attention layer (Table 2, the symbols Z_c, mu and kappa_c;
+ * section 2.3, "Why chunk-level momentum").
+ *   reset    : NULL, or DEVICE bytes [B, T]; nonzero marks a token that starts
+ *              a new document: the state carried into it is discarded
+ *              (S_{t-1} <- 0 before its step).  Packed documents of any
+ *              lengths therefore share one row of the batch.
+ *   momentum : mu of the chunk-boundary momentum; 0 turns it off (z0 and zT
+ *              are then ignored).  With mu != 0, over chunks of `chunk`
+ *              tokens counted from each sequence's first token (the last may
+ *              be shorter), with S~_c the state after chunk c's last token
+ *              (evolved token by token from S_{c-1}; the chunk's outputs are
+ *              read from that evolution), F_c the product of the chunk's
+ *              decays and kappa_c = 0 when a reset falls in the chunk:
+ *                carry = kappa_c F_c S_{c-1},
+ *                Z_c = mu kappa_c Z_{c-1} + (S~_c - carry),  S_c = carry + Z_c.
+ *              The result depends on where chunks start: a sequence split
+ *              across calls must be split at a multiple of `chunk`.
+ *   z0, zT   : momentum buffer in / out, fp32 [B, H_v, d_k, d_v] like h0 / hT;
+ *              NULL z0 = zero, NULL zT = not written; zT may alias z0.
+ */
+typedef struct {
+  const uint8_t *reset;
+  float momentum;
+  const float *z0;
+  float *zT;
+} gdr_layer_opts;
+
+/*
+ * gdr_chunk_fwd with layer options (opts NULL = gdr_chunk_fwd).  The
+ * prepared chunks of a chunk holding a reset are formed entry by entry on
+ * the block-pivot route: pairs of tokens from different documents get no
+ * decay factor, the rows of Kbar and Qbar after the chunk's first reset and
+ * the rows of Khat before its last one are zero, and region GM holds -0 in
+ * every channel.  Other arguments, results and errors as for gdr_chunk_fwd;
+ * a non-finite momentum is GDR_ERR_INVALID_ARG.
+ */
+gdr_status gdr_chunk_fwd_ex(const gdr_problem *p, const gdr_layer_opts *opts, const void *q, const void *k,
+                            const void *v, const void *beta, const void *log_alpha, const float *h0,
+                            void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Output epilogue of the same layer (section 2.3, token-level recurrence
+ * box): per (batch, token, value head) row of d_v entries,
+ *     y = sigmoid(z) (.) o / sqrt(mean(o^2) + eps) (.) weight,
+ * o and y of p->out_dtype, z of p->in_dtype, all [B, T, H_v, d_v]; weight
+ * fp32 [d_v] or NULL (= 1); eps >= 0.  y may alias o.  The pages fix
+ * neither eps nor a scale vector: both are the caller's.
+ */
+gdr_status gdr_gated_rmsnorm(const gdr_problem *p, const void *o, const void *z, const float *weight,
+                             float eps, void *y, void *stream);
+
+/*
  * Token recurrence, p->T tokens in order (Systolic Linear Attention, section
  * 2.1, Eq. (2)), updating `state` in place (fp32 [B,H_v,d_k,d_v], read and
  * written) and writing o [B,T,H_v,d_v].  chunk / solve fields are ignored.
