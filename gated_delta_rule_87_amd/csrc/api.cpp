@@ -116,7 +116,10 @@ gdr_status check_ptr(const void *ptr, const char *name, bool required, uintptr_t
 gdr::WsLayout layout_of(const gdr_problem *p) {
   const int nc = (int)(((size_t)p->T + p->chunk - 1) / p->chunk);
   const int hb = p->beta_per_key_head ? p->H_k : p->H_v;
-  return gdr::ws_layout(p->B, p->H_k, hb, nc, p->chunk, p->d_k, p->in_dtype == GDR_BF16);
+  gdr::WsLayout w = gdr::ws_layout(p->B, p->H_k, hb, nc, p->chunk, p->d_k, p->in_dtype == GDR_BF16);
+  w.seg_bytes = gdr::scan_seg_bytes(p->B, p->H_v, nc, p->d_k, p->d_v);
+  w.total = w.seg_off + ((w.seg_bytes + 255) & ~(size_t)255);
+  return w;
 }
 
 size_t ws_bytes(const gdr_problem *p) { return layout_of(p).total; }

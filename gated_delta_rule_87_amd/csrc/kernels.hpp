@@ -19,6 +19,7 @@ namespace gdr {
 struct WsLayout {
   size_t tile[6];   // bytes per tile, in region order
   size_t off[6];    // region offsets
+  size_t seg_off, seg_bytes;   // the segment-parallel scan's region (0 bytes when not used)
   size_t total;
 };
 enum WsRegion { kWsA = 0, kWsL, kWsKB, kWsQB, kWsKH, kWsGM };
@@ -39,6 +40,8 @@ __host__ __device__ inline WsLayout ws_layout(int B, int H_k, int H_beta, int N_
     at += (size_t)B * heads * N_c * w.tile[r];
     at = (at + 255) & ~(size_t)255;
   }
+  w.seg_off = at;
+  w.seg_bytes = 0;
   w.total = at;
   return w;
 }
@@ -61,6 +64,12 @@ struct ChunkArgs {
   float momentum;
   const float *z0;
   float *zT;
+  // Segment-parallel scan: chunks per segment (0 = one segment); the scan's
+  // h0 of segment y (blockIdx.y) is h0 + y * h0_seg_stride; the transfer pass
+  // writes [J | B] per segment to xfer.
+  int seg_len;
+  size_t h0_seg_stride;
+  float *xfer;
 };
 
 // Tile of region r for (batch b, head, chunk c).
@@ -108,6 +117,10 @@ hipError_t allow_full_lds(const void *kernel);
 // Whether a shape is compiled in (the API layer reports GDR_ERR_UNSUPPORTED otherwise).
 bool prep_supported(int C, int d_k, int G);
 int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16);
+// Segments of the segment-parallel scan (1 = one scan over the whole
+// sequence) and the bytes of its workspace region.
+int scan_segments(int B, int H_v, int N_c, int d_v);
+size_t scan_seg_bytes(int B, int H_v, int N_c, int d_k, int d_v);
 size_t prep_lds_bytes(int C, int d_k, int G);
 
 }  // namespace gdr

@@ -858,12 +858,14 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   // chunk's end (Khat rows), and pairs of different segments are zero.  Every
   // mask is a select, so an infinite factor of a pair across a reset (whose
   // Lambda values belong to different documents) never reaches a kept entry.
-  const int seg_last = x.seg[C - 1];
+  const bool resets = a.reset != nullptr;             // uniform: without resets no segment is read
+  const int seg_last = resets ? x.seg[C - 1] : 0;
+  auto same_doc = [&](int r_, int c_) { return !resets || x.seg[r_] == x.seg[c_]; };
   for (int r = 0; r < NR; ++r) {
     const int I = own(r);
     const int tr = 16 * I + lr, piv = 16 * I;
     const float mt = (t0 + tr < T) ? 1.f : 0.f;
-    const bool sees_entry = x.seg[tr] == 0, carries = x.seg[tr] == seg_last;
+    const bool sees_entry = !resets || x.seg[tr] == 0, carries = !resets || x.seg[tr] == seg_last;
     Split ak[KS], aq[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -923,7 +925,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
         for (int q4 = 0; q4 < 4; ++q4) {
           const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
           float sg = 0.f, sl = 0.f;
-          if (row >= col && t0 + row < T && x.seg[row] == x.seg[col]) {
+          if (row >= col && t0 + row < T && same_doc(row, col)) {
             const size_t rrow = x.tok(row) * x.row_stride, rcol = x.tok(col) * x.row_stride;
             for (int ch = 0; ch < DK; ++ch) {
               const int g = ch >> x.gs;
@@ -940,7 +942,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int row = 16 * I + 4 * lq + q4, col = 16 * J + lr;
-        const bool same = x.seg[row] == x.seg[col];
+        const bool same = same_doc(row, col);
         gmat[row * (C + 4) + col] = ((I > J || row > col) && same) ? accG[q4] : 0.f;
         accL[q4] = same ? accL[q4] : 0.f;
       }

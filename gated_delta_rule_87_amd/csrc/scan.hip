@@ -73,7 +73,9 @@ __device__ __forceinline__ int tri_index(int I, int s) {
 }
 
 // FB: bytes of one 16 x 32 operand block in the workspace (fp16 1 KiB, fp32 2 KiB).
-template <int C, int DK, int BV, int FB>
+// XF: the transfer pass of the segment-parallel scan, which stages no output
+// and no L_c blocks.
+template <int C, int DK, int BV, int FB, bool XF = false>
 struct ScanLayout {
   static constexpr int S_LD = DK + 8;   // S^T rows (elements), 16-byte pad per bf16 plane
   static constexpr int Y_LD = C + 8;    // Y^T, E^T rows
@@ -88,8 +90,9 @@ struct ScanLayout {
   static constexpr size_t st_bytes = (size_t)C * (4 * BV + 16);
   // nonzero blocks of diag(beta) A_c, then of L_c, each followed by one zero block
   static constexpr int NZ = tri_blocks(C / 16);
-  static constexpr size_t al_bytes = 2 * (size_t)(NZ + 1) * FB;
-  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes + 2 * st_bytes + al_bytes;
+  static constexpr int NREG = XF ? 1 : 2;     // staged lower-triangular operands: A (and L)
+  static constexpr size_t al_bytes = NREG * (size_t)(NZ + 1) * FB;
+  static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes + (XF ? 1 : 2) * st_bytes + al_bytes;
 };
 
 // One thread's share when all 64 * kScanWaves threads move a row-major C x BV
@@ -136,10 +139,15 @@ __device__ __forceinline__ T *at(T *base, unsigned off) {
   return reinterpret_cast<T *>(reinterpret_cast<B *>(base) + off * (unsigned)sizeof(T));
 }
 
-template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom>
+// kXfer: the transfer pass of the segment-parallel scan.  Its columns are
+// the d_k columns of the segment's transition J (value input 0, initial
+// state the identity) followed by the d_v columns of its offset B (the real
+// values, initial state 0); it writes [J | B] and no output.
+template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom, bool kXfer = false>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
+  static_assert(!(kMom && kXfer), "momentum doubles the carried state: no transfer pass");
   constexpr int FB = P::kF32 ? 2048 : 1024;
-  using Lay = ScanLayout<C, DK, BV, FB>;
+  using Lay = ScanLayout<C, DK, BV, FB, kXfer>;
   using IO = TileIO<P>;
   using Plain = typename P::Plain;
   constexpr int NB = C / 16;                  // token row blocks
@@ -170,10 +178,17 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   // receives a contiguous range of (head, tile) units puts the d_v / BV tiles
   // of one head, which read the same operand tiles, on one XCD and so behind
   // one L2.
-  const int NX = a.d_v / BV;
+  const int NX = (kXfer ? DK + a.d_v : a.d_v) / BV;
   int unit = blockIdx.x;
   if (gridDim.x % kXcds == 0) unit = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
   const int c0 = (unit % NX) * BV, hv = (unit / NX) % a.H_v, b = unit / (NX * a.H_v);
+  const bool jcols = kXfer && c0 < DK;        // transfer pass: columns of J (no value input)
+  const int vc0 = kXfer ? c0 - DK : c0;       // first value column of the tile
+  // Segment of the sequence (blockIdx.y): chunks [cb, ce).  One segment (the
+  // whole sequence) unless the segment-parallel scan split it.
+  const int sgi = blockIdx.y;
+  const int cb = a.seg_len ? min(sgi * a.seg_len, a.N_c) : 0;
+  const int ce = a.seg_len ? min(cb + a.seg_len, a.N_c) : a.N_c;
   const int R = a.H_v / a.H_k;
   const int hk = hv / R;
   const int hb = a.beta_per_key_head ? hk : hv;
@@ -188,7 +203,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   using OS = RowSegs<C, BV, (int)sizeof(TOut)>;
   unsigned char *vst = smem_raw + Lay::s_bytes + 2 * Lay::y_bytes + Lay::x_bytes;   // v_c, row-major
   unsigned char *ost = vst + Lay::st_bytes;                                           // o_c, row-major
-  unsigned char *alA = ost + Lay::st_bytes;                                           // diag(beta) A_c blocks
+  unsigned char *alA = ost + (kXfer ? 0 : Lay::st_bytes);                             // diag(beta) A_c blocks
   unsigned char *alL = alA + (Lay::NZ + 1) * FB;                                      // L_c blocks
   const int tid = threadIdx.x;
   // LDS block of (I, s): its compacted position, or the zero block
@@ -201,6 +216,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   auto row_ok = [&](int c, int t) { return c * C + t < T; };
   auto at_chunk = [&](auto *p, int row, int c) { return p + ((size_t)b * T + (size_t)c * C) * (size_t)row; };
   auto crow = [&](int c, int t) { return (unsigned)min(t, T - 1 - c * C); };   // clamped token row in chunk c
+  auto last = [&](int c) { return min(c, ce - 1); };                            // prefetch index, clamped to the segment
   auto tile = [&](int r, int heads, int head, int c) -> const void * { return ws_tile(a, r, heads, head, b, c); };
 
   // ---------------------------------------------------- prefetch registers
@@ -218,11 +234,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   // by all threads in pieces of AW bytes (piece p at byte AW p of the A
   // blocks followed by the L blocks) during chunk c-1 and staged in LDS in
   // the Y phase of chunk c, where no wave reads either.
-  constexpr int AL_BYTES = 2 * Lay::NZ * FB / (64 * kScanWaves);
-  constexpr int AW = AL_BYTES % 16 == 0 ? 16 : 8;
+  constexpr int AL_BYTES = Lay::NREG * Lay::NZ * FB / (64 * kScanWaves);
+  constexpr int AW = AL_BYTES % 16 == 0 ? 16 : AL_BYTES % 8 == 0 ? 8 : 4;
   constexpr int ANREP = AL_BYTES / AW;
   static_assert(AL_BYTES % AW == 0 && FB % AW == 0, "operand block pieces");
-  using AVec = typename std::conditional<AW == 8, u32x2, u32x4>::type;
+  using AVec = typename std::conditional<AW == 4, unsigned,
+               typename std::conditional<AW == 8, u32x2, u32x4>::type>::type;
   AVec alseg[ANREP];
   unsigned al_src[ANREP], al_dst[ANREP];   // byte offsets in the chunk's A or L tile / in LDS
   bool al_isl[ANREP];
@@ -248,7 +265,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
       for (int s = 0; s < YKS; ++s) {
         fkb[r][s] = IO::get_plain(tkb, I * KSTEPS + yh * YKS + s, l);
-        fqb[r][s] = IO::get_plain(tqb, I * KSTEPS + yh * YKS + s, l);
+        if constexpr (!kXfer) fqb[r][s] = IO::get_plain(tqb, I * KSTEPS + yh * YKS + s, l);
       }
     }
   };
@@ -258,8 +275,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
     for (int k = 0; k < VS::NREP; ++k) {
       const int t = VS::row(tid, k);
-      dst[k] = *reinterpret_cast<const typename VS::Vec *>(
-          at(at_chunk(vp, v_row, c), crow(c, t) * v_row + hv * a.d_v + c0 + VS::colb(tid, k) / (int)sizeof(TIn)));
+      if (jcols) {
+        dst[k] = typename VS::Vec{};
+      } else {
+        dst[k] = *reinterpret_cast<const typename VS::Vec *>(
+            at(at_chunk(vp, v_row, c), crow(c, t) * v_row + hv * a.d_v + vc0 + VS::colb(tid, k) / (int)sizeof(TIn)));
+      }
     }
   };
   auto put_v = [&]() __attribute__((always_inline)) {
@@ -320,7 +341,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = i0 + 4 * lq + e, col = c0 + 16 * n + lr;
-        S[r][u][e] = a.h0 ? a.h0[sbase + (size_t)i * a.d_v + col] : 0.f;
+        if constexpr (kXfer) {
+          S[r][u][e] = (jcols && i == col) ? 1.f : 0.f;   // [I | 0]
+        } else {
+          S[r][u][e] = a.h0 ? a.h0[(size_t)sgi * a.h0_seg_stride + sbase + (size_t)i * a.d_v + col] : 0.f;
+        }
         if constexpr (kMom) Z[r][u][e] = a.z0 ? a.z0[sbase + (size_t)i * a.d_v + col] : 0.f;
       }
       sT.put4(16 * n + lr, i0 + 4 * lq, S[r][u]);
@@ -331,12 +356,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     reinterpret_cast<u32x4 *>(alA + Lay::NZ * FB)[i] = u32x4{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4 *>(alL + Lay::NZ * FB)[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  if (a.N_c > 0) {
-    load_y(0);
-    load_v(vseg, 0);
-    load_v(vnext, min(1, a.N_c - 1));
-    load_al(0);
-    load_s(0);
+  if (ce > cb) {
+    load_y(cb);
+    load_v(vseg, cb);
+    load_v(vnext, last(cb + 1));
+    load_al(cb);
+    load_s(cb);
     put_v();
   }
   __syncthreads();
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   // final, possibly ragged chunk masks v and guards its output stores.
   auto step = [&](int c, auto tail_tag) __attribute__((always_inline)) {
     constexpr bool kTail = decltype(tail_tag)::value;
-    const int c1 = min(c + 1, a.N_c - 1);
+    const int c1 = last(c + 1);
 
     // ---- Y = V - Kbar S, and Qbar S
     f32x4 accO[J::RPW][J::TPW];
@@ -365,7 +390,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
           if (!(YS == 2 || J::kAllTiles) && n >= NT) continue;
           const auto fs = sT.get(16 * n + lr, 32 * (yh * YKS + s) + 8 * lq);
           mma(accY[u], fkb[r][s], fs);
-          mma(accQ[u], fqb[r][s], fs);
+          if constexpr (!kXfer) mma(accQ[u], fqb[r][s], fs);
         }
       }
       if constexpr (YS == 2 && NT == 2) {
@@ -377,7 +402,25 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         const f32x4 *take = xch + ((I * NT + yh) * 2) * 64;
         accY[0] += take[l];
         accQ[0] += take[64 + l];
+      } else if constexpr (YS == 2 && NT == 4) {
+        // accumulator u holds tile (yh + u) % 4; this wave owns tiles yh and
+        // yh + 2 (accumulators 0 and 2) and hands accumulators 1 and 3 to
+        // the partner, then keeps its own two in accumulators 0 and 1
+#pragma unroll
+        for (int u = 1; u < NT; u += 2) {
+          f32x4 *give = xch + ((I * NT + (yh + u) % NT) * 2) * 64;
+          give[l] = accY[u];
+          give[64 + l] = accQ[u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NT; u += 2) {
+          const f32x4 *take = xch + ((I * NT + yh + u) * 2) * 64;
+          accY[u / 2] = accY[u] + take[l];
+          accQ[u / 2] = accQ[u] + take[64 + l];
+        }
       } else if constexpr (YS == 2) {
+        static_assert(NT == 1, "channel split for 1, 2 or 4 column tiles");
         // one tile: the yh = 1 wave only contributes its partials
         f32x4 *slot = xch + (I * NT * 2) * 64;
         if (yh == 1) {
@@ -406,7 +449,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     load_y(c1);
 #pragma unroll
     for (int k = 0; k < VS::NREP; ++k) vseg[k] = vnext[k];
-    load_v(vnext, min(c + 2, a.N_c - 1));
+    load_v(vnext, last(c + 2));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);          // keep each phase's work (and waits) in its phase
 
@@ -438,7 +481,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
 
     // ---- O = Qbar S + L E (staged in LDS; stored after the chunk's last barrier)
 #pragma unroll
-    for (int r = 0; r < J::RPW; ++r) {
+    for (int r = 0; r < (kXfer ? 0 : J::RPW); ++r) {
       const int I = J::blk(w, r);
 #pragma unroll
       for (int s = 0; s < CSTEPS; ++s) {        // all steps: blocks above the diagonal read the zero block
@@ -516,19 +559,36 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     put_v();                                    // v_{c+1}: the Y phase above was the last reader of v_c
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    store_o(c, tail_tag);                       // the next O phase rewrites the staging after two barriers
+    if constexpr (!kXfer) store_o(c, tail_tag);   // the next O phase rewrites the staging after two barriers
   };
   // The first chunk is peeled so the loop is entered from an iteration with
   // the same memory-instruction order as its own back edge: the compiler's
   // wait counts at the loop head then allow the whole next-chunk prefetch to
   // stay in flight.
-  if (a.N_c > 1) {
-    step(0, std::integral_constant<bool, false>());
-    for (int c = 1; c + 1 < a.N_c; ++c) step(c, std::integral_constant<bool, false>());
+  if (ce - cb > 1) {
+    step(cb, std::integral_constant<bool, false>());
+    for (int c = cb + 1; c + 1 < ce; ++c) step(c, std::integral_constant<bool, false>());
   }
-  if (a.N_c > 0) step(a.N_c - 1, std::integral_constant<bool, true>());
+  if (ce > cb) step(ce - 1, std::integral_constant<bool, true>());
 
-  if (a.hT) {
+  if constexpr (kXfer) {
+    // [J | B] of this segment: [B][H_v][d_k][d_k + d_v] per segment
+    const int W = DK + a.d_v;
+    float *xo = a.xfer + (size_t)sgi * ((size_t)a.B * a.H_v * DK * W) + ((size_t)b * a.H_v + hv) * DK * W;
+#pragma unroll
+    for (int r = 0; r < SJ::RPW; ++r) {
+      const int i0 = 16 * SJ::blk(w, r);
+#pragma unroll
+      for (int u = 0; u < SJ::TPW; ++u) {
+        const int n = SJ::tile(w, u);
+        if (n >= NT) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[(size_t)(i0 + 4 * lq + e) * W + c0 + 16 * n + lr] = S[r][u][e];
+      }
+    }
+    return;
+  }
+  if (a.hT && sgi == (int)gridDim.y - 1) {
 #pragma unroll
     for (int r = 0; r < SJ::RPW; ++r) {
       const int i0 = 16 * SJ::blk(w, r);
@@ -587,20 +647,166 @@ int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16) {
   return fit16 ? 16 : 0;
 }
 
+// ------------------------------------------------ segment-parallel scan
+// When the (batch, value head, 32-column tile) units cannot fill the GPU
+// (fewer than 256), the sequence is cut into P segments of L chunks that are
+// scanned at the same time (Systolic Linear Attention, section 3.3: a
+// chunk's state update is an affine map S -> J S + B, and maps compose).
+//   1. Transfer pass (scan_kernel, kXfer): segments 0 .. P-2 each scan the
+//      columns [J | B] of their own map from [I | 0], without output.
+//   2. Combine (seg_combine_kernel): S_in(0) = h0, S_in(p+1) = J_p S_in(p) + B_p.
+//   3. The ordinary scan of all P segments at once, segment p from S_in(p),
+//      writing o; the last one writes hT.
+// Momentum doubles the carried state (S and Z), so it keeps one segment.
+// The transfer columns cost about (d_k + d_v) / d_v of a scan without its
+// output phase, so splitting pays only when it adds CUs.
+int scan_segments(int B, int H_v, int N_c, int d_v) {
+  if (d_v % 32 != 0) return 1;
+  const long units = (long)B * H_v * (d_v / 32);
+  if (units >= 256) return 1;
+  int P = (int)(256 / units);
+  P = P < 16 ? P : 16;
+  P = P < N_c / 8 ? P : N_c / 8;              // at least 8 chunks per segment
+  return P >= 2 ? P : 1;
+}
+
+size_t scan_seg_bytes(int B, int H_v, int N_c, int d_k, int d_v) {
+  const int P = scan_segments(B, H_v, N_c, d_v);
+  if (P < 2) return 0;
+  const size_t unit = (size_t)B * H_v * d_k;
+  return 4 * ((size_t)(P - 1) * unit * (d_k + d_v) + (size_t)P * unit * d_v);   // [J | B] per segment, S_in per segment
+}
+
+// S_in of every segment for one (batch, value head, 32-column tile):
+// S_in(0) = h0 (or 0), S_in(p + 1) = J_p S_in(p) + B_p, in fp32.  The kernel
+// is a chain of P - 1 dependent steps, so its time is load latency, not
+// arithmetic: 256 threads each own RT = d_k / 32 rows and 4 columns (column
+// group t % 8) and read their rows of J_p with 32 loads in flight per slab.
+// (One row per thread, 8 d_k threads, reads S from LDS RT times as often and
+// measured slower.)
+template <int DK>
+constexpr int combine_threads() { return 256; }
+template <int DK>
+__global__ __launch_bounds__(combine_threads<DK>()) void seg_combine_kernel(ChunkArgs a, int P, float *xstate) {
+  constexpr int NTH = combine_threads<DK>();
+  constexpr int RT = DK * 8 / NTH;            // rows per thread
+  constexpr int QW = 32 / RT < DK / 4 ? 32 / RT : DK / 4;   // float4 per row and slab
+  constexpr int NSLAB = DK / (4 * QW);
+  static_assert(NSLAB >= 1 && NSLAB * 4 * QW == DK, "slabs cover the rows of J");
+  __shared__ float4 sh[DK][8];                // S_in(p), [DK][32]
+  const int tid = threadIdx.x, tc = tid & 7, tr = tid >> 3;
+  const int c0 = blockIdx.x * 32, hv = blockIdx.y, b = blockIdx.z;
+  const int W = DK + a.d_v;
+  const size_t unit = (size_t)b * a.H_v + hv;
+  const size_t slot = (size_t)a.B * a.H_v * DK * a.d_v;           // elements of one segment's states
+  float *xs0 = xstate + unit * DK * a.d_v + c0;
+  for (int i = tid; i < DK * 8; i += NTH) {
+    const int r = i >> 3, q = i & 7;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.h0) v = *reinterpret_cast<const float4 *>(a.h0 + unit * DK * a.d_v + (size_t)r * a.d_v + c0 + 4 * q);
+    sh[r][q] = v;
+    *reinterpret_cast<float4 *>(xs0 + (size_t)r * a.d_v + 4 * q) = v;
+  }
+  __syncthreads();
+  for (int p = 0; p + 1 < P; ++p) {
+    const float *xo = a.xfer + (size_t)p * a.B * a.H_v * DK * W + unit * DK * W + (size_t)(tr * RT) * W;
+    float4 acc[RT];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) acc[j] = *reinterpret_cast<const float4 *>(xo + (size_t)j * W + DK + c0 + 4 * tc);
+#pragma unroll
+    for (int sl = 0; sl < NSLAB; ++sl) {
+      float4 jr[RT][QW];                      // rows of J_p, columns 4 QW sl ..
+#pragma unroll
+      for (int j = 0; j < RT; ++j) {
+#pragma unroll
+        for (int q = 0; q < QW; ++q)
+          jr[j][q] = *reinterpret_cast<const float4 *>(xo + (size_t)j * W + 4 * (QW * sl + q));
+      }
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        const int k = 4 * (QW * sl + q);
+        const float4 s0 = sh[k][tc], s1 = sh[k + 1][tc], s2 = sh[k + 2][tc], s3 = sh[k + 3][tc];
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+          const float4 m = jr[j][q];
+          acc[j].x += m.x * s0.x + m.y * s1.x + m.z * s2.x + m.w * s3.x;
+          acc[j].y += m.x * s0.y + m.y * s1.y + m.z * s2.y + m.w * s3.y;
+          acc[j].z += m.x * s0.z + m.y * s1.z + m.z * s2.z + m.w * s3.z;
+          acc[j].w += m.x * s0.w + m.y * s1.w + m.z * s2.w + m.w * s3.w;
+        }
+      }
+    }
+    __syncthreads();                          // every thread has read S_in(p)
+    float *xs = xs0 + (size_t)(p + 1) * slot;
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      sh[tr * RT + j][tc] = acc[j];
+      *reinterpret_cast<float4 *>(xs + (size_t)(tr * RT + j) * a.d_v + 4 * tc) = acc[j];
+    }
+    __syncthreads();
+  }
+}
+
 template <typename TIn, typename TOut, class P, int C, int DK, int BV>
-static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream) {
+static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream, int segments = 1) {
   const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024>::total;
   auto kern = a.momentum != 0.f ? scan_kernel<TIn, TOut, P, C, DK, BV, true>
                                 : scan_kernel<TIn, TOut, P, C, DK, BV, false>;
   hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
   if (e != hipSuccess) return e;
-  dim3 grid((a.d_v / BV) * a.H_v * a.B);
+  dim3 grid((a.d_v / BV) * a.H_v * a.B, segments);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut, class P, int C, int DK, int BV>
+static hipError_t launch_xfer_t(const ChunkArgs &a, hipStream_t stream, int segments) {
+  const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024, true>::total;
+  auto kern = scan_kernel<TIn, TOut, P, C, DK, BV, false, true>;
+  hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
+  if (e != hipSuccess) return e;
+  dim3 grid(((DK + a.d_v) / BV) * a.H_v * a.B, segments);
   hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), lds, stream, a);
   return hipGetLastError();
 }
 
 template <typename TIn, typename TOut, class P, int C, int DK>
+static hipError_t launch_segmented(const ChunkArgs &a, hipStream_t s, int segments) {
+  constexpr int FB = P::kF32 ? 2048 : 1024;
+  const int L = (a.N_c + segments - 1) / segments;
+  segments = (a.N_c + L - 1) / L;
+  float *seg = reinterpret_cast<float *>(a.ws + a.wl.seg_off);
+  const size_t unit = (size_t)a.B * a.H_v * DK;
+  float *xstate = seg + (size_t)(segments - 1) * unit * (DK + a.d_v);
+  ChunkArgs ax = a;
+  ax.seg_len = L;
+  ax.xfer = seg;
+  hipError_t e;
+  // transfer pass over segments 0 .. P-2: 64-column tiles where the lean
+  // layout fits the CU's LDS (fewer workgroups stream the same operands)
+  constexpr bool k64 = ScanLayout<C, DK, 64, FB, true>::total <= 160 * 1024;
+  if (k64 && (DK + a.d_v) % 64 == 0) {
+    e = launch_xfer_t<TIn, TOut, P, C, DK, k64 ? 64 : 32>(ax, s, segments - 1);
+  } else {
+    e = launch_xfer_t<TIn, TOut, P, C, DK, 32>(ax, s, segments - 1);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_combine_kernel<DK>, dim3(a.d_v / 32, a.H_v, a.B), dim3(combine_threads<DK>()), 0, s, ax,
+                     segments, xstate);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  ChunkArgs ac = a;
+  ac.seg_len = L;
+  ac.h0 = xstate;
+  ac.h0_seg_stride = unit * a.d_v;
+  return launch_scan_t<TIn, TOut, P, C, DK, 32>(ac, s, segments);
+}
+
+template <typename TIn, typename TOut, class P, int C, int DK>
 static hipError_t launch_scan_bv(const ChunkArgs &a, hipStream_t s) {
+  const int segments = a.momentum != 0.f ? 1 : scan_segments(a.B, a.H_v, a.N_c, a.d_v);
+  if (segments > 1 && a.wl.seg_bytes >= scan_seg_bytes(a.B, a.H_v, a.N_c, DK, a.d_v) &&
+      scan_lds_bytes(C, DK, 32, P::kF32 ? 2048 : 1024) <= 160 * 1024)
+    return launch_segmented<TIn, TOut, P, C, DK>(a, s, segments);
   const int bv = scan_choose_bv(a.B, a.H_v, C, DK, a.d_v, sizeof(TIn) == 2);
   if (bv == 32) return launch_scan_t<TIn, TOut, P, C, DK, 32>(a, s);
   if (bv == 16) return launch_scan_t<TIn, TOut, P, C, DK, 16>(a, s);

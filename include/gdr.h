@@ -111,6 +111,13 @@ typedef struct {
  * (columns of KH) of a short final chunk past T are zero and its gate values
  * are those of its last real token.  Region
  * offsets: gdr_chunk_workspace_layout.
+ * When the (batch, value head, 32 value columns) units number fewer than
+ * 256, d_v is a multiple of 32 and there are at least 16 chunks, the scan is
+ * split into P segments of the sequence scanned at once (the affine chunk
+ * map of section 3.3 composed across segments) and the workspace ends with
+ * one more region, after GM at a 256-byte boundary, of
+ * 4 B H_v d_k ((P - 1)(d_k + d_v) + P d_v) bytes: each segment's transition
+ * [J | B] and entry state.  The total size includes it.
  */
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p);
 
