@@ -19,7 +19,9 @@ GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
 
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_workspace_layout", "gdr_chunk_prepare",
            "gdr_chunk_scan", "gdr_chunk_fwd_noalloc", "gdr_chunk_fwd_ex", "gdr_gated_rmsnorm", "gdr_recurrent_step",
+           "gdr_verify", "gdr_recurrent_step_ex", "gdr_state_quantize", "gdr_state_dequantize",
            "gdr_status_string", "gdr_last_error")
+GDR_STATE_F32, GDR_STATE_E4M3 = 0, 1
 NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
 # Workspace regions, in order (include/gdr.h, gdr_chunk_fwd_workspace_size).
 WS_REGIONS = ("A", "L", "KB", "QB", "KH", "GM")
@@ -34,6 +36,11 @@ class GdrProblem(ctypes.Structure):
 class GdrLayerOpts(ctypes.Structure):
     _fields_ = [("reset", ctypes.c_void_p), ("momentum", ctypes.c_float), ("z0", ctypes.c_void_p),
                 ("zT", ctypes.c_void_p)]
+
+
+class GdrStepOpts(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_void_p), ("reset", ctypes.c_void_p), ("state_format", ctypes.c_int32),
+                ("state_scale", ctypes.c_void_p)]
 
 
 class GdrError(RuntimeError):
@@ -73,6 +80,14 @@ def load():
         lib.gdr_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdr_recurrent_step.restype = ctypes.c_int
         lib.gdr_recurrent_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_verify.restype = ctypes.c_int
+        lib.gdr_verify.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_recurrent_step_ex.restype = ctypes.c_int
+        lib.gdr_recurrent_step_ex.argtypes = [P, ctypes.POINTER(GdrStepOpts), vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdr_state_quantize.restype = ctypes.c_int
+        lib.gdr_state_quantize.argtypes = [P, vp, vp, vp, vp]
+        lib.gdr_state_dequantize.restype = ctypes.c_int
+        lib.gdr_state_dequantize.argtypes = [P, vp, vp, vp, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
@@ -337,3 +352,80 @@ def gdr_recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float
         _ptr(state, "state", torch.float32, (p.B, p.H_v, p.d_k, p.d_v)),
         _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _stream(stream)))
     return o
+
+
+def gdr_verify(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None, stream=None):
+    """Outputs of T <= 16 drafted tokens read from ``state`` (fp32
+    [B, H_v, d_k, d_v], not modified).  Returns o [B, T, H_v, d_v]."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, out_dtype=out_dtype)
+    if o is None:
+        o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=q.device)
+    _check(lib.gdr_verify(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
+        _ptr(state, "state", torch.float32, (p.B, p.H_v, p.d_k, p.d_v)),
+        _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _stream(stream)))
+    return o
+
+
+def gdr_recurrent_step_ex(q, k, v, beta, log_alpha, state, *, n_tokens=None, reset=None, state_scale=None,
+                          out_dtype=torch.float32, o=None, stream=None):
+    """gdr_recurrent_step with per-sequence token counts ``n_tokens`` (int32
+    [B]), document ``reset`` flags (uint8 [B, T]) and, when ``state`` is a
+    uint8 tensor of E4M3 codes, the row-scaled FP8 state with its fp32
+    ``state_scale`` [B, H_v, d_k] (both updated in place)."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, out_dtype=out_dtype)
+    if o is None:
+        o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=q.device)
+    opts = GdrStepOpts()
+    shape = (p.B, p.H_v, p.d_k, p.d_v)
+    if state.dtype == torch.uint8:
+        opts.state_format = GDR_STATE_E4M3
+        sp = _ptr(state, "state", torch.uint8, shape)
+        opts.state_scale = _ptr(state_scale, "state_scale", torch.float32, shape[:3])
+    else:
+        opts.state_format = GDR_STATE_F32
+        sp = _ptr(state, "state", torch.float32, shape)
+    opts.n_tokens = _ptr(n_tokens, "n_tokens", torch.int32, (p.B,))
+    opts.reset = _ptr(reset, "reset", torch.uint8, (p.B, p.T))
+    _check(lib.gdr_recurrent_step_ex(
+        ctypes.byref(p), ctypes.byref(opts), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"),
+        _ptr(log_alpha, "log_alpha"), sp, _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)), _stream(stream)))
+    return o
+
+
+def _state_problem(shape):
+    B, Hv, dk, dv = shape
+    p = GdrProblem()
+    p.B, p.T, p.H_k, p.H_v, p.d_k, p.d_v = B, 1, Hv, Hv, dk, dv
+    p.chunk, p.gate_groups = 64, 1
+    return p
+
+
+def gdr_state_quantize(state, *, codes=None, scale=None, stream=None):
+    """fp32 state [B, H_v, d_k, d_v] -> (E4M3 codes uint8, fp32 row scales [B, H_v, d_k])."""
+    lib = load()
+    p = _state_problem(tuple(state.shape))
+    if codes is None:
+        codes = torch.empty(state.shape, dtype=torch.uint8, device=state.device)
+    if scale is None:
+        scale = torch.empty(state.shape[:3], dtype=torch.float32, device=state.device)
+    _check(lib.gdr_state_quantize(ctypes.byref(p), _ptr(state, "state", torch.float32),
+                                  _ptr(codes, "codes", torch.uint8, tuple(state.shape)),
+                                  _ptr(scale, "scale", torch.float32, tuple(state.shape[:3])), _stream(stream)))
+    return codes, scale
+
+
+def gdr_state_dequantize(codes, scale, *, state=None, stream=None):
+    """(E4M3 codes, row scales) -> fp32 state [B, H_v, d_k, d_v]."""
+    lib = load()
+    p = _state_problem(tuple(codes.shape))
+    if state is None:
+        state = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _check(lib.gdr_state_dequantize(ctypes.byref(p), _ptr(codes, "codes", torch.uint8),
+                                    _ptr(scale, "scale", torch.float32, tuple(codes.shape[:3])),
+                                    _ptr(state, "state", torch.float32, tuple(codes.shape)), _stream(stream)))
+    return state

@@ -317,20 +317,20 @@ gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, 
 
 gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                               const void *log_alpha, float *state, void *o, void *stream) {
-  gdr_status s = check_problem(p, false);
-  if (s != GDR_OK) return s;
-  if (p->B == 0 || p->T == 0) return GDR_OK;
-  if ((s = check_ptr(q, "q", true)) || (s = check_ptr(k, "k", true)) || (s = check_ptr(v, "v", true)) ||
-      (s = check_ptr(beta, "beta", true)) || (s = check_ptr(log_alpha, "log_alpha", true)) ||
-      (s = check_ptr(state, "state", true)) || (s = check_ptr(o, "o", true)))
-    return s;
+  return gdr_recurrent_step_ex(p, nullptr, q, k, v, beta, log_alpha, state, o, stream);
+}
+
+namespace {
+
+gdr::StepArgs make_step_args(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                             const void *log_alpha, void *state, void *o) {
   gdr::StepArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.beta = beta;
   a.log_alpha = log_alpha;
-  a.state = state;
+  a.state = static_cast<float *>(state);
   a.o = o;
   a.B = p->B;
   a.T = p->T;
@@ -341,8 +341,87 @@ gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k
   a.G = p->gate_groups;
   a.gshift = log2_exact(p->d_k / p->gate_groups);
   a.beta_per_key_head = p->beta_per_key_head;
-  return launched(gdr::launch_step(a, p->in_dtype == GDR_BF16, p->out_dtype == GDR_BF16, static_cast<hipStream_t>(stream)),
-                  "recurrent kernel");
+  return a;
+}
+
+}  // namespace
+
+gdr_status gdr_recurrent_step_ex(const gdr_problem *p, const gdr_step_opts *opts, const void *q, const void *k,
+                                 const void *v, const void *beta, const void *log_alpha, void *state, void *o,
+                                 void *stream) {
+  gdr_status s = check_problem(p, false);
+  if (s != GDR_OK) return s;
+  const int fmt = opts ? opts->state_format : GDR_STATE_F32;
+  if (fmt != GDR_STATE_F32 && fmt != GDR_STATE_E4M3)
+    return fail(GDR_ERR_INVALID_ARG, "state_format=%d is not a gdr_state_format", fmt);
+  if (fmt == GDR_STATE_E4M3) {
+    if (!(p->d_v == 32 || p->d_v == 64 || p->d_v == 128))
+      return fail(GDR_ERR_UNSUPPORTED, "d_v=%d: the E4M3 state supports d_v in {32, 64, 128}", p->d_v);
+    if ((s = check_ptr(opts->state_scale, "state_scale", true, 4))) return s;
+  }
+  if (p->B == 0 || p->T == 0) return GDR_OK;
+  if ((s = check_ptr(q, "q", true)) || (s = check_ptr(k, "k", true)) || (s = check_ptr(v, "v", true)) ||
+      (s = check_ptr(beta, "beta", true)) || (s = check_ptr(log_alpha, "log_alpha", true)) ||
+      (s = check_ptr(state, "state", true)) || (s = check_ptr(o, "o", true)) ||
+      (opts && (s = check_ptr(opts->n_tokens, "n_tokens", false, 4))))
+    return s;
+  if (fmt == GDR_STATE_E4M3 && (s = check_ptr(state, "state", true, 256))) return s;
+  gdr::StepArgs a = make_step_args(p, q, k, v, beta, log_alpha, state, o);
+  if (opts) {
+    a.n_tokens = opts->n_tokens;
+    a.reset = opts->reset;
+    a.scale = opts->state_scale;
+  }
+  const bool in_bf16 = p->in_dtype == GDR_BF16, out_bf16 = p->out_dtype == GDR_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fmt == GDR_STATE_E4M3) return launched(gdr::launch_step_e4m3(a, in_bf16, out_bf16, st), "recurrent kernel");
+  return launched(gdr::launch_step(a, in_bf16, out_bf16, st), "recurrent kernel");
+}
+
+gdr_status gdr_verify(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                      const void *log_alpha, const float *state, void *o, void *stream) {
+  gdr_status s = check_problem(p, false);
+  if (s != GDR_OK) return s;
+  if (p->T > gdr::kVerifyMaxTokens)
+    return fail(GDR_ERR_UNSUPPORTED, "T=%d drafted tokens: gdr_verify takes at most %d", p->T, gdr::kVerifyMaxTokens);
+  if (p->B == 0 || p->T == 0) return GDR_OK;
+  if ((s = check_ptr(q, "q", true)) || (s = check_ptr(k, "k", true)) || (s = check_ptr(v, "v", true)) ||
+      (s = check_ptr(beta, "beta", true)) || (s = check_ptr(log_alpha, "log_alpha", true)) ||
+      (s = check_ptr(state, "state", true)) || (s = check_ptr(o, "o", true)))
+    return s;
+  gdr::StepArgs a = make_step_args(p, q, k, v, beta, log_alpha, const_cast<float *>(state), o);
+  return launched(gdr::launch_verify(a, p->in_dtype == GDR_BF16, p->out_dtype == GDR_BF16,
+                                     static_cast<hipStream_t>(stream)),
+                  "verify kernel");
+}
+
+gdr_status gdr_state_quantize(const gdr_problem *p, const float *state, void *codes, float *scale, void *stream) {
+  gdr_status s = check_problem(p, false);
+  if (s != GDR_OK) return s;
+  if (p->d_v > 256) return fail(GDR_ERR_UNSUPPORTED, "d_v=%d: state conversion supports d_v <= 256", p->d_v);
+  if (p->B == 0) return GDR_OK;
+  if ((s = check_ptr(state, "state", true)) || (s = check_ptr(codes, "codes", true, 4)) ||
+      (s = check_ptr(scale, "scale", true, 4)))
+    return s;
+  const long long rows = (long long)p->B * p->H_v * p->d_k;
+  return launched(gdr::launch_state_quantize(state, static_cast<unsigned char *>(codes), scale, rows, p->d_v,
+                                             static_cast<hipStream_t>(stream)),
+                  "state quantize kernel");
+}
+
+gdr_status gdr_state_dequantize(const gdr_problem *p, const void *codes, const float *scale, float *state,
+                                void *stream) {
+  gdr_status s = check_problem(p, false);
+  if (s != GDR_OK) return s;
+  if (p->d_v > 256) return fail(GDR_ERR_UNSUPPORTED, "d_v=%d: state conversion supports d_v <= 256", p->d_v);
+  if (p->B == 0) return GDR_OK;
+  if ((s = check_ptr(state, "state", true)) || (s = check_ptr(codes, "codes", true, 4)) ||
+      (s = check_ptr(scale, "scale", true, 4)))
+    return s;
+  const long long rows = (long long)p->B * p->H_v * p->d_k;
+  return launched(gdr::launch_state_dequantize(static_cast<const unsigned char *>(codes), scale, state, rows, p->d_v,
+                                               static_cast<hipStream_t>(stream)),
+                  "state dequantize kernel");
 }
 
 const char *gdr_status_string(gdr_status s) {

@@ -79,11 +79,19 @@ __device__ inline unsigned char *ws_tile(const ChunkArgs &a, int r, int heads, i
 
 struct StepArgs {
   const void *q, *k, *v, *beta, *log_alpha;
-  float *state;
+  float *state;                 // fp32 state, or (E4M3 format) the row codes as bytes
   void *o;
   int B, T, H_k, H_v, d_k, d_v, G, gshift;
   int beta_per_key_head;
+  const int *n_tokens;          // nullable [B]: tokens stepped per sequence (prefix of the T given)
+  const unsigned char *reset;   // nullable [B, T]: the token starts a new document
+  float *scale;                 // E4M3 format: one fp32 scale per state row [B, H_v, d_k]
 };
+
+// Drafted tokens one verification call takes.
+constexpr int kVerifyMaxTokens = 16;
+// Largest finite value of the E4M3 format (OCP FP8, 4 exponent bits, bias 7).
+constexpr float kE4M3Max = 448.f;
 
 // Each launcher validates nothing (the API layer did) and returns the launch
 // status.  `in_bf16`/`out_bf16` select the element types.
@@ -92,6 +100,13 @@ hipError_t launch_scan(const ChunkArgs &a, bool in_bf16, bool out_bf16, hipStrea
 hipError_t launch_gated_rmsnorm(const void *o, const void *z, const float *weight, float eps, void *y,
                                 long long rows, int d_v, bool o_bf16, bool z_bf16, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
+hipError_t launch_step_e4m3(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
+hipError_t launch_verify(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
+// Row-scaled E4M3 <-> fp32 for `rows` state rows of d_v values.
+hipError_t launch_state_quantize(const float *x, unsigned char *codes, float *scale, long long rows, int d_v,
+                                 hipStream_t stream);
+hipError_t launch_state_dequantize(const unsigned char *codes, const float *scale, float *x, long long rows, int d_v,
+                                   hipStream_t stream);
 
 }  // namespace gdr
 

@@ -257,6 +257,65 @@ gdr_status gdr_recurrent_step(const gdr_problem *p, const void *q, const void *k
                               const void *beta, const void *log_alpha, float *state, void *o,
                               void *stream);
 
+/*
+ * Speculative verification (Systolic Linear Attention, section 3.2): the
+ * outputs o [B, T, H_v, d_v] of T <= 16 drafted tokens per sequence, read
+ * from `state` (fp32 [B, H_v, d_k, d_v], READ ONLY: the call does not advance
+ * it) with the same block inversion as the chunk path -- the drafted tokens
+ * form one chunk of the WY form (Table 2).  chunk / solve fields are
+ * ignored; T > 16 is GDR_ERR_UNSUPPORTED.  Once n_b of sequence b's drafted
+ * tokens are accepted, gdr_recurrent_step_ex with n_tokens advances each
+ * state by exactly its accepted prefix.
+ */
+gdr_status gdr_verify(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                      const void *log_alpha, const float *state, void *o, void *stream);
+
+typedef enum {
+  GDR_STATE_F32 = 0,   /* fp32 [B, H_v, d_k, d_v] */
+  GDR_STATE_E4M3 = 1   /* row-scaled FP8: E4M3 codes (bytes) [B, H_v, d_k, d_v] and fp32 scales [B, H_v, d_k] */
+} gdr_state_format;
+
+/*
+ * Options of the recurrent step (serving; all nullable / 0 = off).
+ *   n_tokens     : DEVICE int32 [B]: sequence b steps only its first
+ *                  min(n_tokens[b], T) tokens (speculative decoding commits
+ *                  the accepted prefix); the outputs of the other tokens are
+ *                  not written.
+ *   reset        : DEVICE bytes [B, T]: nonzero = the token starts a new
+ *                  document (the state carried into it is discarded).
+ *   state_format : gdr_state_format of `state`.  GDR_STATE_E4M3 (the
+ *                  row-scaled FP8 state of the same paper's serving study):
+ *                  row i of a (batch, value head) state -- key channel i --
+ *                  is stored as E4M3 codes c (OCP FP8, 4 exponent and 3
+ *                  mantissa bits, largest finite 448) with one fp32 scale
+ *                  s_i = max_j |S_ij| / 448, S_ij = value(c_ij) s_i.  The
+ *                  call dequantises the state once, steps its tokens in fp32
+ *                  and quantises once at the end: x (448 / max_j |S_ij|)
+ *                  (fp32), clamped to +-448, rounded to E4M3 to nearest even;
+ *                  a zero row gets scale 0.  Supported for d_v in {32, 64,
+ *                  128}; one workgroup per (batch, value head).
+ *   state_scale  : the fp32 scales [B, H_v, d_k] (E4M3 only), read and written.
+ */
+typedef struct {
+  const int32_t *n_tokens;
+  const uint8_t *reset;
+  int32_t state_format;
+  float *state_scale;
+} gdr_step_opts;
+
+/* gdr_recurrent_step with step options (opts NULL = gdr_recurrent_step);
+ * `state` is fp32, or E4M3 codes when opts->state_format says so. */
+gdr_status gdr_recurrent_step_ex(const gdr_problem *p, const gdr_step_opts *opts, const void *q, const void *k,
+                                 const void *v, const void *beta, const void *log_alpha, void *state, void *o,
+                                 void *stream);
+
+/* Conversions between an fp32 state [B, H_v, d_k, d_v] and the row-scaled
+ * E4M3 form above (codes [B, H_v, d_k, d_v] bytes, scales [B, H_v, d_k] fp32),
+ * with the same rounding as gdr_recurrent_step_ex.  d_v <= 256. */
+gdr_status gdr_state_quantize(const gdr_problem *p, const float *state, void *codes, float *scale, void *stream);
+gdr_status gdr_state_dequantize(const gdr_problem *p, const void *codes, const float *scale, float *state,
+                                void *stream);
+
 /* Static text for a status code. */
 const char *gdr_status_string(gdr_status s);
 
