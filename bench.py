@@ -4,7 +4,8 @@ and the fp64 CPU oracle timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--solve exact|neumann]   (defaults 200, 400, 2)
     python bench.py --copy-calibration BYTES      # plain copy, for rocprofv3 --pmc scaling
-    python bench.py --decode [--config 2]         # the recurrent step, one token per sequence
+    python bench.py --decode [--config 2] [--state-format e4m3]   # the recurrent step, one token per sequence
+    python bench.py --verify 16 [--config 2]      # speculative verify of 16 drafted tokens + commit
 
 One step is one full forward over the workload's synthetic batch, inputs
 already resident in HBM: the chunk-prep kernel then the scan/output kernel
@@ -181,26 +182,36 @@ def decode_bench(w, args, q, k, v, beta, la):
 
     n_tok = min(w.T, 64)
     toks = [tuple(x[:, t:t + 1].contiguous() for x in (q, k, v, beta, la)) for t in range(n_tok)]
-    state = torch.zeros((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    e4m3 = args.state_format == "e4m3"
+    state = torch.zeros((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.uint8 if e4m3 else torch.float32, device="cuda")
+    scale = torch.zeros((w.B, w.H_v, w.d_k), dtype=torch.float32, device="cuda") if e4m3 else None
     o = torch.empty((w.B, 1, w.H_v, w.d_v), dtype=torch.float32, device="cuda")
 
     def steps():
         for tq, tk, tv, tb, tl in toks:
-            gb.gdr_recurrent_step(tq, tk, tv, tb, tl, state, o=o)
+            if e4m3:
+                gb.gdr_recurrent_step_ex(tq, tk, tv, tb, tl, state, state_scale=scale, o=o)
+            else:
+                gb.gdr_recurrent_step(tq, tk, tv, tb, tl, state, o=o)
+
+    def reset_state():
+        state.zero_()
+        if e4m3:
+            scale.zero_()
 
     steps()                                     # eager reference from the zero state
     torch.cuda.synchronize()
     ref = state.clone()
-    state.zero_()
+    reset_state()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         steps()
-    state.zero_()
+    reset_state()
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
-    replay_diff = float((state - ref).abs().max().item())
+    replay_diff = float((state.float() - ref.float()).abs().max().item())
     reps = max(1, args.steps // n_tok)
     for _ in range(max(1, args.warmup // n_tok)):
         graph.replay()
@@ -213,19 +224,64 @@ def decode_bench(w, args, q, k, v, beta, la):
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / (reps * n_tok)
     es = 2 if w.dtype == "bf16" else 4
-    state_bytes = 4 * w.B * w.H_v * w.d_k * w.d_v
+    state_bytes = (1 if e4m3 else 4) * w.B * w.H_v * w.d_k * w.d_v + (4 * w.B * w.H_v * w.d_k if e4m3 else 0)
     io_bytes = w.B * (es * (2 * w.H_k * w.d_k + w.H_v * w.d_v + w.H_beta + w.H_k * w.G) + 4 * w.H_v * w.d_v)
     achieved = (2 * state_bytes + io_bytes) / (ms_step * 1e-3) / 1e9
     print(json.dumps({
         "metric": "decode tokens/s (recurrent step, one token per sequence), 1 GPU",
         "value": w.B / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": reps * n_tok,
         "warmup": max(1, args.warmup // n_tok) * n_tok, "ms_per_step": ms_step, "higher_is_better": True,
-        "dtype": "f32 state, " + w.dtype + " inputs", "data": "synthetic", "timing": "HIP graph of 64 steps",
-        "graph_replay_max_abs_diff_vs_eager": replay_diff,
+        "dtype": ("row-scaled E4M3 state, " if e4m3 else "f32 state, ") + w.dtype + " inputs", "data": "synthetic",
+        "timing": "HIP graph of 64 steps", "graph_replay_max_abs_diff_vs_eager": replay_diff,
         "config": {"workload": w.name + "_decode", "B": w.B, "T": 1, "H_k": w.H_k, "H_v": w.H_v,
-                   "d_k": w.d_k, "d_v": w.d_v, "gate_groups": w.G},
+                   "d_k": w.d_k, "d_v": w.d_v, "gate_groups": w.G, "state": args.state_format},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "kernel": "step", "traffic": None},
+    }), flush=True)
+
+
+def verify_bench(w, args, q, k, v, beta, la):
+    """Speculative decoding step: verify T_ver drafted tokens of every
+    sequence from its state (gdr_verify), then commit an accepted prefix of
+    each (gdr_recurrent_step_ex with per-sequence token counts; here half of
+    the drafted tokens).  Both launches are captured in a HIP graph and
+    replayed; tokens/s counts the accepted tokens."""
+    import torch
+    from gated_delta_rule_87_amd import binding as gb
+
+    tv = args.verify
+    draft = tuple(x[:, :tv].contiguous() for x in (q, k, v, beta, la))
+    state = torch.zeros((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, tv, w.H_v, w.d_v), dtype=torch.float32, device="cuda")
+    oc = torch.empty_like(o)
+    n_acc = torch.full((w.B,), tv // 2, dtype=torch.int32, device="cuda")
+
+    def step():
+        gb.gdr_verify(*draft, state, o=o)
+        gb.gdr_recurrent_step_ex(*draft, state, n_tokens=n_acc, o=oc)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(max(1, args.warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({
+        "metric": "speculative decoding: verify T_ver drafted tokens + commit accepted prefix, 1 GPU",
+        "value": w.B * (tv // 2) / (ms * 1e-3), "unit": "accepted tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "f32 state, " + w.dtype,
+        "data": "synthetic", "timing": "HIP graph of verify + commit",
+        "config": {"workload": w.name + "_verify", "B": w.B, "T_ver": tv, "accepted": tv // 2, "H_k": w.H_k,
+                   "H_v": w.H_v, "d_k": w.d_k, "d_v": w.d_v, "gate_groups": w.G},
     }), flush=True)
 
 
@@ -245,6 +301,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--decode", action="store_true",
                     help="time gdr_recurrent_step on one token per sequence (its own metric)")
+    ap.add_argument("--state-format", default="f32", choices=["f32", "e4m3"], help="decode state format")
+    ap.add_argument("--batch", type=int, default=0, help="decode / verify: sequences in the batch (default: workload's)")
+    ap.add_argument("--verify", type=int, default=0, metavar="T_VER",
+                    help="time verify of T_VER drafted tokens + commit of half of them (its own metric)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -264,6 +324,10 @@ def main():
 
     w = WORKLOADS[args.config]
     solve = args.solve or w.solves[0]
+    serving = args.decode or args.verify
+    if serving:
+        # decode and verification read only the first 64 tokens of each sequence
+        w = w.with_(T=64, B=args.batch or w.B)
     print(f"[bench] workload {w.name}: {w.description}; solve={solve}", file=sys.stderr, flush=True)
     raw = make_inputs(w)
 
@@ -276,6 +340,9 @@ def main():
     q, k, v, beta, la = (dev(raw[n]) for n in ("q", "k", "v", "beta", "log_alpha"))
     if args.decode:
         decode_bench(w, args, q, k, v, beta, la)
+        return
+    if args.verify:
+        verify_bench(w, args, q, k, v, beta, la)
         return
     p = gb.make_problem(q, v, la, beta, chunk=w.chunk, solve=solve, neumann_order=w.neumann_order,
                         neumann_residual_steps=w.neumann_residual)

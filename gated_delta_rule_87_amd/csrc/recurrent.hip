@@ -146,14 +146,18 @@ __device__ __forceinline__ float e4m3_row_inv(float amax) { return amax > 0.f ? 
 
 // The recurrent step over an E4M3 state: one workgroup per (batch, value
 // head) holds the whole d_k x d_v state in fp32 registers (row scaling needs
-// all of a row, the step's reductions all of a column).  Thread t owns
-// columns 4 (t % NQ) .. + 3 and RP rows; the state is dequantised once,
-// stepped over the call's tokens in fp32 and quantised once at the end.
-template <typename TIn, typename TOut, int DK, int NQ>
-__global__ __launch_bounds__(kStepThreads) void step_e4m3_kernel(StepArgs a) {
-  constexpr int NG = kStepThreads / NQ;       // row groups
+// all of a row, the step's reductions all of a column); with few heads in
+// the batch it takes up to 1024 threads so that each carries few rows.  Thread t owns columns
+// 4 (t % NQ) .. + 3 and RP rows; the state is dequantised once, stepped
+// over the call's tokens in fp32 and quantised once at the end.
+template <int DK, int NQ, bool kWide>
+constexpr int e4m3_threads() { return kWide ? (DK * NQ < 1024 ? DK * NQ : 1024) : (DK * NQ < 256 ? DK * NQ : 256); }
+template <typename TIn, typename TOut, int DK, int NQ, bool kWide>
+__global__ __launch_bounds__((e4m3_threads<DK, NQ, kWide>())) void step_e4m3_kernel(StepArgs a) {
+  constexpr int NTH = e4m3_threads<DK, NQ, kWide>();
+  constexpr int NG = NTH / NQ;                // row groups
   constexpr int RP = DK / NG;                 // rows per thread
-  constexpr int NW = kStepThreads / 64;
+  constexpr int NW = NTH / 64;
   static_assert(RP >= 1 && DK % NG == 0 && NQ <= 64, "rows per thread");
   __shared__ f32x4 red[2][NW][NQ];
 
@@ -244,12 +248,25 @@ __global__ __launch_bounds__(kStepThreads) void step_e4m3_kernel(StepArgs a) {
 template <typename TIn, typename TOut, int NQ>
 static hipError_t launch_step_e4m3_q(const StepArgs &a, hipStream_t s) {
   dim3 grid(a.H_v, a.B);
+  // few (batch, head) workgroups: up to 1024 threads each, so each carries
+  // few rows (latency); many: 256 threads, fewer waves in each reduction
+  // (measured at B = 2 / 64 / 256, H = 32: 6.4 / 48 / 190 us per step with
+  // 1024 threads, 9.8 / 43.6 / 173 us with 256)
+  const bool wide = (long)a.B * a.H_v < 512;
+#define GDR_E4M3(dk_)                                                                                         \
+  if (wide)                                                                                                   \
+    hipLaunchKernelGGL((step_e4m3_kernel<TIn, TOut, dk_, NQ, true>), grid, dim3(e4m3_threads<dk_, NQ, true>()), \
+                       0, s, a);                                                                              \
+  else                                                                                                        \
+    hipLaunchKernelGGL((step_e4m3_kernel<TIn, TOut, dk_, NQ, false>), grid,                                   \
+                       dim3(e4m3_threads<dk_, NQ, false>()), 0, s, a)
   switch (a.d_k) {
-    case 64: hipLaunchKernelGGL((step_e4m3_kernel<TIn, TOut, 64, NQ>), grid, dim3(kStepThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((step_e4m3_kernel<TIn, TOut, 128, NQ>), grid, dim3(kStepThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((step_e4m3_kernel<TIn, TOut, 256, NQ>), grid, dim3(kStepThreads), 0, s, a); break;
+    case 64: GDR_E4M3(64); break;
+    case 128: GDR_E4M3(128); break;
+    case 256: GDR_E4M3(256); break;
     default: return hipErrorInvalidValue;
   }
+#undef GDR_E4M3
   return hipGetLastError();
 }
 
