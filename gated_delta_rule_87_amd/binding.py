@@ -20,6 +20,7 @@ GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_workspace_layout", "gdr_chunk_prepare",
            "gdr_chunk_scan", "gdr_chunk_fwd_noalloc", "gdr_chunk_fwd_ex", "gdr_gated_rmsnorm", "gdr_recurrent_step",
            "gdr_verify", "gdr_recurrent_step_ex", "gdr_state_quantize", "gdr_state_dequantize",
+           "gdr_chunk_states_size", "gdr_chunk_fwd_train", "gdr_chunk_bwd_workspace_size", "gdr_chunk_bwd",
            "gdr_status_string", "gdr_last_error")
 GDR_STATE_F32, GDR_STATE_E4M3 = 0, 1
 NOALLOC_SCRATCH_BYTES = 128 << 20   # GDR_NOALLOC_SCRATCH_BYTES
@@ -88,6 +89,14 @@ def load():
         lib.gdr_state_quantize.argtypes = [P, vp, vp, vp, vp]
         lib.gdr_state_dequantize.restype = ctypes.c_int
         lib.gdr_state_dequantize.argtypes = [P, vp, vp, vp, vp]
+        lib.gdr_chunk_states_size.restype = ctypes.c_size_t
+        lib.gdr_chunk_states_size.argtypes = [P]
+        lib.gdr_chunk_fwd_train.restype = ctypes.c_int
+        lib.gdr_chunk_fwd_train.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.gdr_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.gdr_chunk_bwd_workspace_size.argtypes = [P]
+        lib.gdr_chunk_bwd.restype = ctypes.c_int
+        lib.gdr_chunk_bwd.argtypes = [P] + [vp] * 15 + [ctypes.c_size_t, vp]
         lib.gdr_status_string.restype = ctypes.c_char_p
         lib.gdr_status_string.argtypes = [ctypes.c_int]
         lib.gdr_last_error.restype = ctypes.c_char_p
@@ -429,3 +438,74 @@ def gdr_state_dequantize(codes, scale, *, state=None, stream=None):
                                     _ptr(scale, "scale", torch.float32, tuple(codes.shape[:3])),
                                     _ptr(state, "state", torch.float32, tuple(codes.shape)), _stream(stream)))
     return state
+
+
+# ------------------------------------------------------------------ training
+def gdr_chunk_states_size(problem):
+    return int(load().gdr_chunk_states_size(ctypes.byref(problem)))
+
+
+def gdr_chunk_bwd_workspace_size(problem):
+    return int(load().gdr_chunk_bwd_workspace_size(ctypes.byref(problem)))
+
+
+def gdr_chunk_fwd_train(q, k, v, beta, log_alpha, h0=None, *, chunk=64, out_dtype=torch.float32, o=None,
+                        hT=None, states=None, workspace=None, stream=None):
+    """Training forward: gdr_chunk_fwd that also keeps the state entering
+    every chunk.  Returns (o, hT, states) with states fp32 [B, H_v, N_c, d_k, d_v]."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    p = make_problem(q, v, log_alpha, beta, chunk=chunk, out_dtype=out_dtype)
+    dev = q.device
+    nc = (p.T + p.chunk - 1) // p.chunk
+    state_shape = (p.B, p.H_v, p.d_k, p.d_v)
+    if o is None:
+        o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=dev)
+    if hT is None:
+        hT = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    if states is None:
+        states = torch.empty((p.B, p.H_v, nc, p.d_k, p.d_v), dtype=torch.float32, device=dev)
+    ws_bytes = gdr_chunk_fwd_workspace_size(p)
+    if gdr_chunk_states_size(p) == 0 and p.B * p.T > 0:
+        _check(lib.gdr_chunk_fwd_train(ctypes.byref(p), *([None] * 10), 0, None))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.gdr_chunk_fwd_train(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
+        _ptr(h0, "h0", torch.float32, state_shape), _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)),
+        _ptr(hT, "hT", torch.float32, state_shape),
+        _ptr(states, "states", torch.float32, (p.B, p.H_v, nc, p.d_k, p.d_v)),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, hT, states
+
+
+def gdr_chunk_bwd(q, k, v, beta, log_alpha, states, d_o, dhT=None, *, chunk=64, want_dh0=True, workspace=None,
+                  stream=None):
+    """Backward pass.  ``d_o`` has the forward's output dtype; ``states``
+    comes from gdr_chunk_fwd_train.  Returns a dict of fp32 gradients dq, dk,
+    dv, dbeta, dlog_alpha and dh0 (None unless ``want_dh0``)."""
+    lib = load()
+    _check_inputs(q, k, v, beta, log_alpha)
+    if d_o.dtype not in _DT:
+        raise TypeError(f"d_o must be float32 or bfloat16, got {d_o.dtype}")
+    p = make_problem(q, v, log_alpha, beta, chunk=chunk, out_dtype=d_o.dtype)
+    dev = q.device
+    nc = (p.T + p.chunk - 1) // p.chunk
+    state_shape = (p.B, p.H_v, p.d_k, p.d_v)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32),
+           "dbeta": torch.empty(beta.shape, **f32), "dlog_alpha": torch.empty(log_alpha.shape, **f32),
+           "dh0": torch.empty(state_shape, **f32) if want_dh0 else None}
+    ws_bytes = gdr_chunk_bwd_workspace_size(p)
+    if ws_bytes == 0:
+        _check(lib.gdr_chunk_bwd(ctypes.byref(p), *([None] * 15), 0, None))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    _check(lib.gdr_chunk_bwd(
+        ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
+        _ptr(states, "states", torch.float32, (p.B, p.H_v, nc, p.d_k, p.d_v)),
+        _ptr(d_o, "d_o", None, (p.B, p.T, p.H_v, p.d_v)), _ptr(dhT, "dhT", torch.float32, state_shape),
+        _ptr(out["dq"], "dq"), _ptr(out["dk"], "dk"), _ptr(out["dv"], "dv"), _ptr(out["dbeta"], "dbeta"),
+        _ptr(out["dlog_alpha"], "dlog_alpha"), _ptr(out["dh0"], "dh0"),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

@@ -213,10 +213,12 @@ namespace gdr {
 // the entry point that brings its own scratch (noalloc.hip).
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
-                         size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts) {
+                         size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts,
+                         float *states) {
   gdr_status s = check_problem(p, true);
   if (s != GDR_OK) return s;
-  if ((s = check_ptr(h0, "h0", false)) || (s = check_ptr(hT, "hT", false))) return s;
+  if ((s = check_ptr(h0, "h0", false)) || (s = check_ptr(hT, "hT", false)) || (s = check_ptr(states, "states", false)))
+    return s;
   const bool mom = opts && opts->momentum != 0.f;
   if (opts && !std::isfinite(opts->momentum))
     return fail(GDR_ERR_INVALID_ARG, "momentum=%g is not finite", (double)opts->momentum);
@@ -254,6 +256,7 @@ gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, con
   a.h0 = h0;
   a.o = o;
   a.hT = hT;
+  a.states = states;
   if (opts) {
     a.reset = opts->reset;
     if (mom) {
@@ -291,6 +294,134 @@ gdr_status gdr_chunk_fwd_ex(const gdr_problem *p, const gdr_layer_opts *opts, co
                             float *hT, void *workspace, size_t workspace_bytes, void *stream) {
   return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true,
                             opts);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Training forward and backward: the shapes and solve the backward supports.
+gdr_status check_train(const gdr_problem *p) {
+  gdr_status s = check_problem(p, true);
+  if (s != GDR_OK) return s;
+  if (!gdr::bwd_supported(p->chunk, p->d_k, p->d_v))
+    return fail(GDR_ERR_UNSUPPORTED, "chunk=%d d_k=%d d_v=%d: the backward pass supports chunk 64, d_k in {64, 128} "
+                "and d_v a multiple of 32", p->chunk, p->d_k, p->d_v);
+  if (p->solve != GDR_SOLVE_EXACT)
+    return fail(GDR_ERR_UNSUPPORTED, "solve=%d: the backward pass differentiates the exact in-chunk solve", p->solve);
+  return GDR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Backward workspace: the forward's six operand regions (holding the reverse
+// scan's operands), then A_c and G_c in fp32, X, and dS_c of every chunk.
+struct BwdLayout {
+  gdr::WsLayout ops;
+  size_t au_off, gu_off, x_off, ds_off, total;
+};
+
+BwdLayout bwd_layout_of(const gdr_problem *p) {
+  const size_t nc = ((size_t)p->T + p->chunk - 1) / p->chunk;
+  const int hb = p->beta_per_key_head ? p->H_k : p->H_v;
+  BwdLayout L;
+  L.ops = gdr::ws_layout(p->B, p->H_k, hb, (int)nc, p->chunk, p->d_k, p->in_dtype == GDR_BF16);
+  const size_t cc = (size_t)p->chunk * p->chunk * 4;
+  size_t at = L.ops.total;
+  L.au_off = at;
+  at = align256(at + (size_t)p->B * hb * nc * cc);
+  L.gu_off = at;
+  at = align256(at + (size_t)p->B * p->H_k * nc * cc);
+  L.x_off = at;
+  at = align256(at + (size_t)p->B * p->T * p->H_v * p->d_v * 4);
+  L.ds_off = at;
+  at = align256(at + (size_t)p->B * p->H_v * nc * p->d_k * p->d_v * 4);
+  L.total = at;
+  return L;
+}
+
+size_t states_bytes(const gdr_problem *p) {
+  const size_t nc = ((size_t)p->T + p->chunk - 1) / p->chunk;
+  return (size_t)p->B * p->H_v * nc * p->d_k * p->d_v * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr_chunk_states_size(const gdr_problem *p) {
+  if (check_train(p) != GDR_OK) return 0;
+  return states_bytes(p);
+}
+
+gdr_status gdr_chunk_fwd_train(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                               const void *log_alpha, const float *h0, void *o, float *hT, float *states,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  gdr_status s = check_train(p);
+  if (s != GDR_OK) return s;
+  if ((s = check_ptr(states, "states", p->B > 0 && p->T > 0))) return s;
+  return gdr::chunk_forward(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, true,
+                            nullptr, p->T > 0 ? states : nullptr);
+}
+
+size_t gdr_chunk_bwd_workspace_size(const gdr_problem *p) {
+  if (check_train(p) != GDR_OK) return 0;
+  return bwd_layout_of(p).total;
+}
+
+gdr_status gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                         const void *log_alpha, const float *states, const void *d_o, const float *dhT, float *dq,
+                         float *dk, float *dv, float *dbeta, float *dlog_alpha, float *dh0, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  gdr_status s = check_train(p);
+  if (s != GDR_OK) return s;
+  if ((s = check_ptr(dhT, "dhT", false)) || (s = check_ptr(dh0, "dh0", false))) return s;
+  if (p->B == 0) return GDR_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool in_bf16 = p->in_dtype == GDR_BF16, g_bf16 = p->out_dtype == GDR_BF16;
+  gdr::ChunkArgs a = make_chunk_args(p, nullptr);
+  gdr::BwdArgs g{};
+  g.dhT = dhT;
+  g.dh0 = dh0;
+  if (p->T == 0) {
+    // No tokens: dh0 = dhT.  The reverse scan over zero chunks writes only dh0.
+    if (!dh0) return GDR_OK;
+    return launched(gdr::launch_bwd_scan(a, g, in_bf16, g_bf16, st), "reverse scan kernel");
+  }
+  if ((s = check_ptr(q, "q", true)) || (s = check_ptr(k, "k", true)) || (s = check_ptr(v, "v", true)) ||
+      (s = check_ptr(beta, "beta", true)) || (s = check_ptr(log_alpha, "log_alpha", true)) ||
+      (s = check_ptr(states, "states", true)) || (s = check_ptr(d_o, "d_o", true)) ||
+      (s = check_ptr(dq, "dq", true)) || (s = check_ptr(dk, "dk", true)) || (s = check_ptr(dv, "dv", true)) ||
+      (s = check_ptr(dbeta, "dbeta", true, 4)) || (s = check_ptr(dlog_alpha, "dlog_alpha", true, 4)) ||
+      (s = check_ptr(workspace, "workspace", true, 256)))
+    return s;
+  const BwdLayout L = bwd_layout_of(p);
+  if (workspace_bytes < L.total)
+    return fail(GDR_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, L.total);
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.log_alpha = log_alpha;
+  a.ws = ws;
+  a.wl = L.ops;
+  a.solve = GDR_SOLVE_EXACT;
+  a.bwd = 1;
+  a.au = reinterpret_cast<float *>(ws + L.au_off);
+  a.gu = reinterpret_cast<float *>(ws + L.gu_off);
+  g.d_o = d_o;
+  g.states = states;
+  g.dq = dq;
+  g.dk = dk;
+  g.dv = dv;
+  g.dbeta = dbeta;
+  g.dla = dlog_alpha;
+  g.x = reinterpret_cast<float *>(ws + L.x_off);
+  g.dstates = reinterpret_cast<float *>(ws + L.ds_off);
+  if ((s = launched(gdr::launch_prep(a, in_bf16, st), "prep kernel (backward operands)")) != GDR_OK) return s;
+  if ((s = launched(gdr::launch_bwd_scan(a, g, in_bf16, g_bf16, st), "reverse scan kernel")) != GDR_OK) return s;
+  return launched(gdr::launch_bwd_grad(a, g, in_bf16, g_bf16, st), "gradient kernel");
 }
 
 gdr_status gdr_gated_rmsnorm(const gdr_problem *p, const void *o, const void *z, const float *weight, float eps,

@@ -396,4 +396,53 @@ template <> struct TileIO<PrecF32> {
   }
 };
 
+// --------------------------------------------------------------- fp32 tiles
+// acc += X[i, k] * Y[k, j] for one 16x16 tile over k in [k0, k0 + 16 N)
+// (element accessors; fp32 MFMA, lane l supplies X[i = l%16][k + l/16] and
+// Y[k + l/16][j = l%16]).  The length is a template constant so the loop
+// unrolls and its LDS reads are issued ahead of the MFMAs.
+template <int N, class FX, class FY>
+__device__ __forceinline__ void tile_f32_n(f32x4 &acc, const FX &x, const FY &y, int k0) {
+  const int l = lane_id();
+  const int i = l & 15, kk = l >> 4;
+  float xa[4 * N], yb[4 * N];
+#pragma unroll
+  for (int u = 0; u < 4 * N; ++u) {
+    xa[u] = x(i, k0 + 4 * u + kk);
+    yb[u] = y(k0 + 4 * u + kk, i);
+  }
+#pragma unroll
+  for (int u = 0; u < 4 * N; ++u) acc = mfma_f32(xa[u], yb[u], acc);
+}
+
+// Same over [k0, k1), k1 - k0 a multiple of 16 up to 16 NMAX (the longest
+// contraction the caller can reach; the registers of the unrolled loads are
+// sized for it).
+template <int NMAX, class FX, class FY>
+__device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, int k0, int k1) {
+  static_assert(NMAX >= 1 && NMAX <= 8, "contraction of 16 to 128");
+  switch ((k1 - k0) >> 4) {
+    case 1: tile_f32_n<1>(acc, x, y, k0); break;
+    case 2: if constexpr (NMAX >= 2) tile_f32_n<2>(acc, x, y, k0); break;
+    case 3: if constexpr (NMAX >= 3) tile_f32_n<3>(acc, x, y, k0); break;
+    case 4: if constexpr (NMAX >= 4) tile_f32_n<4>(acc, x, y, k0); break;
+    case 5: if constexpr (NMAX >= 5) tile_f32_n<5>(acc, x, y, k0); break;
+    case 6: if constexpr (NMAX >= 6) tile_f32_n<6>(acc, x, y, k0); break;
+    case 7: if constexpr (NMAX >= 7) tile_f32_n<7>(acc, x, y, k0); break;
+    case 8: if constexpr (NMAX >= 8) tile_f32_n<8>(acc, x, y, k0); break;
+    default: break;
+  }
+}
+
+// Lower-triangular chunk operands (diag(beta) A_c and L_c, and the reversed
+// transposes the backward pass uses): of their 16 x 32 operand blocks (I, s)
+// (row block I, contraction step s) only those with s <= I / 2 are nonzero.
+// Their number, and the position of block (I, s) among them in row-major
+// order.
+__host__ __device__ constexpr int tri_blocks(int nb) { return (nb / 2) * (nb / 2 + 1); }
+__device__ __forceinline__ int tri_index(int I, int s) {
+  const int m = I >> 1;
+  return ((I & 1) ? (m + 1) * (m + 1) : m * (m + 1)) + s;
+}
+
 }  // namespace gdr

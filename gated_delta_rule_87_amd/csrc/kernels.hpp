@@ -70,6 +70,19 @@ struct ChunkArgs {
   int seg_len;
   size_t h0_seg_stride;
   float *xfer;
+  // Training forward: the scan stores the state entering every chunk,
+  // S_{c-1}, to states [B][H_v][N_c][d_k][d_v] (fp32; nullable).
+  float *states;
+  // Backward preparation (bwd != 0): the prep kernels write the operands of
+  // the reverse scan in place of the forward ones -- in reversed token order
+  // within the chunk (J the reversal) region A holds J (diag(beta) A_c)^T J,
+  // L holds J L_c^T J (both lower triangular again), KB holds J Khat_c
+  // (token rows), QB holds (J Qbar_c)^T and KH holds (J Kbar_c)^T (channel
+  // rows) -- and also the unscaled A_c to au [B][H_beta][N_c][C][C] and the
+  // beta-free Gram G_c to gu [B][H_k][N_c][C][C] (fp32, row-major, zero above
+  // the diagonal).
+  int bwd;
+  float *au, *gu;
 };
 
 // Tile of region r for (batch b, head, chunk c).
@@ -88,6 +101,21 @@ struct StepArgs {
   float *scale;                 // E4M3 format: one fp32 scale per state row [B, H_v, d_k]
 };
 
+// Backward pass (chunk size 64): the upstream gradients and the outputs of
+// the reverse scan and the gradient kernel.
+struct BwdArgs {
+  const void *d_o;            // [B, T, H_v, d_v] out_dtype
+  const float *dhT;           // nullable [B, H_v, d_k, d_v]
+  const float *states;        // S_{c-1} of every chunk, [B][H_v][N_c][d_k][d_v]
+  float *dq, *dk;             // [B, T, H_k, d_k]
+  float *dv;                  // [B, T, H_v, d_v]
+  float *dbeta;               // [B, T, H_beta]
+  float *dla;                 // [B, T, H_k, G]
+  float *dh0;                 // nullable [B, H_v, d_k, d_v]
+  float *x;                   // workspace: X_c = L_c^T dO_c + Khat_c dS_c, [B, T, H_v, d_v]
+  float *dstates;             // workspace: dS_c of every chunk, [B][H_v][N_c][d_k][d_v]
+};
+
 // Drafted tokens one verification call takes.
 constexpr int kVerifyMaxTokens = 16;
 // Largest finite value of the E4M3 format (OCP FP8, 4 exponent bits, bias 7).
@@ -102,6 +130,11 @@ hipError_t launch_gated_rmsnorm(const void *o, const void *z, const float *weigh
 hipError_t launch_step(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_step_e4m3(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
 hipError_t launch_verify(const StepArgs &a, bool in_bf16, bool out_bf16, hipStream_t stream);
+// Backward: the reverse state scan (dv, X, dS_c, dh0) and the per-chunk
+// gradient kernel (dq, dk, dbeta, dlog_alpha).  `g_bf16`: d_o is bf16.
+hipError_t launch_bwd_scan(const ChunkArgs &a, const BwdArgs &g, bool in_bf16, bool g_bf16, hipStream_t stream);
+hipError_t launch_bwd_grad(const ChunkArgs &a, const BwdArgs &g, bool in_bf16, bool g_bf16, hipStream_t stream);
+bool bwd_supported(int C, int d_k, int d_v);
 // Row-scaled E4M3 <-> fp32 for `rows` state rows of d_v values.
 hipError_t launch_state_quantize(const float *x, unsigned char *codes, float *scale, long long rows, int d_v,
                                  hipStream_t stream);
@@ -117,9 +150,11 @@ namespace gdr {
 // The chunk forward behind gdr_chunk_fwd and gdr_chunk_fwd_ex (prepare =
 // true) and gdr_chunk_scan (prepare = false): validation, then the launches.
 // opts may be NULL.  api.cpp.
+// `states` (nullable): the training forward's chunk-entry states.
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
-                         size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts);
+                         size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts,
+                         float *states = nullptr);
 // Workspace bytes of a valid problem (else the validation status).
 gdr_status workspace_bytes_of(const gdr_problem *p, size_t *bytes);
 // Record `text` as this thread's gdr_last_error() and return s.

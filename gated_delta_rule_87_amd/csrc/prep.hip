@@ -116,44 +116,6 @@ __device__ __forceinline__ F lds_get_frag(const unsigned char *base, int idx) {
   return f;
 }
 
-// --------------------------------------------------------------- fp32 tiles
-// acc += X[i, k] * Y[k, j] for one 16x16 tile over k in [k0, k0 + 16 N)
-// (element accessors; fp32 MFMA, lane l supplies X[i = l%16][k + l/16] and
-// Y[k + l/16][j = l%16]).  The length is a template constant so the loop
-// unrolls and its LDS reads are issued ahead of the MFMAs.
-template <int N, class FX, class FY>
-__device__ __forceinline__ void tile_f32_n(f32x4 &acc, const FX &x, const FY &y, int k0) {
-  const int l = lane_id();
-  const int i = l & 15, kk = l >> 4;
-  float xa[4 * N], yb[4 * N];
-#pragma unroll
-  for (int u = 0; u < 4 * N; ++u) {
-    xa[u] = x(i, k0 + 4 * u + kk);
-    yb[u] = y(k0 + 4 * u + kk, i);
-  }
-#pragma unroll
-  for (int u = 0; u < 4 * N; ++u) acc = mfma_f32(xa[u], yb[u], acc);
-}
-
-// Same over [k0, k1), k1 - k0 a multiple of 16 up to 16 NMAX (the longest
-// contraction the caller can reach; the registers of the unrolled loads are
-// sized for it).
-template <int NMAX, class FX, class FY>
-__device__ __forceinline__ void tile_f32(f32x4 &acc, const FX &x, const FY &y, int k0, int k1) {
-  static_assert(NMAX >= 1 && NMAX <= 8, "contraction of 16 to 128");
-  switch ((k1 - k0) >> 4) {
-    case 1: tile_f32_n<1>(acc, x, y, k0); break;
-    case 2: if constexpr (NMAX >= 2) tile_f32_n<2>(acc, x, y, k0); break;
-    case 3: if constexpr (NMAX >= 3) tile_f32_n<3>(acc, x, y, k0); break;
-    case 4: if constexpr (NMAX >= 4) tile_f32_n<4>(acc, x, y, k0); break;
-    case 5: if constexpr (NMAX >= 5) tile_f32_n<5>(acc, x, y, k0); break;
-    case 6: if constexpr (NMAX >= 6) tile_f32_n<6>(acc, x, y, k0); break;
-    case 7: if constexpr (NMAX >= 7) tile_f32_n<7>(acc, x, y, k0); break;
-    case 8: if constexpr (NMAX >= 8) tile_f32_n<8>(acc, x, y, k0); break;
-    default: break;
-  }
-}
-
 // ------------------------------------------------------------- exact solve
 // amat <- (I + M)^{-1}, M = gmat diag(bet): 16x16 diagonal blocks by forward
 // substitution (one lane per column), then block-doubling merges
@@ -501,43 +463,71 @@ struct PrepItem {
   // Attention, Table 2; lane: token 16 I + lr, channels 32 s + 8 lq ..):
   // kbar = K (.) exp(Lambda_t), qbar = Q (.) exp(Lambda_t) and
   // kh = K (.) exp(Lambda_C - Lambda_t), the last transposed through the
-  // wave's LDS buffer into channel-row fragments.
+  // wave's LDS buffer into channel-row fragments.  Backward preparation: the
+  // reverse scan's operands instead, tokens reversed within the chunk --
+  // KB = J Khat (token rows), QB = (J Qbar)^T and KH = (J Kbar)^T.
   __device__ __forceinline__ void scan_operands(int I, int s, const float (&kbar)[8], const float (&qbar)[8],
                                                 const float (&kh)[8]) const {
+    if (a.bwd) {
+      IO::put_plain8(tKB, (NB - 1 - I) * KS + s, 16 * lq + 15 - lr, kh);
+      put_channel_rows(tQB, I, s, qbar, true);
+      put_channel_rows(tKH, I, s, kbar, true);
+      return;
+    }
     IO::put_plain8(tKB, I * KS + s, l, kbar);
     IO::put_plain8(tQB, I * KS + s, l, qbar);
-    // Khat^T: lane (token lr, channels 8 lq ..) writes, lane (channel
-    // 16 (l >> 5) + (l & 15), tokens 8 g ..) reads back a fragment
+    put_channel_rows(tKH, I, s, kh, false);
+  }
+
+  // A d_k x C channel-row tile from token-row values: lane (token lr,
+  // channels 8 lq ..) writes, lane (channel 16 (l >> 5) + (l & 15), tokens
+  // 8 g ..) reads back a fragment.  `rev`: token t goes to column C - 1 - t.
+  __device__ __forceinline__ void put_channel_rows(void *tile, int I, int s, const float (&v)[8], bool rev) const {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xb[(8 * lq + e) * kXbLd + lr] = kh[e];
+    for (int e = 0; e < 8; ++e) xb[(8 * lq + e) * kXbLd + lr] = v[e];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int chl = 16 * (l >> 5) + (l & 15), g = (l >> 4) & 1;
     float xt[8];
     const float4 u0 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g);
     const float4 u1 = *reinterpret_cast<const float4 *>(xb + chl * kXbLd + 8 * g + 4);
-    xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    IO::put_plain8(tKH, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+    if (!rev) {
+      xt[0] = u0.x; xt[1] = u0.y; xt[2] = u0.z; xt[3] = u0.w; xt[4] = u1.x; xt[5] = u1.y; xt[6] = u1.z; xt[7] = u1.w;
+      IO::put_plain8(tile, (2 * s + (l >> 5)) * (C / 32) + I / 2, 16 * (2 * (I & 1) + g) + (l & 15), xt);
+    } else {
+      // tokens 16 I + 8 g + e -> 16 Ir + 8 (1 - g) + 7 - e
+      const int Ir = NB - 1 - I, gr = 1 - g;
+      xt[0] = u1.w; xt[1] = u1.z; xt[2] = u1.y; xt[3] = u1.x; xt[4] = u0.w; xt[5] = u0.z; xt[6] = u0.y; xt[7] = u0.x;
+      IO::put_plain8(tile, (2 * s + (l >> 5)) * (C / 32) + Ir / 2, 16 * (2 * (Ir & 1) + gr) + (l & 15), xt);
+    }
   }
 
   // The 16 x 16 block (I, J) of L from an MFMA accumulator (lane: rows
   // 4 lq .. 4 lq + 3, column lr), through the wave's LDS buffer, as 32
   // fragments of 8 columns; on the diagonal block the entries above the
-  // diagonal are zero.
+  // diagonal are zero.  Backward preparation: block (I, J) of L is block
+  // (NB-1-J, NB-1-I) of J L^T J, entry (r, c) at (15 - c, 15 - r).
   __device__ __forceinline__ void store_L_block(int I, int J, const f32x4 &acc) const {
+    const bool rev = a.bwd != 0;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int r = 4 * lq + q4;
-      xb[r * kXbLd + lr] = (I > J || r >= lr) ? acc[q4] : 0.f;
+      const float v = (I > J || r >= lr) ? acc[q4] : 0.f;
+      if (rev) {
+        xb[(15 - lr) * kXbLd + 15 - r] = v;
+      } else {
+        xb[r * kXbLd + lr] = v;
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int r = l & 15, h = (l >> 4) & 1;
     const float4 u0 = *reinterpret_cast<const float4 *>(xb + r * kXbLd + 8 * h);
     const float4 u1 = *reinterpret_cast<const float4 *>(xb + r * kXbLd + 8 * h + 4);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int bi = rev ? NB - 1 - J : I, bj = rev ? NB - 1 - I : J;
     if (l < 32) {
       const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-      IO::put_plain8(tL, I * (C / 32) + J / 2, 16 * (2 * (J & 1) + h) + r, v);
+      IO::put_plain8(tL, bi * (C / 32) + bj / 2, 16 * (2 * (bj & 1) + h) + r, v);
     }
   }
 
@@ -598,14 +588,45 @@ struct PrepItem {
         const int blk = u >> 6, f = u & 63;
         if (2 * (blk % (C / 32)) > blk / (C / 32)) continue;   // block wholly above the diagonal: not written
         const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
-        const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
-        const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
         const bool upper = col / 16 > row / 16;             // the half of a straddling block above the diagonal
-        const float bt = bet[row];
-        float x[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
+        float x[8];
+        if (a.bwd) {
+          // J (diag(beta) A)^T J: entry (row, col) = beta_r A[r][C-1-row], r = C-1-col
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = upper ? 0.f : x[e];
+          for (int e = 0; e < 8; ++e) {
+            const int rr = C - 1 - col - e;
+            x[e] = upper ? 0.f : bet[rr] * asolve[rr * (C + 4) + C - 1 - row];
+          }
+        } else {
+          const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
+          const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
+          const float bt = bet[row];
+          const float y[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = upper ? 0.f : y[e];
+        }
         IO::put_plain8(tA, blk, f, x);
+      }
+      if (a.bwd) {
+        // the gradient kernel's copies: A_c unscaled and (once) G_c, fp32 row-major
+        float *au = a.au + (((size_t)b * a.H_beta + hb) * a.N_c + c) * (C * C);
+        for (int u = tid; u < C * C / 4; u += blockDim.x) {
+          const int row = u / (C / 4), col = 4 * (u % (C / 4));
+          const float4 v = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
+          *reinterpret_cast<float4 *>(au + row * C + col) =
+              make_float4(col <= row ? v.x : 0.f, col + 1 <= row ? v.y : 0.f, col + 2 <= row ? v.z : 0.f,
+                          col + 3 <= row ? v.w : 0.f);
+        }
+        if (rb == 0) {
+          float *gu = a.gu + (((size_t)b * a.H_k + hk) * a.N_c + c) * (C * C);
+          for (int u = tid; u < C * C / 4; u += blockDim.x) {
+            const int row = u / (C / 4), col = 4 * (u % (C / 4));
+            const float4 v = *reinterpret_cast<const float4 *>(gsolve + row * (C + 4) + col);
+            *reinterpret_cast<float4 *>(gu + row * C + col) =
+                make_float4(col < row ? v.x : 0.f, col + 1 < row ? v.y : 0.f, col + 2 < row ? v.z : 0.f,
+                            col + 3 < row ? v.w : 0.f);
+          }
+        }
       }
     }
   }

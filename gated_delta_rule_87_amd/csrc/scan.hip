@@ -62,16 +62,6 @@ namespace gdr {
 constexpr int kScanWaves = 8;
 constexpr int kXcds = 8;   // accelerator complex dies of the MI355X, each with its own L2
 
-// The chunk operands diag(beta) A_c and L_c are lower triangular: of their
-// 16 x 32 operand blocks (I, s) (row block I, contraction step s) only those
-// with s <= I / 2 are nonzero.  Their number, and the position of block
-// (I, s) among them in row-major order.
-__host__ __device__ constexpr int tri_blocks(int nb) { return (nb / 2) * (nb / 2 + 1); }
-__device__ __forceinline__ int tri_index(int I, int s) {
-  const int m = I >> 1;
-  return ((I & 1) ? (m + 1) * (m + 1) : m * (m + 1)) + s;
-}
-
 // FB: bytes of one 16 x 32 operand block in the workspace (fp16 1 KiB, fp32 2 KiB).
 // XF: the transfer pass of the segment-parallel scan, which stages no output
 // and no L_c blocks.
@@ -143,9 +133,13 @@ __device__ __forceinline__ T *at(T *base, unsigned off) {
 // the d_k columns of the segment's transition J (value input 0, initial
 // state the identity) followed by the d_v columns of its offset B (the real
 // values, initial state 0); it writes [J | B] and no output.
-template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom, bool kXfer = false>
+// kSave (training forward): the state entering each chunk, S_{c-1}, is also
+// stored to a.states for the backward pass.
+template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom, bool kXfer = false,
+          bool kSave = false>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   static_assert(!(kMom && kXfer), "momentum doubles the carried state: no transfer pass");
+  static_assert(!(kSave && (kMom || kXfer)), "saved states: plain forward only");
   constexpr int FB = P::kF32 ? 2048 : 1024;
   using Lay = ScanLayout<C, DK, BV, FB, kXfer>;
   using IO = TileIO<P>;
@@ -372,6 +366,21 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   auto step = [&](int c, auto tail_tag) __attribute__((always_inline)) {
     constexpr bool kTail = decltype(tail_tag)::value;
     const int c1 = last(c + 1);
+    if constexpr (kSave) {
+      float *st = a.states + (((size_t)b * a.H_v + hv) * a.N_c + c) * DK * a.d_v;
+#pragma unroll
+      for (int r = 0; r < SJ::RPW; ++r) {
+        const int i0 = 16 * SJ::blk(w, r);
+#pragma unroll
+        for (int u = 0; u < SJ::TPW; ++u) {
+          const int n = SJ::tile(w, u);
+          if (!SJ::kAllTiles && n >= NT) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_nontemporal_store(S[r][u][e], st + (size_t)(i0 + 4 * lq + e) * a.d_v + c0 + 16 * n + lr);
+        }
+      }
+    }
 
     // ---- Y = V - Kbar S, and Qbar S
     f32x4 accO[J::RPW][J::TPW];
@@ -752,6 +761,13 @@ static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream, int segm
   const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024>::total;
   auto kern = a.momentum != 0.f ? scan_kernel<TIn, TOut, P, C, DK, BV, true>
                                 : scan_kernel<TIn, TOut, P, C, DK, BV, false>;
+  if (a.states) {                              // training forward: the shapes the backward pass takes
+    if constexpr (C == 64 && DK <= 128 && BV == 32) {
+      kern = scan_kernel<TIn, TOut, P, C, DK, BV, false, false, true>;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
   if (e != hipSuccess) return e;
   dim3 grid((a.d_v / BV) * a.H_v * a.B, segments);
@@ -807,7 +823,7 @@ static hipError_t launch_scan_bv(const ChunkArgs &a, hipStream_t s) {
   if (segments > 1 && a.wl.seg_bytes >= scan_seg_bytes(a.B, a.H_v, a.N_c, DK, a.d_v) &&
       scan_lds_bytes(C, DK, 32, P::kF32 ? 2048 : 1024) <= 160 * 1024)
     return launch_segmented<TIn, TOut, P, C, DK>(a, s, segments);
-  const int bv = scan_choose_bv(a.B, a.H_v, C, DK, a.d_v, sizeof(TIn) == 2);
+  const int bv = a.states ? 32 : scan_choose_bv(a.B, a.H_v, C, DK, a.d_v, sizeof(TIn) == 2);
   if (bv == 32) return launch_scan_t<TIn, TOut, P, C, DK, 32>(a, s);
   if (bv == 16) return launch_scan_t<TIn, TOut, P, C, DK, 16>(a, s);
   return hipErrorInvalidValue;

@@ -236,6 +236,62 @@ gdr_status gdr_chunk_fwd_ex(const gdr_problem *p, const gdr_layer_opts *opts, co
                             void *o, float *hT, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training: forward with saved chunk-entry states, and the backward pass
+ * (Systolic Linear Attention, section 2.5: a custom VJP that saves only the
+ * state S_{c-1} entering each chunk and recomputes M_c, L_c and A_c;
+ * D_c = A_c^T diag(beta) dE_c and dM_c = -tril_{-1}(D_c E~_c^T) with
+ * E~_c = A_c (V_c - Kbar_c S_{c-1})).
+ *
+ * Supported: chunk 64, d_k in {64, 128}, d_v a multiple of 32, the exact
+ * solve, in_dtype bf16 or f32; no layer options (resets, momentum).  Other
+ * problems return GDR_ERR_UNSUPPORTED (size functions: 0).
+ *
+ * gdr_chunk_states_size: bytes of `states`, fp32 [B, H_v, N_c, d_k, d_v]
+ * (N_c = ceil(T / chunk)): S_{c-1} of every chunk c, S_{-1} = h0 (or 0).
+ *
+ * gdr_chunk_fwd_train: gdr_chunk_fwd (same arguments, workspace size and
+ * results) that also writes `states` (16-byte aligned; NULL allowed only
+ * when B T = 0).
+ */
+size_t gdr_chunk_states_size(const gdr_problem *p);
+gdr_status gdr_chunk_fwd_train(const gdr_problem *p, const void *q, const void *k, const void *v,
+                               const void *beta, const void *log_alpha, const float *h0, void *o,
+                               float *hT, float *states, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * Bytes of device workspace gdr_chunk_bwd needs (0 for an unsupported
+ * problem): the six operand regions of gdr_chunk_fwd_workspace_size (no
+ * segment region) holding the reverse scan's operands, A_c and G_c in fp32
+ * ([B][H_beta][N_c][C][C] and [B][H_k][N_c][C][C]), X_c = L_c^T dO_c +
+ * Khat_c dS_c (fp32 [B, T, H_v, d_v]) and dS_c of every chunk (fp32
+ * [B, H_v, N_c, d_k, d_v]), each at a 256-byte boundary.
+ */
+size_t gdr_chunk_bwd_workspace_size(const gdr_problem *p);
+
+/*
+ * Backward pass: gradients of sum(o (.) d_o) + sum(hT (.) dhT) with respect
+ * to every input of gdr_chunk_fwd_train.
+ *   q, k, v, beta, log_alpha : the forward's inputs (layouts and dtype as there).
+ *   states : what gdr_chunk_fwd_train wrote for these inputs and h0.
+ *   d_o    : upstream gradient of o, out_dtype [B, T, H_v, d_v].
+ *   dhT    : upstream gradient of hT, fp32 [B, H_v, d_k, d_v]; NULL = zero.
+ *   dq, dk : fp32 [B, T, H_k, d_k];  dv : fp32 [B, T, H_v, d_v];
+ *   dbeta  : fp32, beta's layout;    dlog_alpha : fp32 [B, T, H_k, G];
+ *   dh0    : fp32 [B, H_v, d_k, d_v], or NULL = not written.
+ * Every output is written in full (no accumulation into existing values).
+ * workspace: at least gdr_chunk_bwd_workspace_size(p) bytes, 256-byte aligned.
+ * Three launches after the prep kernels (which write the reverse operands):
+ * the reverse state scan (dv, X, dS_c, dh0; sequential over chunks) and the
+ * per-chunk gradient kernel (dq, dk, dbeta, dlog_alpha; all chunks at once).
+ */
+gdr_status gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void *v,
+                         const void *beta, const void *log_alpha, const float *states, const void *d_o,
+                         const float *dhT, float *dq, float *dk, float *dv, float *dbeta,
+                         float *dlog_alpha, float *dh0, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
  * Output epilogue of the same layer (section 2.3, token-level recurrence
  * box): per (batch, token, value head) row of d_v entries,
  *     y = sigmoid(z) (.) o / sqrt(mean(o^2) + eps) (.) weight,
