@@ -285,6 +285,63 @@ def verify_bench(w, args, q, k, v, beta, la):
     }), flush=True)
 
 
+def train_bench(w, args, q, k, v, beta, la):
+    """Training step: the forward that keeps every chunk-entry state
+    (gdr_chunk_fwd_train) and the backward pass (gdr_chunk_bwd) with a
+    seeded upstream gradient of o; tokens/s of forward + backward."""
+    import torch
+    from gated_delta_rule_87_amd import binding as gb
+
+    p = gb.make_problem(q, v, la, beta, chunk=w.chunk)
+    ws_f = torch.empty(gb.gdr_chunk_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(gb.gdr_chunk_bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    nc = -(-w.T // w.chunk)
+    states = torch.empty((w.B, w.H_v, nc, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, w.T, w.H_v, w.d_v), dtype=torch.float32, device="cuda")
+    hT = torch.empty((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 7)
+    d_o = torch.randn(o.shape, generator=gen, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32),
+           "dbeta": torch.empty(beta.shape, **f32), "dlog_alpha": torch.empty(la.shape, **f32),
+           "dh0": torch.empty(hT.shape, **f32)}
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        gb.gdr_chunk_fwd_train(q, k, v, beta, la, None, chunk=w.chunk, o=o, hT=hT, states=states, workspace=ws_f)
+        if evs:
+            evs[1].record()
+        gb.gdr_chunk_bwd(q, k, v, beta, la, states, d_o, None, chunk=w.chunk, workspace=ws_b, out=out)
+        if evs:
+            evs[2].record()
+
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(5):
+            step()
+        n_warm += 5
+        torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    print(json.dumps({
+        "metric": "training step (chunkwise forward keeping chunk states + backward), 1 GPU",
+        "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": w.dtype,
+        "data": "synthetic", "kernel_ms": {"forward_train": fwd_ms, "backward": bwd_ms},
+        "config": {"workload": w.name + "_train", "B": w.B, "T": w.T, "H_k": w.H_k, "H_v": w.H_v, "d_k": w.d_k,
+                   "d_v": w.d_v, "chunk": w.chunk, "gate_groups": w.G, "grad_dtype": "f32"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +360,8 @@ def main():
                     help="time gdr_recurrent_step on one token per sequence (its own metric)")
     ap.add_argument("--state-format", default="f32", choices=["f32", "e4m3"], help="decode state format")
     ap.add_argument("--batch", type=int, default=0, help="decode / verify: sequences in the batch (default: workload's)")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step: forward keeping chunk states + backward (its own metric)")
     ap.add_argument("--verify", type=int, default=0, metavar="T_VER",
                     help="time verify of T_VER drafted tokens + commit of half of them (its own metric)")
     args = ap.parse_args()
@@ -343,6 +402,9 @@ def main():
         return
     if args.verify:
         verify_bench(w, args, q, k, v, beta, la)
+        return
+    if args.train:
+        train_bench(w, args, q, k, v, beta, la)
         return
     p = gb.make_problem(q, v, la, beta, chunk=w.chunk, solve=solve, neumann_order=w.neumann_order,
                         neumann_residual_steps=w.neumann_residual)

@@ -480,10 +480,11 @@ def gdr_chunk_fwd_train(q, k, v, beta, log_alpha, h0=None, *, chunk=64, out_dtyp
 
 
 def gdr_chunk_bwd(q, k, v, beta, log_alpha, states, d_o, dhT=None, *, chunk=64, want_dh0=True, workspace=None,
-                  stream=None):
+                  out=None, stream=None):
     """Backward pass.  ``d_o`` has the forward's output dtype; ``states``
     comes from gdr_chunk_fwd_train.  Returns a dict of fp32 gradients dq, dk,
-    dv, dbeta, dlog_alpha and dh0 (None unless ``want_dh0``)."""
+    dv, dbeta, dlog_alpha and dh0 (None unless ``want_dh0``); ``out`` may
+    hold preallocated tensors for them."""
     lib = load()
     _check_inputs(q, k, v, beta, log_alpha)
     if d_o.dtype not in _DT:
@@ -493,9 +494,14 @@ def gdr_chunk_bwd(q, k, v, beta, log_alpha, states, d_o, dhT=None, *, chunk=64, 
     nc = (p.T + p.chunk - 1) // p.chunk
     state_shape = (p.B, p.H_v, p.d_k, p.d_v)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32),
-           "dbeta": torch.empty(beta.shape, **f32), "dlog_alpha": torch.empty(log_alpha.shape, **f32),
-           "dh0": torch.empty(state_shape, **f32) if want_dh0 else None}
+    if out is None:
+        out = {"dq": torch.empty(q.shape, **f32), "dk": torch.empty(k.shape, **f32),
+               "dv": torch.empty(v.shape, **f32), "dbeta": torch.empty(beta.shape, **f32),
+               "dlog_alpha": torch.empty(log_alpha.shape, **f32),
+               "dh0": torch.empty(state_shape, **f32) if want_dh0 else None}
+    for n, t in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta), ("dlog_alpha", log_alpha)):
+        _ptr(out[n], n, torch.float32, t.shape)
+    _ptr(out.get("dh0"), "dh0", torch.float32, state_shape)
     ws_bytes = gdr_chunk_bwd_workspace_size(p)
     if ws_bytes == 0:
         _check(lib.gdr_chunk_bwd(ctypes.byref(p), *([None] * 15), 0, None))
