@@ -296,7 +296,8 @@ def train_bench(w, args, q, k, v, beta, la):
     ws_f = torch.empty(gb.gdr_chunk_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(gb.gdr_chunk_bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
     nc = -(-w.T // w.chunk)
-    states = torch.empty((w.B, w.H_v, nc, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    states = torch.empty((w.B, w.H_v, nc, w.d_k, w.d_v), device="cuda",
+                         dtype=torch.float16 if q.dtype == torch.bfloat16 else torch.float32)
     o = torch.empty((w.B, w.T, w.H_v, w.d_v), dtype=torch.float32, device="cuda")
     hT = torch.empty((w.B, w.H_v, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
     gen = torch.Generator(device="cuda").manual_seed(w.seed + 7)

@@ -452,7 +452,8 @@ def gdr_chunk_bwd_workspace_size(problem):
 def gdr_chunk_fwd_train(q, k, v, beta, log_alpha, h0=None, *, chunk=64, out_dtype=torch.float32, o=None,
                         hT=None, states=None, workspace=None, stream=None):
     """Training forward: gdr_chunk_fwd that also keeps the state entering
-    every chunk.  Returns (o, hT, states) with states fp32 [B, H_v, N_c, d_k, d_v]."""
+    every chunk.  Returns (o, hT, states) with states [B, H_v, N_c, d_k, d_v],
+    float16 for bfloat16 inputs and float32 for float32 inputs."""
     lib = load()
     _check_inputs(q, k, v, beta, log_alpha)
     p = make_problem(q, v, log_alpha, beta, chunk=chunk, out_dtype=out_dtype)
@@ -463,8 +464,9 @@ def gdr_chunk_fwd_train(q, k, v, beta, log_alpha, h0=None, *, chunk=64, out_dtyp
         o = torch.empty((p.B, p.T, p.H_v, p.d_v), dtype=out_dtype, device=dev)
     if hT is None:
         hT = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    st_dtype = torch.float16 if q.dtype == torch.bfloat16 else torch.float32
     if states is None:
-        states = torch.empty((p.B, p.H_v, nc, p.d_k, p.d_v), dtype=torch.float32, device=dev)
+        states = torch.empty((p.B, p.H_v, nc, p.d_k, p.d_v), dtype=st_dtype, device=dev)
     ws_bytes = gdr_chunk_fwd_workspace_size(p)
     if gdr_chunk_states_size(p) == 0 and p.B * p.T > 0:
         _check(lib.gdr_chunk_fwd_train(ctypes.byref(p), *([None] * 10), 0, None))
@@ -474,7 +476,7 @@ def gdr_chunk_fwd_train(q, k, v, beta, log_alpha, h0=None, *, chunk=64, out_dtyp
         ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
         _ptr(h0, "h0", torch.float32, state_shape), _ptr(o, "o", out_dtype, (p.B, p.T, p.H_v, p.d_v)),
         _ptr(hT, "hT", torch.float32, state_shape),
-        _ptr(states, "states", torch.float32, (p.B, p.H_v, nc, p.d_k, p.d_v)),
+        _ptr(states, "states", st_dtype, (p.B, p.H_v, nc, p.d_k, p.d_v)),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, hT, states
 
@@ -509,7 +511,8 @@ def gdr_chunk_bwd(q, k, v, beta, log_alpha, states, d_o, dhT=None, *, chunk=64, 
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     _check(lib.gdr_chunk_bwd(
         ctypes.byref(p), _ptr(q, "q"), _ptr(k, "k"), _ptr(v, "v"), _ptr(beta, "beta"), _ptr(log_alpha, "log_alpha"),
-        _ptr(states, "states", torch.float32, (p.B, p.H_v, nc, p.d_k, p.d_v)),
+        _ptr(states, "states", torch.float16 if q.dtype == torch.bfloat16 else torch.float32,
+             (p.B, p.H_v, nc, p.d_k, p.d_v)),
         _ptr(d_o, "d_o", None, (p.B, p.T, p.H_v, p.d_v)), _ptr(dhT, "dhT", torch.float32, state_shape),
         _ptr(out["dq"], "dq"), _ptr(out["dk"], "dk"), _ptr(out["dv"], "dv"), _ptr(out["dbeta"], "dbeta"),
         _ptr(out["dlog_alpha"], "dlog_alpha"), _ptr(out["dh0"], "dh0"),

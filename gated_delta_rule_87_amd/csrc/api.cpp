@@ -214,7 +214,7 @@ namespace gdr {
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
                          size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts,
-                         float *states) {
+                         void *states) {
   gdr_status s = check_problem(p, true);
   if (s != GDR_OK) return s;
   if ((s = check_ptr(h0, "h0", false)) || (s = check_ptr(hT, "hT", false)) || (s = check_ptr(states, "states", false)))
@@ -333,16 +333,17 @@ BwdLayout bwd_layout_of(const gdr_problem *p) {
   L.gu_off = at;
   at = align256(at + (size_t)p->B * p->H_k * nc * cc);
   L.x_off = at;
-  at = align256(at + (size_t)p->B * p->T * p->H_v * p->d_v * 4);
+  const size_t wb = p->in_dtype == GDR_BF16 ? 2 : 4;   // X and dS_c: fp16 for bf16 inputs
+  at = align256(at + (size_t)p->B * p->T * p->H_v * p->d_v * wb);
   L.ds_off = at;
-  at = align256(at + (size_t)p->B * p->H_v * nc * p->d_k * p->d_v * 4);
+  at = align256(at + (size_t)p->B * p->H_v * nc * p->d_k * p->d_v * wb);
   L.total = at;
   return L;
 }
 
 size_t states_bytes(const gdr_problem *p) {
   const size_t nc = ((size_t)p->T + p->chunk - 1) / p->chunk;
-  return (size_t)p->B * p->H_v * nc * p->d_k * p->d_v * 4;
+  return (size_t)p->B * p->H_v * nc * p->d_k * p->d_v * (p->in_dtype == GDR_BF16 ? 2 : 4);
 }
 
 }  // namespace
@@ -355,7 +356,7 @@ size_t gdr_chunk_states_size(const gdr_problem *p) {
 }
 
 gdr_status gdr_chunk_fwd_train(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
-                               const void *log_alpha, const float *h0, void *o, float *hT, float *states,
+                               const void *log_alpha, const float *h0, void *o, float *hT, void *states,
                                void *workspace, size_t workspace_bytes, void *stream) {
   gdr_status s = check_train(p);
   if (s != GDR_OK) return s;
@@ -370,7 +371,7 @@ size_t gdr_chunk_bwd_workspace_size(const gdr_problem *p) {
 }
 
 gdr_status gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
-                         const void *log_alpha, const float *states, const void *d_o, const float *dhT, float *dq,
+                         const void *log_alpha, const void *states, const void *d_o, const float *dhT, float *dq,
                          float *dk, float *dv, float *dbeta, float *dlog_alpha, float *dh0, void *workspace,
                          size_t workspace_bytes, void *stream) {
   gdr_status s = check_train(p);
@@ -417,8 +418,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, con
   g.dv = dv;
   g.dbeta = dbeta;
   g.dla = dlog_alpha;
-  g.x = reinterpret_cast<float *>(ws + L.x_off);
-  g.dstates = reinterpret_cast<float *>(ws + L.ds_off);
+  g.x = ws + L.x_off;
+  g.dstates = ws + L.ds_off;
   if ((s = launched(gdr::launch_prep(a, in_bf16, st), "prep kernel (backward operands)")) != GDR_OK) return s;
   if ((s = launched(gdr::launch_bwd_scan(a, g, in_bf16, g_bf16, st), "reverse scan kernel")) != GDR_OK) return s;
   return launched(gdr::launch_bwd_grad(a, g, in_bf16, g_bf16, st), "gradient kernel");

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(64 * kBScanWaves) void bscan_kernel(ChunkArgs a, Bw
   static_assert(NB * NT == kBScanWaves && SPW * kBScanWaves == NCB * NT, "job split");
   using IO = TileIO<P>;
   using Plain = typename P::Plain;
+  using WT = typename std::conditional<P::kF32, float, f16>::type;   // X and dS_c in the workspace
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   StateLds<P> sT;
@@ -213,12 +214,13 @@ __global__ __launch_bounds__(64 * kBScanWaves) void bscan_kernel(ChunkArgs a, Bw
     put_al();                                          // last readers (previous chunk) were before its final barrier
     put_do();
     {
-      float *ds = g.dstates + (((size_t)b * a.H_v + hv) * NC + c) * DK * a.d_v;
+      WT *ds = static_cast<WT *>(g.dstates) + (((size_t)b * a.H_v + hv) * NC + c) * DK * a.d_v;
 #pragma unroll
       for (int r = 0; r < SPW; ++r) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          __builtin_nontemporal_store(dS[r][e], ds + (size_t)(16 * sb(r) + 4 * lq + e) * a.d_v + c0 + 16 * sn(r) + lr);
+          __builtin_nontemporal_store(static_cast<WT>(dS[r][e]),
+                                      ds + (size_t)(16 * sb(r) + 4 * lq + e) * a.d_v + c0 + 16 * sn(r) + lr);
       }
     }
     __syncthreads();
@@ -236,7 +238,9 @@ __global__ __launch_bounds__(64 * kBScanWaves) void bscan_kernel(ChunkArgs a, Bw
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = c * C + C - 1 - (16 * XI + 4 * lq + e);
-        if (row < T) g.x[((size_t)b * T + row) * vrow + (size_t)hv * a.d_v + c0 + 16 * Xn + lr] = acc[e];
+        if (row < T)
+          static_cast<WT *>(g.x)[((size_t)b * T + row) * vrow + (size_t)hv * a.d_v + c0 + 16 * Xn + lr] =
+              static_cast<WT>(acc[e]);
       }
     }
     load_kb(cn);
@@ -427,8 +431,8 @@ __global__ __launch_bounds__(512) void bgrad_kernel(ChunkArgs a, BwdArgs g) {
       for (int i = tid; i < DK * VS / 4; i += 512) {
         const int rr = i / (VS / 4), cc = 4 * (i % (VS / 4));
         const size_t o = sidx + (size_t)rr * a.d_v + v0 + cc;
-        *reinterpret_cast<float4 *>(sp + rr * LDV + cc) = *reinterpret_cast<const float4 *>(g.states + o);
-        *reinterpret_cast<float4 *>(dss + rr * LDV + cc) = *reinterpret_cast<const float4 *>(g.dstates + o);
+        *reinterpret_cast<float4 *>(sp + rr * LDV + cc) = *reinterpret_cast<const float4 *>(static_cast<const float *>(g.states) + o);
+        *reinterpret_cast<float4 *>(dss + rr * LDV + cc) = *reinterpret_cast<const float4 *>(static_cast<const float *>(g.dstates) + o);
       }
       for (int i = tid; i < C * VS / 4; i += 512) {
         const int t = i / (VS / 4), cc = 4 * (i % (VS / 4));
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(512) void bgrad_kernel(ChunkArgs a, BwdArgs g) {
             make_float4(ldf(pg) * m, ldf(pg + 1) * m, ldf(pg + 2) * m, ldf(pg + 3) * m);
         *reinterpret_cast<float4 *>(vy + t * LDV + cc) =
             make_float4(ldf(pv) * m, ldf(pv + 1) * m, ldf(pv + 2) * m, ldf(pv + 3) * m);
-        const float4 xv = *reinterpret_cast<const float4 *>(g.x + o);
+        const float4 xv = *reinterpret_cast<const float4 *>(static_cast<const float *>(g.x) + o);
         const float4 dv = *reinterpret_cast<const float4 *>(g.dv + o);
         *reinterpret_cast<float4 *>(xs + t * LDV + cc) = make_float4(xv.x * m, xv.y * m, xv.z * m, xv.w * m);
         *reinterpret_cast<float4 *>(dd + t * LDV + cc) = make_float4(dv.x * m, dv.y * m, dv.z * m, dv.w * m);
@@ -654,6 +658,473 @@ __global__ __launch_bounds__(512) void bgrad_kernel(ChunkArgs a, BwdArgs g) {
   }
 }
 
+// ------------------------------------------- gradient kernel, fp16 operands
+// The same computation for bf16 inputs with every product on fp16 MFMA
+// (fp32 accumulation): operands are rounded once to fp16 in LDS, as the
+// forward's scan operands are.  The d_v products use 16x16x32 tiles; the
+// pair sums go over 16-token blocks (16x16x16 tiles) with block pivots, so
+// that every fp16 operand stays in range whatever the decay:
+//   row side   (t in block I, j in block J <= I): pivot p = first token of I,
+//              P_tj = e^{Lambda_t - Lambda_p} e^{Lambda_p - Lambda_j};
+//   column side (j in block J, t in block I >= J): pivot p' = last token of
+//              J, P_tj = e^{Lambda_t - Lambda_p'} e^{Lambda_p' - Lambda_j}.
+// Off the diagonal both factors are <= 1 (log alpha <= 0); on a diagonal
+// block one factor is at most e^{range of Lambda over the block}, so a block
+// whose range exceeds kDiagRange in some channel is summed entry by entry,
+// and a chunk with a positive log alpha is summed entry by entry throughout.
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+constexpr float kDiagRange = 8.f;   // e^8 ~ 3e3: pivoted unit-norm keys stay far inside fp16
+
+__device__ __forceinline__ f32x4 mfma_k16(const f16x4 &a, const f16x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+template <int DK>
+struct Grad16Layout {
+  static constexpr int C = kBwdC, VS = 32;
+  static constexpr int LDK = DK + 4;          // fp32 rows of Lambda, K, Q
+  static constexpr int KLD = DK + 8;          // fp16 rows of Kbar and S^T
+  static constexpr int CLD = C + 8;           // fp16 rows of A, G, Y^T
+  static constexpr int SLD = VS + 8;          // fp16 rows of the slab operands
+  static constexpr int PLD = C + 4;           // fp16 rows of dL, dG and their transposes
+  static constexpr int VLD = VS + 4;          // fp32 rows of V
+  static constexpr size_t lam = 0;
+  static constexpr size_t kb = lam + 4 * (size_t)C * LDK;
+  static constexpr size_t au = kb + 2 * (size_t)C * KLD;
+  static constexpr size_t gu = au + 2 * (size_t)C * CLD;
+  static constexpr size_t mats_end = gu + 2 * (size_t)C * CLD;
+  static constexpr size_t pm = kb;            // after the slabs: dL, dG, dL^T, dG^T
+  static constexpr size_t pm_end = pm + 4 * 2 * (size_t)C * PLD;
+  static constexpr size_t slab = mats_end > pm_end ? mats_end : pm_end;
+  static constexpr size_t sa = slab;                          // S_{c-1}[:, slab]   [DK][SLD]
+  static constexpr size_t sb = sa + 2 * (size_t)DK * SLD;     // its transpose      [VS][KLD]
+  static constexpr size_t dsa = sb + 2 * (size_t)VS * KLD;    // dS_c[:, slab]      [DK][SLD]
+  static constexpr size_t doh = dsa + 2 * (size_t)DK * SLD;   // dO, D, E~, E, X    [C][SLD] each
+  static constexpr size_t dh = doh + 2 * (size_t)C * SLD;
+  static constexpr size_t eth = dh + 2 * (size_t)C * SLD;
+  static constexpr size_t eh = eth + 2 * (size_t)C * SLD;
+  static constexpr size_t xh = eh + 2 * (size_t)C * SLD;
+  static constexpr size_t yt = xh + 2 * (size_t)C * SLD;      // Y^T [VS][CLD]
+  static constexpr size_t vf = yt + 2 * (size_t)VS * CLD;     // V fp32 [C][VLD]
+  static constexpr size_t slab_end = vf + 4 * (size_t)C * VLD;
+  static constexpr size_t ks = slab, qs = ks + 4 * (size_t)C * LDK;   // after the slabs: K, Q rows fp32
+  static constexpr size_t kq_end = qs + 4 * (size_t)C * LDK;
+  static constexpr size_t misc = slab_end > kq_end ? slab_end : kq_end;
+  static constexpr size_t bet = misc;                         // floats: beta [C], dbeta parts [2][C],
+  static constexpr size_t dbp = bet + 4 * C;                  //   column sums [C], dgamma [DK],
+  static constexpr size_t dbcol = dbp + 4 * 2 * C;            //   Lambda_C terms [DK], flags
+  static constexpr size_t dgam = dbcol + 4 * C;
+  static constexpr size_t dlast = dgam + 4 * DK;
+  static constexpr size_t flags = dlast + 4 * DK;
+  static constexpr size_t bytes = flags + 4 * 8;
+  static_assert(bytes <= 160 * 1024, "gradient kernel LDS");
+  static_assert(4 * (size_t)C * DK <= slab_end - slab, "log alpha staging fits the slab region");
+};
+
+template <typename TIn, typename TG, int DK>
+__global__ __launch_bounds__(512) void bgrad16_kernel(ChunkArgs a, BwdArgs g) {
+  constexpr int C = kBwdC, VS = 32, NB = C / 16;
+  constexpr int HCT = DK / 32;                         // channel tiles per half
+  using Lay = Grad16Layout<DK>;
+  constexpr int LDK = Lay::LDK, KLD = Lay::KLD, CLD = Lay::CLD, SLD = Lay::SLD, PLD = Lay::PLD, VLD = Lay::VLD;
+  extern __shared__ __align__(16) unsigned char sm8[];
+  float *lam = reinterpret_cast<float *>(sm8 + Lay::lam);
+  f16 *kb = reinterpret_cast<f16 *>(sm8 + Lay::kb), *au = reinterpret_cast<f16 *>(sm8 + Lay::au);
+  f16 *gu = reinterpret_cast<f16 *>(sm8 + Lay::gu);
+  f16 *dLh = reinterpret_cast<f16 *>(sm8 + Lay::pm), *dGh = dLh + C * PLD, *dLt = dGh + C * PLD, *dGt = dLt + C * PLD;
+  f16 *sa = reinterpret_cast<f16 *>(sm8 + Lay::sa), *sb = reinterpret_cast<f16 *>(sm8 + Lay::sb);
+  f16 *dsa = reinterpret_cast<f16 *>(sm8 + Lay::dsa), *doh = reinterpret_cast<f16 *>(sm8 + Lay::doh);
+  f16 *dh = reinterpret_cast<f16 *>(sm8 + Lay::dh), *eth = reinterpret_cast<f16 *>(sm8 + Lay::eth);
+  f16 *eh = reinterpret_cast<f16 *>(sm8 + Lay::eh), *xh = reinterpret_cast<f16 *>(sm8 + Lay::xh);
+  f16 *yt = reinterpret_cast<f16 *>(sm8 + Lay::yt);
+  float *vf = reinterpret_cast<float *>(sm8 + Lay::vf);
+  float *ks = reinterpret_cast<float *>(sm8 + Lay::ks), *qs = reinterpret_cast<float *>(sm8 + Lay::qs);
+  float *bet = reinterpret_cast<float *>(sm8 + Lay::bet), *dbp = reinterpret_cast<float *>(sm8 + Lay::dbp);
+  float *dbcol = reinterpret_cast<float *>(sm8 + Lay::dbcol), *dgam = reinterpret_cast<float *>(sm8 + Lay::dgam);
+  float *dlast = reinterpret_cast<float *>(sm8 + Lay::dlast);
+  int *flags = reinterpret_cast<int *>(sm8 + Lay::flags);   // [0]: a positive log alpha; [1 + I]: block I too wide
+
+  const int c = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), lr = l & 15, lq = l >> 4;
+  const int I = w & 3, h = w >> 2;
+  const int T = a.T, t0 = c * C, nv = min(C, T - t0);
+  const int R = a.H_v / a.H_k, G = a.G, gs = a.gshift;
+  const TIn *qp = reinterpret_cast<const TIn *>(a.q) + (size_t)hk * DK;
+  const TIn *kp = reinterpret_cast<const TIn *>(a.k) + (size_t)hk * DK;
+  const TIn *vp = reinterpret_cast<const TIn *>(a.v);
+  const TIn *bp = reinterpret_cast<const TIn *>(a.beta);
+  const TIn *lap = reinterpret_cast<const TIn *>(a.log_alpha);
+  const TG *dop = reinterpret_cast<const TG *>(g.d_o);
+  const f16 *xg = static_cast<const f16 *>(g.x);
+  const f16 *dsg = static_cast<const f16 *>(g.dstates);
+  const size_t krow = (size_t)a.H_k * DK, vrow = (size_t)a.H_v * a.d_v;
+  const size_t row0 = (size_t)b * T + t0;
+  auto trow = [&](int t) { return row0 + (size_t)min(t, nv - 1); };
+  auto f4 = [](float x0, float x1, float x2, float x3) {
+    f16x4 r;
+    r[0] = static_cast<f16>(x0); r[1] = static_cast<f16>(x1); r[2] = static_cast<f16>(x2); r[3] = static_cast<f16>(x3);
+    return r;
+  };
+
+  // ---- Lambda, the rising flag and the diagonal blocks' decay ranges
+  float *las = reinterpret_cast<float *>(sm8 + Lay::slab);
+  for (int i = tid; i < C * G; i += 512) {
+    const int t = i / G, q = i % G;
+    const float x = ldf(lap + (trow(t) * a.H_k + hk) * G + q);
+    las[i] = t < nv ? x : 0.f;
+  }
+  if (tid < 8) flags[tid] = 0;
+  __syncthreads();
+  if (tid < DK) {
+    const int q = tid >> gs;
+    float run = 0.f;
+    bool rising = false;
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      float lo = 0.f, hi = 0.f;
+      for (int u = 0; u < 16; ++u) {
+        const float x = las[(16 * J + u) * G + q];
+        rising |= x > 0.f;
+        run += x;
+        lam[(16 * J + u) * LDK + tid] = run;
+        lo = u ? fminf(lo, run) : run;
+        hi = u ? fmaxf(hi, run) : run;
+      }
+      if (!(hi - lo <= kDiagRange)) flags[1 + J] = 1;   // several threads may store the same 1
+    }
+    if (rising) flags[0] = 1;
+  }
+  __syncthreads();
+  // ---- Kbar = K (.) e^Lambda and G_c as fp16 operands
+  for (int i = tid; i < C * DK / 4; i += 512) {
+    const int t = i / (DK / 4), ch = 4 * (i % (DK / 4));
+    const TIn *pk = kp + trow(t) * krow + ch;
+    const float m = t < nv ? 1.f : 0.f;
+    const float4 lv = *reinterpret_cast<const float4 *>(lam + t * LDK + ch);
+    *reinterpret_cast<f16x4 *>(kb + t * KLD + ch) =
+        f4(ldf(pk) * m * __expf(lv.x), ldf(pk + 1) * m * __expf(lv.y), ldf(pk + 2) * m * __expf(lv.z),
+           ldf(pk + 3) * m * __expf(lv.w));
+  }
+  {
+    const float *gsrc = a.gu + (((size_t)b * a.H_k + hk) * a.N_c + c) * (C * C);
+    for (int i = tid; i < C * C / 4; i += 512) {
+      const int r = i / (C / 4), cc = 4 * (i % (C / 4));
+      const float4 x = *reinterpret_cast<const float4 *>(gsrc + r * C + cc);
+      *reinterpret_cast<f16x4 *>(gu + r * CLD + cc) = f4(x.x, x.y, x.z, x.w);
+    }
+  }
+
+  // One slab's inputs, fetched into registers one slab ahead: 4-column
+  // pieces of S_{c-1} and dS_c (SQ per thread) and of the dO, D, X and V rows
+  // (one per thread).
+  constexpr int SQ = DK * VS / 4 / 512;
+  static_assert(SQ >= 1 && SQ * 512 * 4 == DK * VS && C * VS / 4 == 512, "slab pieces");
+  const f16 *stg = static_cast<const f16 *>(g.states);
+  f16x4 rS[SQ], rdS[SQ], rX;
+  float4 rdO, rD, rV;
+  const int pt = tid / (VS / 4), pv = 4 * (tid % (VS / 4));
+  auto fetch = [&](int hv, int v0) {
+    const size_t sidx = (((size_t)b * a.H_v + hv) * a.N_c + c) * DK * a.d_v;
+#pragma unroll
+    for (int q = 0; q < SQ; ++q) {
+      const int i = tid + 512 * q, rr = i / (VS / 4), vq = 4 * (i % (VS / 4));
+      const size_t o = sidx + (size_t)rr * a.d_v + v0 + vq;
+      rS[q] = *reinterpret_cast<const f16x4 *>(stg + o);
+      rdS[q] = *reinterpret_cast<const f16x4 *>(dsg + o);
+    }
+    const size_t o = trow(pt) * vrow + (size_t)hv * a.d_v + v0 + pv;
+    rdO = make_float4(ldf(dop + o), ldf(dop + o + 1), ldf(dop + o + 2), ldf(dop + o + 3));
+    rD = *reinterpret_cast<const float4 *>(g.dv + o);
+    rX = *reinterpret_cast<const f16x4 *>(xg + o);
+    rV = make_float4(ldf(vp + o), ldf(vp + o + 1), ldf(vp + o + 2), ldf(vp + o + 3));
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int q = 0; q < SQ; ++q) {
+      const int i = tid + 512 * q, rr = i / (VS / 4), vq = 4 * (i % (VS / 4));
+      *reinterpret_cast<f16x4 *>(sa + rr * SLD + vq) = rS[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sb[(vq + e) * KLD + rr] = rS[q][e];
+      *reinterpret_cast<f16x4 *>(dsa + rr * SLD + vq) = rdS[q];
+    }
+    const float m = pt < nv ? 1.f : 0.f;             // rows past T: zero
+    *reinterpret_cast<f16x4 *>(doh + pt * SLD + pv) = f4(rdO.x * m, rdO.y * m, rdO.z * m, rdO.w * m);
+    *reinterpret_cast<f16x4 *>(dh + pt * SLD + pv) = f4(rD.x * m, rD.y * m, rD.z * m, rD.w * m);
+    *reinterpret_cast<f16x4 *>(xh + pt * SLD + pv) = pt < nv ? rX : f16x4{};
+    *reinterpret_cast<float4 *>(vf + pt * VLD + pv) = make_float4(rV.x * m, rV.y * m, rV.z * m, rV.w * m);
+  };
+  // dgamma: TPR threads per state row, VPT columns each
+  constexpr int TPR = 512 / DK, VPT = VS / TPR;
+  const int gr = tid / TPR, gc = (tid % TPR) * VPT;
+
+  f32x4 aQ[HCT], aKb[HCT], aKh[HCT], aL[2], aG[2];
+#pragma unroll
+  for (int n = 0; n < HCT; ++n) aQ[n] = aKb[n] = aKh[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  aL[0] = aL[1] = aG[0] = aG[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dgacc = 0.f, dbk = 0.f;
+
+  fetch(hk * R, 0);
+  for (int r = 0; r < R; ++r) {
+    const int hv = hk * R + r, hb = a.beta_per_key_head ? hk : hv;
+    __syncthreads();                                   // the previous head's readers are done
+    if (r == 0 || !a.beta_per_key_head) {
+      const float *asrc = a.au + (((size_t)b * a.H_beta + hb) * a.N_c + c) * (C * C);
+      for (int i = tid; i < C * C / 4; i += 512) {
+        const int rr = i / (C / 4), cc = 4 * (i % (C / 4));
+        const float4 x = *reinterpret_cast<const float4 *>(asrc + rr * C + cc);
+        *reinterpret_cast<f16x4 *>(au + rr * CLD + cc) = f4(x.x, x.y, x.z, x.w);
+      }
+      if (tid < C) {
+        const float x = ldf(bp + trow(tid) * a.H_beta + hb);
+        bet[tid] = tid < nv ? x : 0.f;
+      }
+    }
+    if (tid < C) dbcol[tid] = 0.f;
+    f32x4 aP[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // D E~^T of this head
+    float dbl = 0.f;                                   // sum_v E~ X of token 16 I + lr (this lane's rows)
+    for (int v0 = 0; v0 < a.d_v; v0 += VS) {
+      __syncthreads();                                 // the previous slab's readers are done
+      stage();
+      if (v0 + VS < a.d_v) {
+        fetch(hv, v0 + VS);
+      } else if (r + 1 < R) {
+        fetch(hv + 1, 0);
+      }
+      __syncthreads();
+      {                                                // Y = V - Kbar S_{c-1}: tile (t block I, v tile h) -> Y^T
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s)
+          acc = mfma_f16(*reinterpret_cast<const f16x8 *>(kb + (16 * I + lr) * KLD + 32 * s + 8 * lq),
+                         *reinterpret_cast<const f16x8 *>(sb + (16 * h + lr) * KLD + 32 * s + 8 * lq), acc);
+        const int t = 16 * I + 4 * lq, v = 16 * h + lr;
+        *reinterpret_cast<f16x4 *>(yt + v * CLD + t) =
+            f4(vf[t * VLD + v] - acc[0], vf[(t + 1) * VLD + v] - acc[1], vf[(t + 2) * VLD + v] - acc[2],
+               vf[(t + 3) * VLD + v] - acc[3]);
+      }
+      __syncthreads();
+      {                                                // E~^T = Y^T A^T: tile (v tile h, t block I)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < C / 32; ++s) {
+          if (2 * s > I) continue;                     // A is lower triangular
+          acc = mfma_f16(*reinterpret_cast<const f16x8 *>(yt + (16 * h + lr) * CLD + 32 * s + 8 * lq),
+                         *reinterpret_cast<const f16x8 *>(au + (16 * I + lr) * CLD + 32 * s + 8 * lq), acc);
+        }
+        const int t = 16 * I + lr, v = 16 * h + 4 * lq;
+        const float bt = bet[t];
+        const f16x4 xv = *reinterpret_cast<const f16x4 *>(xh + t * SLD + v);
+        *reinterpret_cast<f16x4 *>(eth + t * SLD + v) = f4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<f16x4 *>(eh + t * SLD + v) = f4(bt * acc[0], bt * acc[1], bt * acc[2], bt * acc[3]);
+        dbl += acc[0] * static_cast<float>(xv[0]) + acc[1] * static_cast<float>(xv[1]) +
+               acc[2] * static_cast<float>(xv[2]) + acc[3] * static_cast<float>(xv[3]);
+      }
+      __syncthreads();
+      {                                                // products over the slab's 32 value columns
+        const f16x8 adO = *reinterpret_cast<const f16x8 *>(doh + (16 * I + lr) * SLD + 8 * lq);
+        const f16x8 aD = *reinterpret_cast<const f16x8 *>(dh + (16 * I + lr) * SLD + 8 * lq);
+        const f16x8 aE = *reinterpret_cast<const f16x8 *>(eh + (16 * I + lr) * SLD + 8 * lq);
+#pragma unroll
+        for (int n = 0; n < HCT; ++n) {
+          const int nt = h * HCT + n;
+          const f16x8 bS = *reinterpret_cast<const f16x8 *>(sa + (16 * nt + lr) * SLD + 8 * lq);
+          const f16x8 bdS = *reinterpret_cast<const f16x8 *>(dsa + (16 * nt + lr) * SLD + 8 * lq);
+          aQ[n] = mfma_f16(adO, bS, aQ[n]);
+          aKb[n] = mfma_f16(aD, bS, aKb[n]);
+          aKh[n] = mfma_f16(aE, bdS, aKh[n]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int J = 2 * jj + h;
+          if (J > I) continue;
+          const f16x8 bE = *reinterpret_cast<const f16x8 *>(eh + (16 * J + lr) * SLD + 8 * lq);
+          const f16x8 bEt = *reinterpret_cast<const f16x8 *>(eth + (16 * J + lr) * SLD + 8 * lq);
+          aL[jj] = mfma_f16(adO, bE, aL[jj]);
+          aP[jj] = mfma_f16(aD, bEt, aP[jj]);
+        }
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+          dgacc += static_cast<float>(sa[gr * SLD + gc + v]) * static_cast<float>(dsa[gr * SLD + gc + v]);
+      }
+    }
+    // dbeta_j = sum_v E~_jv X_jv - sum_{t>j} G_tj (D E~^T)_tj; dG -= (D E~^T) diag(beta), strictly lower
+    dbl += __shfl_xor(dbl, 16);
+    dbl += __shfl_xor(dbl, 32);
+    if (lq == 0) dbp[h * C + 16 * I + lr] = dbl;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int J = 2 * jj + h;
+      if (J > I) continue;
+      const int j = 16 * J + lr;
+      const float bj = bet[j];
+      float s2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * lq + e;
+        const bool below = t > j;
+        const float pv = aP[jj][e];
+        s2 += below ? static_cast<float>(gu[t * CLD + j]) * pv : 0.f;
+        aG[jj][e] -= below ? pv * bj : 0.f;
+      }
+      atomicAdd(dbcol + j, s2);
+    }
+    __syncthreads();
+    if (tid < C) {
+      const float d = dbp[tid] + dbp[C + tid] - dbcol[tid];
+      if (a.beta_per_key_head) {
+        dbk += d;
+      } else if (tid < nv) {
+        g.dbeta[trow(tid) * a.H_v + hv] = d;
+      }
+    }
+  }
+  if (a.beta_per_key_head && tid < nv) g.dbeta[trow(tid) * a.H_k + hk] = dbk;
+
+  // ---- pair sums
+  __syncthreads();                                     // slab operands, Kbar, A and G are dead
+  load_key_rows<TIn, DK>(ks, kp, row0, krow, nv);
+  load_key_rows<TIn, DK>(qs, qp, row0, krow, nv);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int J = 2 * jj + h, j = 16 * J + lr;
+    f16x4 lv, gv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * I + 4 * lq + e;
+      lv[e] = static_cast<f16>((J <= I && t >= j) ? aL[jj][e] : 0.f);
+      gv[e] = static_cast<f16>((J <= I && t > j) ? aG[jj][e] : 0.f);
+      dLh[t * PLD + j] = lv[e];
+      dGh[t * PLD + j] = gv[e];
+    }
+    *reinterpret_cast<f16x4 *>(dLt + j * PLD + 16 * I + 4 * lq) = lv;
+    *reinterpret_cast<f16x4 *>(dGt + j * PLD + 16 * I + 4 * lq) = gv;
+  }
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) dgacc += __shfl_xor(dgacc, m);
+  if (tid % TPR == 0) dgam[gr] = dgacc;
+  if (tid < DK) dlast[tid] = 0.f;
+  __syncthreads();
+  const bool rising = flags[0] != 0;
+  const bool diag_wide = flags[1 + I] != 0;
+  f32x4 pq[HCT], pr[HCT], pc[HCT];                      // sum_j dL P k, sum_j dG P k, sum_t (dG k + dL q) P
+#pragma unroll
+  for (int n = 0; n < HCT; ++n) {
+    const int ch = 16 * (h * HCT + n) + lr;
+    pq[n] = pr[n] = pc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!rising) {
+      const float lp = lam[16 * I * LDK + ch], lpc = lam[(16 * I + 15) * LDK + ch];
+      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ar = aq, ac = aq;
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        if (J < I || (J == I && !diag_wide)) {         // row side: j in block J
+          f16x4 bk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * J + 4 * lq + e;
+            bk[e] = static_cast<f16>(ks[j * LDK + ch] * __expf(lp - lam[j * LDK + ch]));
+          }
+          aq = mfma_k16(*reinterpret_cast<const f16x4 *>(dLh + (16 * I + lr) * PLD + 16 * J + 4 * lq), bk, aq);
+          ar = mfma_k16(*reinterpret_cast<const f16x4 *>(dGh + (16 * I + lr) * PLD + 16 * J + 4 * lq), bk, ar);
+        }
+        if (J > I || (J == I && !diag_wide)) {         // column side: t in block J
+          f16x4 bk, bq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * J + 4 * lq + e;
+            const float f = __expf(lam[t * LDK + ch] - lpc);
+            bk[e] = static_cast<f16>(ks[t * LDK + ch] * f);
+            bq[e] = static_cast<f16>(qs[t * LDK + ch] * f);
+          }
+          ac = mfma_k16(*reinterpret_cast<const f16x4 *>(dGt + (16 * I + lr) * PLD + 16 * J + 4 * lq), bk, ac);
+          ac = mfma_k16(*reinterpret_cast<const f16x4 *>(dLt + (16 * I + lr) * PLD + 16 * J + 4 * lq), bq, ac);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lt = lam[(16 * I + 4 * lq + e) * LDK + ch];
+        const float rf = __expf(lt - lp), cf = __expf(lpc - lt);
+        pq[n][e] = aq[e] * rf;
+        pr[n][e] = ar[e] * rf;
+        pc[n][e] = ac[e] * cf;
+      }
+    }
+    if (rising || diag_wide) {
+      // pairs summed entry by entry, causal side only: all pairs of the chunk
+      // (rising), or those inside this row block's diagonal block
+      const int lo = rising ? 0 : 16 * I, hi = rising ? C : 16 * I + 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * I + 4 * lq + e;
+        const float lt = lam[t * LDK + ch];
+        float sq = 0.f, sr = 0.f, sc = 0.f;
+        for (int j = lo; j <= t; ++j) {
+          const float kj = ks[j * LDK + ch] * __expf(lt - lam[j * LDK + ch]);
+          sq += static_cast<float>(dLh[t * PLD + j]) * kj;
+          sr += static_cast<float>(dGh[t * PLD + j]) * kj;
+        }
+        for (int s = t; s < hi; ++s) {
+          const float p = __expf(lam[s * LDK + ch] - lt);
+          sc += (static_cast<float>(dGh[s * PLD + t]) * ks[s * LDK + ch] +
+                 static_cast<float>(dLh[s * PLD + t]) * qs[s * LDK + ch]) * p;
+        }
+        pq[n][e] += sq;
+        pr[n][e] += sr;
+        pc[n][e] += sc;
+      }
+    }
+  }
+  // ---- dq, dk and dLambda of the lane's entries
+  float dl[HCT][4];
+#pragma unroll
+  for (int n = 0; n < HCT; ++n) {
+    const int ch = 16 * (h * HCT + n) + lr;
+    const float lc = lam[(C - 1) * LDK + ch];
+    float last = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * I + 4 * lq + e;
+      const float lt = lam[t * LDK + ch];
+      const float ex = __expf(lt), hx = __expf(lc - lt);
+      const float kv = ks[t * LDK + ch], qv = qs[t * LDK + ch];
+      const float dQb = aQ[n][e], dKb = -aKb[n][e], dKh = aKh[n][e];
+      const float dqv = dQb * ex + pq[n][e];
+      const float dkv = dKb * ex + dKh * hx + pr[n][e] + pc[n][e];
+      dl[n][e] = qv * dqv + kv * (dKb * ex + pr[n][e] - pc[n][e] - dKh * hx);
+      last += kv * dKh * hx;
+      if (t < nv) {
+        const size_t o = (trow(t) * a.H_k + hk) * DK + ch;
+        g.dq[o] = dqv;
+        g.dk[o] = dkv;
+      }
+    }
+    atomicAdd(dlast + ch, last);
+  }
+  __syncthreads();                                     // every read of the K and Q rows is done
+  float *dlam = ks;
+#pragma unroll
+  for (int n = 0; n < HCT; ++n) {
+    const int ch = 16 * (h * HCT + n) + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dlam[(16 * I + 4 * lq + e) * LDK + ch] = dl[n][e];
+  }
+  __syncthreads();
+  if (tid < DK) {
+    float run = dlast[tid] + dgam[tid] * __expf(lam[(C - 1) * LDK + tid]);
+    for (int t = C - 1; t >= 0; --t) {
+      run += dlam[t * LDK + tid];
+      dlam[t * LDK + tid] = run;
+    }
+  }
+  __syncthreads();
+  const int cpg = DK / G;
+  for (int i = tid; i < nv * G; i += 512) {
+    const int t = i / G, q = i % G;
+    float s = 0.f;
+    for (int j = 0; j < cpg; ++j) s += dlam[t * LDK + q * cpg + j];
+    g.dla[(trow(t) * a.H_k + hk) * G + q] = s;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename TG, class P, int DK>
 static hipError_t launch_bscan_t(const ChunkArgs &a, const BwdArgs &g, hipStream_t s) {
@@ -680,10 +1151,19 @@ hipError_t launch_bwd_scan(const ChunkArgs &a, const BwdArgs &g, bool in_bf16, b
 
 template <typename TIn, typename TG, int DK>
 static hipError_t launch_grad_t(const ChunkArgs &a, const BwdArgs &g, hipStream_t s) {
-  auto kern = bgrad_kernel<TIn, TG, DK>;
+  // fp32 inputs: every product in fp32; bf16 inputs: fp16 operands
+  void (*kern)(ChunkArgs, BwdArgs);
+  size_t lds;
+  if constexpr (std::is_same<TIn, float>::value) {
+    kern = bgrad_kernel<TIn, TG, DK>;
+    lds = GradLayout<DK>::bytes;
+  } else {
+    kern = bgrad16_kernel<TIn, TG, DK>;
+    lds = Grad16Layout<DK>::bytes;
+  }
   hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.N_c, a.H_k, a.B), dim3(512), GradLayout<DK>::bytes, s, a, g);
+  hipLaunchKernelGGL(kern, dim3(a.N_c, a.H_k, a.B), dim3(512), lds, s, a, g);
   return hipGetLastError();
 }
 

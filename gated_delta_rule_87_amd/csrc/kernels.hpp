@@ -71,8 +71,9 @@ struct ChunkArgs {
   size_t h0_seg_stride;
   float *xfer;
   // Training forward: the scan stores the state entering every chunk,
-  // S_{c-1}, to states [B][H_v][N_c][d_k][d_v] (fp32; nullable).
-  float *states;
+  // S_{c-1}, to states [B][H_v][N_c][d_k][d_v] (nullable; fp16 for bf16
+  // inputs, fp32 for fp32 inputs).
+  void *states;
   // Backward preparation (bwd != 0): the prep kernels write the operands of
   // the reverse scan in place of the forward ones -- in reversed token order
   // within the chunk (J the reversal) region A holds J (diag(beta) A_c)^T J,
@@ -106,14 +107,15 @@ struct StepArgs {
 struct BwdArgs {
   const void *d_o;            // [B, T, H_v, d_v] out_dtype
   const float *dhT;           // nullable [B, H_v, d_k, d_v]
-  const float *states;        // S_{c-1} of every chunk, [B][H_v][N_c][d_k][d_v]
+  const void *states;         // S_{c-1} of every chunk, [B][H_v][N_c][d_k][d_v] (fp16 / fp32 as above)
   float *dq, *dk;             // [B, T, H_k, d_k]
   float *dv;                  // [B, T, H_v, d_v]
   float *dbeta;               // [B, T, H_beta]
   float *dla;                 // [B, T, H_k, G]
   float *dh0;                 // nullable [B, H_v, d_k, d_v]
-  float *x;                   // workspace: X_c = L_c^T dO_c + Khat_c dS_c, [B, T, H_v, d_v]
-  float *dstates;             // workspace: dS_c of every chunk, [B][H_v][N_c][d_k][d_v]
+  // workspace, fp16 for bf16 inputs and fp32 for fp32 inputs:
+  void *x;                    // X_c = L_c^T dO_c + Khat_c dS_c, [B, T, H_v, d_v]
+  void *dstates;              // dS_c of every chunk, [B][H_v][N_c][d_k][d_v]
 };
 
 // Drafted tokens one verification call takes.
@@ -154,7 +156,7 @@ namespace gdr {
 gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
                          const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
                          size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts,
-                         float *states = nullptr);
+                         void *states = nullptr);
 // Workspace bytes of a valid problem (else the validation status).
 gdr_status workspace_bytes_of(const gdr_problem *p, size_t *bytes);
 // Record `text` as this thread's gdr_last_error() and return s.

@@ -367,7 +367,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     constexpr bool kTail = decltype(tail_tag)::value;
     const int c1 = last(c + 1);
     if constexpr (kSave) {
-      float *st = a.states + (((size_t)b * a.H_v + hv) * a.N_c + c) * DK * a.d_v;
+      using ST = typename std::conditional<P::kF32, float, f16>::type;   // fp16 for bf16 inputs
+      ST *st = static_cast<ST *>(a.states) + (((size_t)b * a.H_v + hv) * a.N_c + c) * DK * a.d_v;
 #pragma unroll
       for (int r = 0; r < SJ::RPW; ++r) {
         const int i0 = 16 * SJ::blk(w, r);
@@ -377,7 +378,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
           if (!SJ::kAllTiles && n >= NT) continue;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(S[r][u][e], st + (size_t)(i0 + 4 * lq + e) * a.d_v + c0 + 16 * n + lr);
+            __builtin_nontemporal_store(static_cast<ST>(S[r][u][e]),
+                                        st + (size_t)(i0 + 4 * lq + e) * a.d_v + c0 + 16 * n + lr);
         }
       }
     }

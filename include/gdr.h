@@ -246,8 +246,11 @@ gdr_status gdr_chunk_fwd_ex(const gdr_problem *p, const gdr_layer_opts *opts, co
  * solve, in_dtype bf16 or f32; no layer options (resets, momentum).  Other
  * problems return GDR_ERR_UNSUPPORTED (size functions: 0).
  *
- * gdr_chunk_states_size: bytes of `states`, fp32 [B, H_v, N_c, d_k, d_v]
- * (N_c = ceil(T / chunk)): S_{c-1} of every chunk c, S_{-1} = h0 (or 0).
+ * gdr_chunk_states_size: bytes of `states`, [B, H_v, N_c, d_k, d_v]
+ * (N_c = ceil(T / chunk)): S_{c-1} of every chunk c, S_{-1} = h0 (or 0),
+ * fp16 for bf16 inputs (round to nearest even: the value the forward's
+ * state operand of that chunk holds, and the precision the gradient
+ * kernel multiplies it in) and fp32 for fp32 inputs.
  *
  * gdr_chunk_fwd_train: gdr_chunk_fwd (same arguments, workspace size and
  * results) that also writes `states` (16-byte aligned; NULL allowed only
@@ -256,7 +259,7 @@ gdr_status gdr_chunk_fwd_ex(const gdr_problem *p, const gdr_layer_opts *opts, co
 size_t gdr_chunk_states_size(const gdr_problem *p);
 gdr_status gdr_chunk_fwd_train(const gdr_problem *p, const void *q, const void *k, const void *v,
                                const void *beta, const void *log_alpha, const float *h0, void *o,
-                               float *hT, float *states, void *workspace, size_t workspace_bytes,
+                               float *hT, void *states, void *workspace, size_t workspace_bytes,
                                void *stream);
 
 /*
@@ -264,8 +267,9 @@ gdr_status gdr_chunk_fwd_train(const gdr_problem *p, const void *q, const void *
  * problem): the six operand regions of gdr_chunk_fwd_workspace_size (no
  * segment region) holding the reverse scan's operands, A_c and G_c in fp32
  * ([B][H_beta][N_c][C][C] and [B][H_k][N_c][C][C]), X_c = L_c^T dO_c +
- * Khat_c dS_c (fp32 [B, T, H_v, d_v]) and dS_c of every chunk (fp32
- * [B, H_v, N_c, d_k, d_v]), each at a 256-byte boundary.
+ * Khat_c dS_c ([B, T, H_v, d_v]) and dS_c of every chunk ([B, H_v, N_c, d_k,
+ * d_v]), the last two fp16 for bf16 inputs and fp32 for fp32 inputs, each
+ * region at a 256-byte boundary.
  */
 size_t gdr_chunk_bwd_workspace_size(const gdr_problem *p);
 
@@ -286,7 +290,7 @@ size_t gdr_chunk_bwd_workspace_size(const gdr_problem *p);
  * per-chunk gradient kernel (dq, dk, dbeta, dlog_alpha; all chunks at once).
  */
 gdr_status gdr_chunk_bwd(const gdr_problem *p, const void *q, const void *k, const void *v,
-                         const void *beta, const void *log_alpha, const float *states, const void *d_o,
+                         const void *beta, const void *log_alpha, const void *states, const void *d_o,
                          const float *dhT, float *dq, float *dk, float *dv, float *dbeta,
                          float *dlog_alpha, float *dh0, void *workspace, size_t workspace_bytes,
                          void *stream);
