@@ -32,7 +32,9 @@ In-chunk inverses:
   under which ||A||^{m+1}/(1-||A||) bounds the tail), followed by r parallel
   residual corrections X <- X + X (I - (I + M) X).
 * :func:`block_neumann_inverse` is the block-Jacobi form of section 2.4.3's
-  block-Neumann factorisation, sum_{s<terms} (-N)^s D_blk^{-1}.
+  block-Neumann factorisation, sum_{s<terms} (-N)^s D_blk^{-1}; with
+  16-row blocks and two terms it is the 1-Step Neumann inverse
+  A_N1 = (I - N) D_blk^{-1} (``solve="block_neumann"``, order 1).
 
 Document resets and chunk-boundary momentum (Table 2: Z_c, mu, kappa_c;
 section 2.3, "Why chunk-level momentum"): a reset at token t discards the
@@ -108,11 +110,20 @@ def block_neumann_inverse(M, block, terms):
     return X @ Dinv
 
 
+BLOCK_NEUMANN_ROWS = 16   # B_blk of the 1-Step Neumann setting in section 2.4.3
+
+
 def invert(M, solve="exact", order=4, residual_steps=1):
+    """``order`` m: the Neumann series keeps powers 0..m of -M (then
+    ``residual_steps`` corrections); the block-Neumann form keeps powers 0..m
+    of -N (m = 1 is the pages' 1-Step Neumann, (I - N) D^{-1}; no residual
+    step)."""
     if solve == "exact":
         return exact_inverse(M)
     if solve == "neumann":
         return neumann_inverse(M, order, residual_steps)
+    if solve == "block_neumann":
+        return block_neumann_inverse(M, BLOCK_NEUMANN_ROWS, order + 1)
     if solve == "block_doubling":
         return block_doubling_inverse(M)
     raise ValueError(solve)

@@ -121,6 +121,58 @@ def test_block_neumann_identity():
     assert np.max(np.abs(ch.block_neumann_inverse(M, blk, C // blk - 1) - X)) > 1e-6
 
 
+def _blocks_inv(IM, blk):
+    return [np.linalg.inv(IM[s:s + blk, s:s + blk]) for s in range(0, IM.shape[0], blk)]
+
+
+def test_one_step_block_neumann_closed_forms():
+    """Systolic Linear Attention section 2.4.3, 1-Step Neumann A_N1 = (I - N) D^{-1}:
+    written block by block it is D_I^{-1} on the diagonal and
+    -D_I^{-1} M_IJ D_J^{-1} below it (every pair of block rows, not only
+    neighbours); with two block rows N^2 = 0 and it is the exact inverse; and
+    the truncation property exact - A_N1 = sum_{s>=2} (-N)^s D^{-1} holds."""
+    blk = 16
+    for C in (32, 64, 128):
+        M = _strict_lower(20 + C, C, 0.4)
+        IM = np.eye(C) + M
+        A1 = ch.invert(M, "block_neumann", order=1)
+        assert np.max(np.abs(A1 - ch.block_neumann_inverse(M, blk, 2))) == 0.0
+        Di = _blocks_inv(IM, blk)
+        want = np.zeros((C, C))
+        for I in range(C // blk):
+            rI = slice(I * blk, I * blk + blk)
+            want[rI, rI] = Di[I]
+            for J in range(I):
+                rJ = slice(J * blk, J * blk + blk)
+                want[rI, rJ] = -Di[I] @ M[rI, rJ] @ Di[J]
+        assert np.max(np.abs(A1 - want)) < 1e-12 * max(1.0, np.max(np.abs(want)))
+        if C == 2 * blk:
+            assert np.max(np.abs(A1 - ch.exact_inverse(M))) < 1e-12
+        else:
+            assert np.max(np.abs(A1 - ch.exact_inverse(M))) > 1e-6
+        D = np.zeros_like(IM)
+        for I, d in enumerate(Di):
+            D[I * blk:(I + 1) * blk, I * blk:(I + 1) * blk] = np.linalg.inv(d)
+        N = np.linalg.inv(D) @ (IM - D)
+        tail = sum((np.linalg.matrix_power(-N, s) for s in range(2, C // blk)), np.zeros((C, C))) @ np.linalg.inv(D)
+        ex = ch.exact_inverse(M)
+        assert np.max(np.abs(ex - A1 - tail)) < 1e-12 * np.max(np.abs(ex))
+        # a transposed order, (I - O D^{-1}) D^{-1}, is a different matrix
+        wrong = (np.eye(C) - (IM - D) @ np.linalg.inv(D)) @ np.linalg.inv(D)
+        assert C == 2 * blk or np.max(np.abs(wrong - A1)) > 1e-6
+
+
+def test_block_neumann_order_in_chunk_form():
+    """The chunk form with the block-Neumann solve of order m >= C/16 - 1 is
+    the exact chunk form (the series ends); order 1 departs from it."""
+    q, k, v, beta, la, h0 = oracle_pins.random_problem(5, B=1, T=70, Hk=1, Hv=2, dk=8, dv=4, G=8, h0=True)
+    o_e, h_e = ch.chunk_forward(q, k, v, beta, la, h0, chunk=64, solve="exact")
+    o_b, h_b = ch.chunk_forward(q, k, v, beta, la, h0, chunk=64, solve="block_neumann", order=3)
+    assert np.max(np.abs(o_b - o_e)) < 1e-10 and np.max(np.abs(h_b - h_e)) < 1e-10
+    o_1, _ = ch.chunk_forward(q, k, v, beta, la, h0, chunk=64, solve="block_neumann", order=1)
+    assert np.max(np.abs(o_1 - o_e)) > 1e-8
+
+
 def test_chunk_pieces_brute_force():
     """Each Table 2 quantity of one chunk against a brute-force evaluation of its
     definition with explicit products of the per-token gates."""
