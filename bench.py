@@ -2,7 +2,7 @@
 """Chunkwise gated delta-rule forward on one MI355X: throughput, roofline,
 and the fp64 CPU oracle timed beside it.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--solve exact|neumann]   (defaults 200, 400, 2)
+    python bench.py [--steps K] [--warmup W] [--config 2] [--solve exact|neumann|block_neumann]   (defaults 200, 400, 2)
     python bench.py --copy-calibration BYTES      # plain copy, for rocprofv3 --pmc scaling
     python bench.py --decode [--config 2] [--state-format e4m3]   # the recurrent step, one token per sequence
     python bench.py --verify 16 [--config 2]      # speculative verify of 16 drafted tokens + commit
@@ -354,7 +354,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--warmup-seconds", type=float, default=0.6)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: per-channel-gate KDA)")
-    ap.add_argument("--solve", default=None, choices=["exact", "neumann"])
+    ap.add_argument("--solve", default=None, choices=["exact", "neumann", "block_neumann"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--decode", action="store_true",
@@ -384,6 +384,8 @@ def main():
 
     w = WORKLOADS[args.config]
     solve = args.solve or w.solves[0]
+    if solve == "block_neumann":
+        w = w.with_(neumann_order=1, neumann_residual=0)   # the pages' 1-Step Neumann
     serving = args.decode or args.verify
     if serving:
         # decode and verification read only the first 64 tokens of each sequence
@@ -471,6 +473,7 @@ def main():
         "warmup_steps_run": n_warm, "warmup_s": round(warm_s, 3),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H_k": w.H_k, "H_v": w.H_v, "d_k": w.d_k,
                    "d_v": w.d_v, "chunk": w.chunk, "gate_groups": w.G, "solve": solve,
+                   "solve_order": None if solve == "exact" else w.neumann_order,
                    "in_dtype": w.dtype, "out_dtype": "f32", "parallelism": "single-gpu"},
         "tflops_useful": tflops, "mfma_frac_useful": tflops / MFMA_PEAK_TFS[dtype],
         "kernel_ms": {"prep": prep_ms, "scan": scan_ms},

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
 GDR_F32, GDR_BF16 = 0, 1
-GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN = 0, 1
+GDR_SOLVE_EXACT, GDR_SOLVE_NEUMANN, GDR_SOLVE_BLOCK_NEUMANN = 0, 1, 2
 
 EXPORTS = ("gdr_chunk_fwd", "gdr_chunk_fwd_workspace_size", "gdr_chunk_workspace_layout", "gdr_chunk_prepare",
            "gdr_chunk_scan", "gdr_chunk_fwd_noalloc", "gdr_chunk_fwd_ex", "gdr_gated_rmsnorm", "gdr_recurrent_step",
@@ -138,7 +138,7 @@ def make_problem(q, v, log_alpha, beta, *, chunk=64, solve="exact", neumann_orde
     p.beta_per_key_head = int(beta.shape[2] == Hk and Hk != Hv)
     p.in_dtype = _DT[q.dtype]
     p.out_dtype = _DT[out_dtype]
-    p.solve = {"exact": GDR_SOLVE_EXACT, "neumann": GDR_SOLVE_NEUMANN}[solve]
+    p.solve = {"exact": GDR_SOLVE_EXACT, "neumann": GDR_SOLVE_NEUMANN, "block_neumann": GDR_SOLVE_BLOCK_NEUMANN}[solve]
     p.neumann_order = neumann_order
     p.neumann_residual_steps = neumann_residual_steps
     return p

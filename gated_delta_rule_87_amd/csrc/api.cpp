@@ -68,9 +68,9 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
   if (p->d_v % 16 != 0) return fail(GDR_ERR_UNSUPPORTED, "d_v=%d: must be a multiple of 16", p->d_v);
   if (chunked) {
     if (p->chunk <= 0) return fail(GDR_ERR_INVALID_ARG, "chunk=%d must be > 0", p->chunk);
-    if (p->solve != GDR_SOLVE_EXACT && p->solve != GDR_SOLVE_NEUMANN)
+    if (p->solve != GDR_SOLVE_EXACT && p->solve != GDR_SOLVE_NEUMANN && p->solve != GDR_SOLVE_BLOCK_NEUMANN)
       return fail(GDR_ERR_INVALID_ARG, "solve=%d is not a gdr_solve", p->solve);
-    if (p->solve == GDR_SOLVE_NEUMANN) {
+    if (p->solve != GDR_SOLVE_EXACT) {
       if (p->neumann_order < 0 || p->neumann_residual_steps < 0)
         return fail(GDR_ERR_INVALID_ARG, "neumann_order=%d residual_steps=%d must be >= 0", p->neumann_order,
                     p->neumann_residual_steps);

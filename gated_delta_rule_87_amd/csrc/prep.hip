@@ -122,11 +122,13 @@ __device__ __forceinline__ F lds_get_frag(const unsigned char *base, int idx) {
 // A[B,T] = -A[B,B] (M[B,T] A[T,T]) with fp32 MFMA.  Only the diagonal and
 // lower 16x16 blocks of amat are written (and read): the blocks above the
 // diagonal are zero by construction and left to the caller.
+// The 16 x 16 diagonal blocks of (I + M)^{-1}, M = gmat diag(bet), by
+// forward substitution: one thread per (block, column).
 template <int C>
-__device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
+__device__ __forceinline__ void invert_diag_blocks(const float *gmat, const float *bet, float *amat) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int tid = threadIdx.x;
   if (tid < NB * 16) {
     const int base = 16 * (tid >> 4), cc = tid & 15;
     float bl[16], x[16];
@@ -150,6 +152,14 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
       amat[(base + i) * LD + base + cc] = s;
     }
   }
+}
+
+template <int C>
+__device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
+  constexpr int NB = C / 16;
+  constexpr int LD = C + 4;
+  const int w = wave_id(), l = lane_id();
+  invert_diag_blocks<C>(gmat, bet, amat);
   __syncthreads();
   // One job per (pair p, column tile tj): a wave forms the column tile of
   // X_p = M[bot, top] A[top, top] and then the same column of
@@ -188,6 +198,56 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           amat[(r0 + 4 * (l >> 4) + r) * LD + top + 16 * tj + (l & 15)] = -acc[r];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------- block-Jacobi Neumann solve
+// Systolic Linear Attention, section 2.4.3, "Block-doubling and block-Neumann
+// factorization": with D the block diagonal of I + M (16-row blocks) and
+// N = D^{-1} (I + M - D), X = sum_{s=0}^{m} (-N)^s D^{-1}; m = 1 is the
+// pages' 1-Step Neumann A_N1 = (I - N) D^{-1}.  By Horner from X = D^{-1},
+// m times X <- D^{-1} - D^{-1} O X (O = I + M - D: the blocks of M below the
+// diagonal).  Block (I, J), I > J, of the update is -D_I^{-1} (O X)_IJ and
+// reads column block J of X at block rows J .. I-1 only, so a wave updates
+// its column block in place from the bottom up; the product (O X)_IJ goes
+// through the wave's own 16 x 16 staging tile before D_I^{-1} multiplies it.
+template <int C>
+__device__ __forceinline__ void solve_block_neumann(const float *gmat, const float *bet, float *amat, float *tmp,
+                                                    int order) {
+  constexpr int NB = C / 16;
+  constexpr int LD = C + 4;
+  constexpr int SLD = 20;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int nw = blockDim.x / kWave;
+  invert_diag_blocks<C>(gmat, bet, amat);
+  for (int i = tid; i < C * C; i += blockDim.x) {
+    const int r = i / C, cc = i % C;
+    if (r / 16 > cc / 16) amat[r * LD + cc] = 0.f;    // X = D^{-1}
+  }
+  __syncthreads();
+  float *st = tmp + w * 16 * SLD;
+  for (int it = 0; it < order; ++it) {
+    for (int J = w; J < NB - 1; J += nw) {
+      for (int I = NB - 1; I > J; --I) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_f32<NB>(acc, [&](int i, int k) { return gmat[(16 * I + i) * LD + k] * bet[k]; },
+                     [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, 16 * I);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[(4 * (l >> 4) + r) * SLD + (l & 15)] = acc[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+        tile_f32_n<1>(acc2, [&](int i, int k) { return amat[(16 * I + i) * LD + 16 * I + k]; },
+                      [&](int k, int j) { return st[k * SLD + j]; }, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) amat[(16 * I + 4 * (l >> 4) + r) * LD + 16 * J + (l & 15)] = -acc2[r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the staging tile's reads before its next writes
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
     __syncthreads();
@@ -578,8 +638,10 @@ struct PrepItem {
       }
       if (a.solve == 0) {
         solve_exact<C>(gsolve, bet, asolve, tmp);
-      } else {
+      } else if (a.solve == 1) {
         solve_neumann<C>(gsolve, bet, asolve, tmp, a.order, a.residual);
+      } else {
+        solve_block_neumann<C>(gsolve, bet, asolve, tmp, a.order);
       }
       __syncthreads();
       // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y

@@ -67,7 +67,10 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 
 typedef enum {
   GDR_SOLVE_EXACT = 0,   /* A_c = (I + M_c)^{-1} exactly (recursive block doubling) */
-  GDR_SOLVE_NEUMANN = 1  /* sum_{s=0}^{m} (-M_c)^s, then r corrections X <- X + X(I - (I + M_c)X) */
+  GDR_SOLVE_NEUMANN = 1, /* sum_{s=0}^{m} (-M_c)^s, then r corrections X <- X + X(I - (I + M_c)X) */
+  GDR_SOLVE_BLOCK_NEUMANN = 2 /* sum_{s=0}^{m} (-N)^s D^{-1}: D the 16-row block diagonal of I + M_c,
+                                 N = D^{-1}(I + M_c - D); m = 1 is SLA's 1-Step Neumann
+                                 (section 2.4.3); r is not used */
 } gdr_solve;
 
 /* Problem description.  Enumerations are stored as int32_t for a stable ABI. */
@@ -81,8 +84,8 @@ typedef struct {
   int32_t in_dtype;                /* gdr_dtype of q, k, v, beta, log_alpha */
   int32_t out_dtype;               /* gdr_dtype of o */
   int32_t solve;                   /* gdr_solve (chunk path only) */
-  int32_t neumann_order;           /* m >= 0: powers 0..m are kept */
-  int32_t neumann_residual_steps;  /* r >= 0 residual corrections */
+  int32_t neumann_order;           /* m >= 0: powers 0..m are kept (both Neumann solves) */
+  int32_t neumann_residual_steps;  /* r >= 0 residual corrections (GDR_SOLVE_NEUMANN) */
 } gdr_problem;
 
 /*

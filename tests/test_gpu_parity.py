@@ -118,6 +118,30 @@ def test_neumann_small(name, order, res):
     assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("name,order", [("kda_c128_strong", 1), ("kda_bf16", 1), ("kda_f32_c128", 1),
+                                        ("gdn_f32_c64_mixed", 2), ("gva_g4_bf16", 1), ("dk64_bkh_gva", 1),
+                                        ("kda_f32_c128", 7), ("gdn_f32", 3)])
+def test_block_neumann_small(name, order):
+    """SLA section 2.4.3's block-Jacobi Neumann solve (order 1 = 1-Step
+    Neumann) against the fp64 chunk form with the same series; at order
+    C/16 - 1 the series is complete and matches the exact recurrence too."""
+    w = SMALL[name]
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    print(f"[case] block_neumann {name} m={order}", flush=True)
+    o, hT = gb.gdr_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], chunk=w.chunk,
+                             solve="block_neumann", neumann_order=order, neumann_residual_steps=0)
+    o_n, h_n = och.chunk_forward(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], chunk=w.chunk,
+                                 solve="block_neumann", order=order, beta_per_key_head=w.beta_per_key_head)
+    o_ref, h_ref = oracle(x, w)
+    eo, eh = rel_err(o.cpu().numpy(), o_n), rel_err(hT.cpu().numpy(), h_n)
+    print(f"  err vs block-Neumann oracle o={eo:.3e} hT={eh:.3e}; that oracle vs exact recurrence "
+          f"{rel_err(o_n, o_ref):.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
+    if order >= w.chunk // 16 - 1:
+        assert rel_err(o.cpu().numpy(), o_ref) <= TOL[w.dtype] and rel_err(hT.cpu().numpy(), h_ref) <= TOL[w.dtype]
+
+
 def expected_operands(x, w):
     """The scan operands of every chunk from the fp64 chunk pieces: Kbar,
     Qbar, Khat^T and exp(Lambda_C) per key head, token rows past T zero."""
