@@ -78,8 +78,10 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
         return fail(GDR_ERR_INVALID_ARG, "neumann_order=%d residual_steps=%d too large", p->neumann_order,
                     p->neumann_residual_steps);
     }
-    if (!(p->chunk == 64 || p->chunk == 128))
-      return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: libgdr supports chunk in {64, 128}", p->chunk);
+    if (!(p->chunk == 32 || p->chunk == 64 || p->chunk == 128))
+      return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: libgdr supports chunk in {32, 64, 128}", p->chunk);
+    if (p->chunk == 32 && p->d_v % 32 != 0)
+      return fail(GDR_ERR_UNSUPPORTED, "chunk=32 needs d_v a multiple of 32 (d_v=%d)", p->d_v);
     // prep: one 256-thread workgroup per chunk along x; scan: one 512-thread
     // workgroup per (batch, value head, tile of at least 16 value columns)
     const long long n_c = ((long long)p->T + p->chunk - 1) / p->chunk;

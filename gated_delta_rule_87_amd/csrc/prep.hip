@@ -60,7 +60,9 @@ __host__ __device__ inline int prep_region0_floats(int C, int G) {
   return (C * G > C * prep_ld(C)) ? C * G : C * prep_ld(C);
 }
 __host__ __device__ inline int prep_tmp_floats(int C) {
-  const int merge = C * (C / 2 + 4) / 2, neumann = C * 20;
+  // block merges of the exact solve; one 16-column block of the Neumann
+  // solve; four waves' 16 x 16 staging tiles of the block-Jacobi solve
+  const int merge = C * (C / 2 + 4) / 2, neumann = C * 20 > 4 * 16 * 20 ? C * 20 : 4 * 16 * 20;
   return merge > neumann ? merge : neumann;
 }
 
@@ -923,7 +925,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   using X = PrepItem<TIn, P, C, DK>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS;
-  constexpr int NR = NB / 4;                           // row blocks per wave
+  constexpr int NR = NB >= 4 ? NB / 4 : 1;             // row blocks per wave (C = 32: waves 2, 3 build none)
   X x(a, c, hk, b, smem, prep_region0_floats(C, a.G));
   const int w = x.w, lr = x.lr, lq = x.lq, T = x.T, t0 = x.t0;
   auto own = [&](int r) { return (r & 1) ? 4 * r + 3 - w : 4 * r + w; };
@@ -946,6 +948,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   auto same_doc = [&](int r_, int c_) { return !resets || x.seg[r_] == x.seg[c_]; };
   for (int r = 0; r < NR; ++r) {
     const int I = own(r);
+    if (I >= NB) continue;                             // uniform per wave
     const int tr = 16 * I + lr, piv = 16 * I;
     const float mt = (t0 + tr < T) ? 1.f : 0.f;
     const bool sees_entry = !resets || x.seg[tr] == 0, carries = !resets || x.seg[tr] == seg_last;
@@ -1087,7 +1090,7 @@ __global__ __launch_bounds__(256) void prep_block_listed_kernel(ChunkArgs a) {
 }
 
 bool prep_supported(int C, int d_k, int G) {
-  if (!(C == 64 || C == 128)) return false;
+  if (!(C == 32 || C == 64 || C == 128)) return false;
   if (!(d_k == 64 || d_k == 128 || d_k == 256)) return false;
   return prep_lds_bytes(C, d_k, G) <= 160 * 1024;
 }
@@ -1129,6 +1132,9 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
 template <typename TIn, class P>
 static hipError_t launch_prep_dk(const ChunkArgs &a, hipStream_t s) {
   switch (a.C * 1000 + a.d_k) {
+    case 32064: return launch_prep_t<TIn, P, 32, 64>(a, s);
+    case 32128: return launch_prep_t<TIn, P, 32, 128>(a, s);
+    case 32256: return launch_prep_t<TIn, P, 32, 256>(a, s);
     case 64064: return launch_prep_t<TIn, P, 64, 64>(a, s);
     case 64128: return launch_prep_t<TIn, P, 64, 128>(a, s);
     case 64256: return launch_prep_t<TIn, P, 64, 256>(a, s);

@@ -73,7 +73,7 @@ struct ScanLayout {
   static constexpr size_t y_bytes = 4 * (size_t)BV * Y_LD;
   // Y split over channel steps (fewer row blocks than waves, d_k >= 128):
   // partial Y and Qbar S products exchanged through [C/16][BV/16][2][64] f32x4
-  static constexpr bool kYSplit = (C / 16 < 8) && DK >= 128;
+  static constexpr bool kYSplit = (C / 16 == 4) && DK >= 128;
   static constexpr size_t x_bytes = kYSplit ? (size_t)(C / 16) * (BV / 16) * 2 * 64 * 16 : 0;
   // Row-major staging of one chunk's v tile and o tile (C x BV elements of
   // up to 4 bytes, rows padded by 16 bytes).
@@ -637,6 +637,7 @@ static size_t scan_lds_bytes(int C, int d_k, int BV, int fb) {
 #define GDR_CASE(c_, dk_, bv_) \
   if (C == c_ && d_k == dk_ && BV == bv_) \
     return fb == 1024 ? ScanLayout<c_, dk_, bv_, 1024>::total : ScanLayout<c_, dk_, bv_, 2048>::total;
+  GDR_CASE(32, 64, 32) GDR_CASE(32, 128, 32) GDR_CASE(32, 256, 32)
   GDR_CASE(64, 64, 16) GDR_CASE(64, 64, 32) GDR_CASE(64, 128, 16) GDR_CASE(64, 128, 32)
   GDR_CASE(64, 256, 16) GDR_CASE(64, 256, 32) GDR_CASE(128, 64, 16) GDR_CASE(128, 64, 32)
   GDR_CASE(128, 128, 16) GDR_CASE(128, 128, 32) GDR_CASE(128, 256, 16) GDR_CASE(128, 256, 32)
@@ -649,7 +650,10 @@ static size_t scan_lds_bytes(int C, int d_k, int BV, int fb) {
 // supported.
 int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16) {
   const int fb = in_bf16 ? 1024 : 2048;
-  if (!(C == 64 || C == 128) || !(d_k == 64 || d_k == 128 || d_k == 256) || d_v % 16 != 0) return 0;
+  if (!(C == 32 || C == 64 || C == 128) || !(d_k == 64 || d_k == 128 || d_k == 256) || d_v % 16 != 0) return 0;
+  // C = 32: a 16-column tile would give each thread fewer than 4 bytes of a
+  // chunk's v rows to move; 32-column tiles only
+  if (C == 32) return (d_v % 32 == 0 && scan_lds_bytes(C, d_k, 32, fb) <= 160 * 1024) ? 32 : 0;
   const size_t cap = 160 * 1024;
   const bool fit32 = d_v % 32 == 0 && scan_lds_bytes(C, d_k, 32, fb) <= cap;
   const bool fit16 = scan_lds_bytes(C, d_k, 16, fb) <= cap;
@@ -827,13 +831,18 @@ static hipError_t launch_scan_bv(const ChunkArgs &a, hipStream_t s) {
     return launch_segmented<TIn, TOut, P, C, DK>(a, s, segments);
   const int bv = a.states ? 32 : scan_choose_bv(a.B, a.H_v, C, DK, a.d_v, sizeof(TIn) == 2);
   if (bv == 32) return launch_scan_t<TIn, TOut, P, C, DK, 32>(a, s);
-  if (bv == 16) return launch_scan_t<TIn, TOut, P, C, DK, 16>(a, s);
+  if constexpr (C >= 64) {
+    if (bv == 16) return launch_scan_t<TIn, TOut, P, C, DK, 16>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 
 template <typename TIn, typename TOut, class P>
 static hipError_t launch_scan_shape(const ChunkArgs &a, hipStream_t s) {
   switch (a.C * 1000 + a.d_k) {
+    case 32064: return launch_scan_bv<TIn, TOut, P, 32, 64>(a, s);
+    case 32128: return launch_scan_bv<TIn, TOut, P, 32, 128>(a, s);
+    case 32256: return launch_scan_bv<TIn, TOut, P, 32, 256>(a, s);
     case 64064: return launch_scan_bv<TIn, TOut, P, 64, 64>(a, s);
     case 64128: return launch_scan_bv<TIn, TOut, P, 64, 128>(a, s);
     case 64256: return launch_scan_bv<TIn, TOut, P, 64, 256>(a, s);

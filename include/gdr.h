@@ -142,8 +142,8 @@ gdr_status gdr_chunk_workspace_layout(const gdr_problem *p, size_t *offsets);
  *   workspace : device scratch of at least gdr_chunk_fwd_workspace_size(p)
  *               bytes, 256-byte aligned; its contents on return are the
  *               per-chunk quantities documented there.
- * Supported here: in_dtype bf16 or f32, chunk 64 or 128, d_k in {64,128,256},
- * d_v a multiple of 16, G a divisor of d_k, B and H_v at most 65535, fewer
+ * Supported here: in_dtype bf16 or f32, chunk 32, 64 or 128, d_k in {64,128,256},
+ * d_v a multiple of 16 (of 32 with chunk 32), G a divisor of d_k, B and H_v at most 65535, fewer
  * than 2^24 chunks per sequence, B H_v d_v / 16 below 2^23 and
  * chunk H_v d_v below 2^30 (one chunk of v or o within 4 GiB); beyond that
  * GDR_ERR_UNSUPPORTED.

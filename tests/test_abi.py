@@ -117,7 +117,9 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, la=FAKE, h0=None, o=FAKE, hT=
     (dict(d_k=96, gate_groups=96), gb.GDR_ERR_UNSUPPORTED),
     (dict(d_v=72), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=48), gb.GDR_ERR_UNSUPPORTED),
-    (dict(chunk=32), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=16), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=32, d_v=48), gb.GDR_ERR_UNSUPPORTED),
+    (dict(solve=2, neumann_order=-1), gb.GDR_ERR_INVALID_ARG),
     (dict(chunk=128, d_k=256, gate_groups=256), gb.GDR_ERR_UNSUPPORTED),
     (dict(B=1 << 20, T=1 << 20), gb.GDR_ERR_INVALID_ARG),
     (dict(B=70000), gb.GDR_ERR_UNSUPPORTED),

@@ -34,6 +34,7 @@ LAYER = {
     "kda_c128_strong": Workload("kda_c128_strong", 1, 700, 2, 2, 128, 128, 128, 128, "bf16", alpha_mu=1.0,
                                 alpha_sigma=2.0, seed=305),
     "gdn_f32": Workload("gdn_f32", 2, 300, 2, 2, 64, 64, 64, 1, "f32", seed=306),
+    "kda_c32": Workload("kda_c32", 2, 700, 2, 2, 128, 64, 32, 128, "bf16", beta_scale=2.0, seed=308),
     "kda_f32_c128": Workload("kda_f32_c128", 1, 333, 2, 4, 128, 32, 128, 128, "f32", beta_scale=2.0, seed=307),
 }
 

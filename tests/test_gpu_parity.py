@@ -53,6 +53,13 @@ SMALL = {
     "c128_bv32_bf16": Workload("c128_bv32_bf16", 1, 260, 64, 64, 128, 128, 128, 128, "bf16", alpha_mu=2.0,
                                seed=15),
     "f32_bv32": Workload("f32_bv32", 2, 150, 64, 64, 64, 64, 64, 1, "f32", seed=16),
+    # chunk 32 (block-pivot route for every chunk, two row blocks per chunk)
+    "gdn_f32_c32": Workload("gdn_f32_c32", 2, 300, 2, 2, 64, 64, 32, 1, "f32", seed=31),
+    "kda_bf16_c32": Workload("kda_bf16_c32", 1, 517, 2, 2, 128, 64, 32, 128, "bf16", seed=32),
+    "sla_c32_bkh": Workload("sla_c32_bkh", 1, 300, 2, 8, 256, 64, 32, 4, "bf16", beta_per_key_head=True,
+                            beta_scale=2.0, seed=33),
+    "kda_c32_mixed": Workload("kda_c32_mixed", 1, 400, 2, 2, 128, 64, 32, 128, "bf16", alpha_mu=0.0,
+                              alpha_sigma=2.0, seed=34),
 }
 
 # the cases above with chunks on both sides of the chunk-pivot range limit
@@ -84,7 +91,7 @@ def test_chunk_fwd_small(name):
     assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name", ["gdn_f32", "kda_bf16", "dk64_bkh_gva"])
+@pytest.mark.parametrize("name", ["gdn_f32", "kda_bf16", "dk64_bkh_gva", "kda_bf16_c32"])
 def test_chunk_fwd_nonzero_h0(name):
     w = SMALL[name]
     raw, x = draw(w)
@@ -101,7 +108,7 @@ def test_chunk_fwd_nonzero_h0(name):
 
 @pytest.mark.parametrize("name,order,res", [("kda_c128_strong", 4, 1), ("kda_bf16", 2, 1), ("kda_f32_c128", 3, 2),
                                             ("kda_c64_mixed", 3, 1), ("gdn_f32_c64_mixed", 4, 1),
-                                            ("gva_g4_bf16", 1, 0)])
+                                            ("gva_g4_bf16", 1, 0), ("kda_bf16_c32", 2, 1), ("gdn_f32_c32", 1, 0)])
 def test_neumann_small(name, order, res):
     w = SMALL[name].with_(neumann_order=order, neumann_residual=res)
     raw, x = draw(w)
@@ -120,7 +127,7 @@ def test_neumann_small(name, order, res):
 
 @pytest.mark.parametrize("name,order", [("kda_c128_strong", 1), ("kda_bf16", 1), ("kda_f32_c128", 1),
                                         ("gdn_f32_c64_mixed", 2), ("gva_g4_bf16", 1), ("dk64_bkh_gva", 1),
-                                        ("kda_f32_c128", 7), ("gdn_f32", 3)])
+                                        ("kda_f32_c128", 7), ("gdn_f32", 3), ("kda_bf16_c32", 1)])
 def test_block_neumann_small(name, order):
     """SLA section 2.4.3's block-Jacobi Neumann solve (order 1 = 1-Step
     Neumann) against the fp64 chunk form with the same series; at order
