@@ -679,6 +679,18 @@ __device__ __forceinline__ f32x4 mfma_k16(const f16x4 &a, const f16x4 &b, f32x4 
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: within each 16-lane DPP
+// row, then the row totals (read from lanes 15, 31, 47) added to the rows
+// after them.
+__device__ __forceinline__ float wave_prefix64(float x) {
+  x = row_prefix16(x);
+  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const int row = lane_id() >> 4;
+  return x + (row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f);
+}
+
 template <int DK>
 struct Grad16Layout {
   static constexpr int C = kBwdC, VS = 32;
@@ -766,54 +778,6 @@ __global__ __launch_bounds__(512) void bgrad16_kernel(ChunkArgs a, BwdArgs g) {
     return r;
   };
 
-  // ---- Lambda, the rising flag and the diagonal blocks' decay ranges
-  float *las = reinterpret_cast<float *>(sm8 + Lay::slab);
-  for (int i = tid; i < C * G; i += 512) {
-    const int t = i / G, q = i % G;
-    const float x = ldf(lap + (trow(t) * a.H_k + hk) * G + q);
-    las[i] = t < nv ? x : 0.f;
-  }
-  if (tid < 8) flags[tid] = 0;
-  __syncthreads();
-  if (tid < DK) {
-    const int q = tid >> gs;
-    float run = 0.f;
-    bool rising = false;
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      float lo = 0.f, hi = 0.f;
-      for (int u = 0; u < 16; ++u) {
-        const float x = las[(16 * J + u) * G + q];
-        rising |= x > 0.f;
-        run += x;
-        lam[(16 * J + u) * LDK + tid] = run;
-        lo = u ? fminf(lo, run) : run;
-        hi = u ? fmaxf(hi, run) : run;
-      }
-      if (!(hi - lo <= kDiagRange)) flags[1 + J] = 1;   // several threads may store the same 1
-    }
-    if (rising) flags[0] = 1;
-  }
-  __syncthreads();
-  // ---- Kbar = K (.) e^Lambda and G_c as fp16 operands
-  for (int i = tid; i < C * DK / 4; i += 512) {
-    const int t = i / (DK / 4), ch = 4 * (i % (DK / 4));
-    const TIn *pk = kp + trow(t) * krow + ch;
-    const float m = t < nv ? 1.f : 0.f;
-    const float4 lv = *reinterpret_cast<const float4 *>(lam + t * LDK + ch);
-    *reinterpret_cast<f16x4 *>(kb + t * KLD + ch) =
-        f4(ldf(pk) * m * __expf(lv.x), ldf(pk + 1) * m * __expf(lv.y), ldf(pk + 2) * m * __expf(lv.z),
-           ldf(pk + 3) * m * __expf(lv.w));
-  }
-  {
-    const float *gsrc = a.gu + (((size_t)b * a.H_k + hk) * a.N_c + c) * (C * C);
-    for (int i = tid; i < C * C / 4; i += 512) {
-      const int r = i / (C / 4), cc = 4 * (i % (C / 4));
-      const float4 x = *reinterpret_cast<const float4 *>(gsrc + r * C + cc);
-      *reinterpret_cast<f16x4 *>(gu + r * CLD + cc) = f4(x.x, x.y, x.z, x.w);
-    }
-  }
-
   // One slab's inputs, fetched into registers one slab ahead: 4-column
   // pieces of S_{c-1} and dS_c (SQ per thread) and of the dO, D, X and V rows
   // (one per thread).
@@ -857,17 +821,87 @@ __global__ __launch_bounds__(512) void bgrad16_kernel(ChunkArgs a, BwdArgs g) {
   constexpr int TPR = 512 / DK, VPT = VS / TPR;
   const int gr = tid / TPR, gc = (tid % TPR) * VPT;
 
+  // ---- every load the item starts with, issued together: log alpha of the
+  // lane's token (the 64 lanes of a wave are the chunk's tokens; wave w takes
+  // channels w CPW ..), the K rows, G_c, A_c and beta of the first head, and
+  // the first value slab
+  constexpr int CPW = DK / 8;                          // channels per wave in the Lambda prefix
+  constexpr int EPT = C * DK / 512;                    // K (and Q) row elements per thread: 8 or 16
+  constexpr int TPRW = DK / EPT;                       // threads per token row
+  const int kt = tid / TPRW, kc = (tid % TPRW) * EPT;
+  float lav[CPW];
+  {
+    const TIn *lrow = lap + (trow(l) * a.H_k + hk) * G;
+#pragma unroll
+    for (int c2 = 0; c2 < CPW; ++c2) lav[c2] = ldf(lrow + ((w * CPW + c2) >> gs));
+  }
+  Raw8<TIn> kraw[EPT / 8], qraw[EPT / 8];
+#pragma unroll
+  for (int e = 0; e < EPT / 8; ++e) kraw[e].load(kp + trow(kt) * krow + kc + 8 * e);
+  const int hb0 = a.beta_per_key_head ? hk : hk * R;
+  const float *gsrc = a.gu + (((size_t)b * a.H_k + hk) * a.N_c + c) * (C * C);
+  const float *asrc0 = a.au + (((size_t)b * a.H_beta + hb0) * a.N_c + c) * (C * C);
+  float4 graw[2], araw[2];
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int i = tid + 512 * q2, rr = i / (C / 4), cc = 4 * (i % (C / 4));
+    graw[q2] = *reinterpret_cast<const float4 *>(gsrc + rr * C + cc);
+    araw[q2] = *reinterpret_cast<const float4 *>(asrc0 + rr * C + cc);
+  }
+  const float bet0 = ldf(bp + trow(tid % C) * a.H_beta + hb0);
+  fetch(hk * R, 0);
+  if (tid < 8) flags[tid] = 0;
+  __syncthreads();
+  // ---- Lambda: inclusive prefix over the wave's lanes per channel (zero log
+  // decay past T); the rising flag and the diagonal blocks' decay ranges
+  {
+    const float mt = l < nv ? 1.f : 0.f;
+    bool rising = false;
+    bool wide = false;
+#pragma unroll
+    for (int c2 = 0; c2 < CPW; ++c2) {
+      const float a0 = lav[c2] * mt;
+      rising |= a0 > 0.f;
+      const float x = wave_prefix64(a0);
+      lam[l * LDK + w * CPW + c2] = x;
+      // the block's range of Lambda when log alpha <= 0 (a chunk with a
+      // positive one is summed entry by entry whatever its ranges)
+      wide |= !(dpp_row_bcast<0>(x) - dpp_row_bcast<15>(x) <= kDiagRange);
+    }
+    if (wide && (l & 15) == 0) flags[1 + (l >> 4)] = 1;   // several waves may store the same 1
+    if (__ballot(rising) != 0 && l == 0) flags[0] = 1;
+  }
+  __syncthreads();
+  // ---- Kbar = K (.) e^Lambda, G_c, A_c and beta of the first head as LDS operands
+#pragma unroll
+  for (int e = 0; e < EPT / 8; ++e) {
+    float x[8];
+    kraw[e].to_float(x);
+    const int ch = kc + 8 * e;
+    const float m = kt < nv ? 1.f : 0.f;
+    f16x8 y;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = static_cast<f16>(x[j] * m * __expf(lam[kt * LDK + ch + j]));
+    *reinterpret_cast<f16x8 *>(kb + kt * KLD + ch) = y;
+  }
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int i = tid + 512 * q2, rr = i / (C / 4), cc = 4 * (i % (C / 4));
+    *reinterpret_cast<f16x4 *>(gu + rr * CLD + cc) = f4(graw[q2].x, graw[q2].y, graw[q2].z, graw[q2].w);
+    *reinterpret_cast<f16x4 *>(au + rr * CLD + cc) = f4(araw[q2].x, araw[q2].y, araw[q2].z, araw[q2].w);
+  }
+  if (tid < C) bet[tid] = tid < nv ? bet0 : 0.f;
+
   f32x4 aQ[HCT], aKb[HCT], aKh[HCT], aL[2], aG[2];
 #pragma unroll
   for (int n = 0; n < HCT; ++n) aQ[n] = aKb[n] = aKh[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   aL[0] = aL[1] = aG[0] = aG[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dgacc = 0.f, dbk = 0.f;
 
-  fetch(hk * R, 0);
   for (int r = 0; r < R; ++r) {
     const int hv = hk * R + r, hb = a.beta_per_key_head ? hk : hv;
     __syncthreads();                                   // the previous head's readers are done
-    if (r == 0 || !a.beta_per_key_head) {
+    if (r > 0 && !a.beta_per_key_head) {              // the first head's A and beta are staged already
       const float *asrc = a.au + (((size_t)b * a.H_beta + hb) * a.N_c + c) * (C * C);
       for (int i = tid; i < C * C / 4; i += 512) {
         const int rr = i / (C / 4), cc = 4 * (i % (C / 4));
@@ -889,6 +923,12 @@ __global__ __launch_bounds__(512) void bgrad16_kernel(ChunkArgs a, BwdArgs g) {
         fetch(hv, v0 + VS);
       } else if (r + 1 < R) {
         fetch(hv + 1, 0);
+      } else {                                         // the pair sums' K and Q rows
+#pragma unroll
+        for (int e = 0; e < EPT / 8; ++e) {
+          kraw[e].load(kp + trow(kt) * krow + kc + 8 * e);
+          qraw[e].load(qp + trow(kt) * krow + kc + 8 * e);
+        }
       }
       __syncthreads();
       {                                                // Y = V - Kbar S_{c-1}: tile (t block I, v tile h) -> Y^T
@@ -982,8 +1022,18 @@ __global__ __launch_bounds__(512) void bgrad16_kernel(ChunkArgs a, BwdArgs g) {
 
   // ---- pair sums
   __syncthreads();                                     // slab operands, Kbar, A and G are dead
-  load_key_rows<TIn, DK>(ks, kp, row0, krow, nv);
-  load_key_rows<TIn, DK>(qs, qp, row0, krow, nv);
+#pragma unroll
+  for (int e = 0; e < EPT / 8; ++e) {
+    float xk[8], xq[8];
+    kraw[e].to_float(xk);
+    qraw[e].to_float(xq);
+    const float m = kt < nv ? 1.f : 0.f;
+    float *pk = ks + kt * LDK + kc + 8 * e, *pq = qs + kt * LDK + kc + 8 * e;
+    *reinterpret_cast<float4 *>(pk) = make_float4(xk[0] * m, xk[1] * m, xk[2] * m, xk[3] * m);
+    *reinterpret_cast<float4 *>(pk + 4) = make_float4(xk[4] * m, xk[5] * m, xk[6] * m, xk[7] * m);
+    *reinterpret_cast<float4 *>(pq) = make_float4(xq[0] * m, xq[1] * m, xq[2] * m, xq[3] * m);
+    *reinterpret_cast<float4 *>(pq + 4) = make_float4(xq[4] * m, xq[5] * m, xq[6] * m, xq[7] * m);
+  }
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const int J = 2 * jj + h, j = 16 * J + lr;
@@ -1108,20 +1158,51 @@ __global__ __launch_bounds__(512) void bgrad16_kernel(ChunkArgs a, BwdArgs g) {
     for (int e = 0; e < 4; ++e) dlam[(16 * I + 4 * lq + e) * LDK + ch] = dl[n][e];
   }
   __syncthreads();
-  if (tid < DK) {
-    float run = dlast[tid] + dgam[tid] * __expf(lam[(C - 1) * LDK + tid]);
-    for (int t = C - 1; t >= 0; --t) {
-      run += dlam[t * LDK + tid];
-      dlam[t * LDK + tid] = run;
-    }
+  // Lambda_C also enters F_c = diag(e^{Lambda_C}); Lambda_t = sum_{s<=t} log alpha_s,
+  // so dlog alpha_t is the suffix sum of dLambda over the chunk: over the
+  // wave's lanes (tokens), wave w taking channels w CPW ..
+  const int cpg = DK / G;                              // channels per gate group
+  float sv[CPW];
+#pragma unroll
+  for (int c2 = 0; c2 < CPW; ++c2) {
+    const int ch = w * CPW + c2;
+    float x = dlam[l * LDK + ch];
+    if (l == C - 1) x += dlast[ch] + dgam[ch] * __expf(lam[(C - 1) * LDK + ch]);
+    const float p = wave_prefix64(x);
+    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 63));
+    sv[c2] = tot - p + x;                              // sum over tokens l .. C - 1
   }
-  __syncthreads();
-  const int cpg = DK / G;
-  for (int i = tid; i < nv * G; i += 512) {
-    const int t = i / G, q = i % G;
-    float s = 0.f;
-    for (int j = 0; j < cpg; ++j) s += dlam[t * LDK + q * cpg + j];
-    g.dla[(trow(t) * a.H_k + hk) * G + q] = s;
+  if (cpg <= CPW) {
+    // each gate group within the wave's channels: summed in registers, one row per lane
+    if (l < nv) {
+      float *drow = g.dla + (trow(l) * a.H_k + hk) * G + (w * CPW) / cpg;
+      if (cpg == 1 && CPW % 4 == 0) {
+#pragma unroll
+        for (int c2 = 0; c2 < CPW; c2 += 4)
+          *reinterpret_cast<float4 *>(drow + c2) = make_float4(sv[c2], sv[c2 + 1], sv[c2 + 2], sv[c2 + 3]);
+      } else {
+        float x = 0.f;                                 // cpg a power of two: groups end at c2 + 1 = k cpg
+#pragma unroll
+        for (int c2 = 0; c2 < CPW; ++c2) {
+          x += sv[c2];
+          if (((c2 + 1) & (cpg - 1)) == 0) {
+            drow[c2 / cpg] = x;
+            x = 0.f;
+          }
+        }
+      }
+    }
+  } else {
+    // groups spanning several waves' channels: through LDS
+#pragma unroll
+    for (int c2 = 0; c2 < CPW; ++c2) dlam[l * LDK + w * CPW + c2] = sv[c2];
+    __syncthreads();
+    for (int i = tid; i < nv * G; i += 512) {
+      const int t = i / G, q = i % G;
+      float x = 0.f;
+      for (int j = 0; j < cpg; ++j) x += dlam[t * LDK + q * cpg + j];
+      g.dla[(trow(t) * a.H_k + hk) * G + q] = x;
+    }
   }
 }
 

@@ -149,6 +149,46 @@ def test_block_neumann_small(name, order):
         assert rel_err(o.cpu().numpy(), o_ref) <= TOL[w.dtype] and rel_err(hT.cpu().numpy(), h_ref) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("name", ["kda_bf16", "gdn_bf16", "f32_bv32", "c128_bv32_bf16", "kda_bf16_c32",
+                                  "seg_kda_c64"])
+def test_chunk_fwd_bf16_output(name):
+    """out_dtype bf16 (its own o staging and row pieces, 16- and 32-column scan
+    tiles, the segment-parallel scan): o is the fp32-output result rounded once
+    to bf16, bit for bit, and hT is unchanged."""
+    w = SMALL[name] if name in SMALL else SEG_CASE
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    print(f"[case] chunk_fwd bf16 output {name}", flush=True)
+    o32, h32 = run_chunk(dev, w)
+    o16, h16 = run_chunk(dev, w, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(h16, h32)
+
+
+# enough chunks and few enough (batch, head) units for the segment-parallel scan
+SEG_CASE = Workload("seg_kda_c64", 1, 3000, 2, 2, 128, 64, 64, 128, "bf16", seed=17)
+
+
+@pytest.mark.parametrize("name", ["kda_bf16", "f32_bv32", "seg_kda_c64"])
+def test_hT_may_alias_h0(name):
+    """gdr.h: hT may alias h0 (each workgroup reads its h0 tile before writing
+    its hT tile; the segment-parallel path reads h0 in the combine, before the
+    scan writes hT)."""
+    w = SMALL[name] if name in SMALL else SEG_CASE
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    h0 = torch.from_numpy((0.2 * np.random.default_rng(3).standard_normal((w.B, w.H_v, w.d_k, w.d_v)))
+                          .astype(np.float32)).cuda()
+    print(f"[case] hT aliases h0 {name}", flush=True)
+    o1, h1 = run_chunk(dev, w, h0=h0.clone())
+    buf = h0.clone()
+    o2, h2 = run_chunk(dev, w, h0=buf, hT=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, buf) and h2.data_ptr() == buf.data_ptr()
+
+
 def expected_operands(x, w):
     """The scan operands of every chunk from the fp64 chunk pieces: Kbar,
     Qbar, Khat^T and exp(Lambda_C) per key head, token rows past T zero."""
