@@ -19,7 +19,10 @@ Cases: scalar, per-channel and four-tile gates; beta per value and per key
 head; grouped value heads (H_v = 2 H_k); ragged final chunks; a nonzero h0
 and dhT; fp32 and bf16 outputs (d_o in the output's dtype); chunks whose
 decay range exceeds the pivot bound (the gradient kernel's entry-by-entry
-route) and T = 0.
+route) and T = 0.  At the full sizes of the scalar-gate and per-channel
+benchmark workloads (the shapes bench.py --train times), sampled (batch,
+key head) units are checked against the fp64 chunkwise backward
+(oracle.backward.vjp_chunk, pinned to vjp_autograd on the CPU).
 """
 import numpy as np
 import pytest
@@ -29,7 +32,7 @@ from gated_delta_rule_87_amd import binding as gb
 from gated_delta_rule_87_amd.inputs import Workload
 from gpu_common import TOL, device_inputs, draw, need_gpu, rel_err
 from oracle import chunk as och
-from oracle.backward import vjp_autograd
+from oracle.backward import vjp_autograd, vjp_chunk
 
 pytestmark = pytest.mark.gpu
 
@@ -162,3 +165,34 @@ def test_backward_rejects_unsupported():
     p = gb.make_problem(dev["q"], dev["v"], dev["log_alpha"], dev["beta"], solve="neumann")
     assert gb.gdr_chunk_bwd_workspace_size(p) == 0
     assert gb.gdr_chunk_states_size(p) == 0
+
+
+FULL_UNITS = {1: [(0, 0), (3, 15)], 2: [(0, 0), (1, 17), (1, 31)]}
+
+
+@pytest.mark.parametrize("cfg", sorted(FULL_UNITS))
+def test_backward_full_size_sampled(cfg):
+    from gated_delta_rule_87_amd.inputs import WORKLOADS
+    w = WORKLOADS[cfg]
+    print(f"case full-size backward {w.name}", flush=True)
+    raw, dec = draw(w)
+    dev = device_inputs(raw)
+    d_o = _normal((w.B, w.T, w.H_v, w.d_v), w.seed + 3)
+    args = (dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"])
+    o, hT, states = gb.gdr_chunk_fwd_train(*args, chunk=w.chunk)
+    g = gb.gdr_chunk_bwd(*args, states, torch.from_numpy(d_o).cuda(), None, chunk=w.chunk)
+    torch.cuda.synchronize()
+    R = w.H_v // w.H_k
+    for b, hk in FULL_UNITS[cfg]:
+        hv = slice(hk * R, hk * R + R)
+        sk = lambda a: a[b:b + 1, :, hk:hk + 1]
+        sv = lambda a: a[b:b + 1, :, hv]
+        ref = vjp_chunk(sk(dec["q"]), sk(dec["k"]), sv(dec["v"]), sv(dec["beta"]), sk(dec["log_alpha"]), None,
+                        sv(d_o), None, chunk=w.chunk)
+        got = {"dq": g["dq"][b:b + 1, :, hk:hk + 1], "dk": g["dk"][b:b + 1, :, hk:hk + 1],
+               "dv": g["dv"][b:b + 1, :, hv], "dbeta": g["dbeta"][b:b + 1, :, hv],
+               "dlog_alpha": g["dlog_alpha"][b:b + 1, :, hk:hk + 1]}
+        errs = {n: rel_err(t.cpu().numpy(), ref[n]) for n, t in got.items()}
+        print(f"  unit b={b} hk={hk}", {n: f"{e:.2e}" for n, e in errs.items()}, flush=True)
+        for n, e in errs.items():
+            assert e <= BWD_TOL[w.dtype], f"{w.name} b={b} hk={hk} {n}: {e:.3e}"
