@@ -84,6 +84,18 @@ __host__ __device__ inline int prep_union_floats(int C, int DK) {
   return solve > colop ? solve : colop;
 }
 
+// The block-pivot kernel of C = 32 and 128 runs eight waves; their transpose
+// buffers take the solve's scratch (idle while the operands and pairs are
+// built) instead of a region of their own.
+__host__ __device__ inline int prep_union8_floats(int C, int DK) {
+  const int scratch = prep_tmp_floats(C) > 8 * 32 * kXbLd ? prep_tmp_floats(C) : 8 * 32 * kXbLd;
+  const int solve = C * prep_ld(C) + scratch, colop = prep_colop_floats(C, DK);
+  return solve > colop ? solve : colop;
+}
+size_t prep_block8_lds_bytes(int C, int DK, int G) {
+  return sizeof(float) * (size_t)(prep_region0_floats(C, G) + prep_union8_floats(C, DK) + C) + sizeof(int) * 16 + C;
+}
+
 // The block-pivot route also keeps each token's document segment (C bytes,
 // after the transpose buffers).
 size_t prep_lds_bytes(int C, int DK, int G) {
@@ -352,10 +364,12 @@ __device__ __forceinline__ void solve_neumann(const float *gmat, const float *be
 constexpr float kWideMark = -1.f;
 
 // One (batch, key head, chunk) work item: indices, LDS carve-up, pointers.
-template <typename TIn, class P, int C, int DK>
+// NTH threads (256 or 512); with 512 the per-wave transpose buffers sit in
+// the solve's scratch.
+template <typename TIn, class P, int C, int DK, int NTH = 256>
 struct PrepItem {
   static constexpr int NB = C / 16;
-  static constexpr int NKV = C * DK / (8 * 256);  // bound on 8-element log-alpha vectors per thread
+  static constexpr int NKV = (C * DK / 8 + NTH - 1) / NTH;  // bound on 8-element log-alpha vectors per thread
   static constexpr int KS = DK / 32;
   using Split = typename P::Split;
   // workspace tiles: fp16 for bf16 inputs, fp32 for fp32 inputs
@@ -382,9 +396,10 @@ struct PrepItem {
         w(wave_id()), l(lane_id()), lr(lane_id() & 15), lq(lane_id() >> 4),
         lgG(__builtin_ctz(DK) - a_.gshift), Rb(a_.H_beta / a_.H_k), smem(smem_), lam(smem_),
         ureg(smem_ + region0), tmp(ureg + C * prep_ld(C)),
-        bet(ureg + prep_union_floats(C, DK)), flags(reinterpret_cast<int *>(bet + C)),
-        xb(reinterpret_cast<float *>(flags + 16) + wave_id() * 32 * kXbLd),
-        seg(reinterpret_cast<unsigned char *>(reinterpret_cast<float *>(flags + 16) + 4 * 32 * kXbLd)),
+        bet(ureg + (NTH == 256 ? prep_union_floats(C, DK) : prep_union8_floats(C, DK))),
+        flags(reinterpret_cast<int *>(bet + C)),
+        xb((NTH == 256 ? reinterpret_cast<float *>(flags + 16) : tmp) + wave_id() * 32 * kXbLd),
+        seg(reinterpret_cast<unsigned char *>(reinterpret_cast<float *>(flags + 16) + (NTH == 256 ? 4 * 32 * kXbLd : 0))),
         la(reinterpret_cast<const TIn *>(a_.log_alpha)), bp(reinterpret_cast<const TIn *>(a_.beta)),
         kbase(reinterpret_cast<const TIn *>(a_.k) + (size_t)hk_ * DK),
         qbase(reinterpret_cast<const TIn *>(a_.q) + (size_t)hk_ * DK), row_stride((size_t)a_.H_k * DK),
@@ -410,13 +425,13 @@ struct PrepItem {
     if (G >= 8) {
 #pragma unroll
       for (int j = 0; j < NKV; ++j) {
-        const int e = min(8 * (tid + 256 * j), C * G - 8);
+        const int e = min(8 * (tid + NTH * j), C * G - 8);
         r.v[j].load(la + tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1)));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NKV; ++j) {
-        const int e = min(tid + 256 * j, C * G - 1);
+        const int e = min(tid + NTH * j, C * G - 1);
         r.s[j] = la[tok(e >> lgG) * la_row + (size_t)hk * G + (e & (G - 1))];
       }
     }
@@ -433,7 +448,7 @@ struct PrepItem {
     if (G >= 8) {
 #pragma unroll
       for (int j = 0; j < NKV; ++j) {
-        const int e = 8 * (tid + 256 * j);
+        const int e = 8 * (tid + NTH * j);
         if (e < C * G) {
           const int t = e >> lgG, g = e & (G - 1);
           float x[8];
@@ -448,7 +463,7 @@ struct PrepItem {
     } else {
 #pragma unroll
       for (int j = 0; j < NKV; ++j) {
-        const int e = tid + 256 * j;
+        const int e = tid + NTH * j;
         if (e < C * G) lam[e] = (t0 + (e >> lgG) < T) ? static_cast<float>(r.s[j]) : 0.f;
       }
     }
@@ -608,18 +623,18 @@ struct PrepItem {
   // beta of the chunk for every beta head of this key head: element e of
   // thread tid's register j is e = tid + 256 j = rb * C + t (up to 4 * 256
   // values, C * Rb)
-  static constexpr int NBET = 4;
+  static constexpr int NBET = 1024 / NTH;              // beta values: C * Rb <= 1024
   __device__ __forceinline__ void load_betas(TIn (&bets)[NBET]) const {
 #pragma unroll
     for (int j = 0; j < NBET; ++j) {
-      const int e = min(tid + 256 * j, C * Rb - 1);
+      const int e = min(tid + NTH * j, C * Rb - 1);
       bets[j] = bp[tok(e % C) * a.H_beta + hk * Rb + e / C];
     }
   }
   __device__ __forceinline__ void put_betas(const TIn (&bets)[NBET], int rb) const {
 #pragma unroll
     for (int j = 0; j < NBET; ++j) {
-      const int e = tid + 256 * j;
+      const int e = tid + NTH * j;
       if (e / C == rb && e < C * Rb) bet[e % C] = (t0 + e % C < T) ? static_cast<float>(bets[j]) : 0.f;
     }
   }
@@ -920,15 +935,16 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
 // is at most the block's decay range (<= kPivotRange unless the block is
 // flagged and evaluated entry by entry).  Wave w owns blocks w (and 7 - w
 // when C = 128).
-template <typename TIn, class P, int C, int DK>
+template <typename TIn, class P, int C, int DK, int NTH>
 __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int hk, int b, float *smem) {
-  using X = PrepItem<TIn, P, C, DK>;
+  using X = PrepItem<TIn, P, C, DK, NTH>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS;
-  constexpr int NR = NB >= 4 ? NB / 4 : 1;             // row blocks per wave (C = 32: waves 2, 3 build none)
+  constexpr int NWV = NTH / 64;                        // waves
+  constexpr int NR = NB >= NWV ? NB / NWV : 1;         // row blocks per wave (waves past NB build none)
   X x(a, c, hk, b, smem, prep_region0_floats(C, a.G));
   const int w = x.w, lr = x.lr, lq = x.lq, T = x.T, t0 = x.t0;
-  auto own = [&](int r) { return (r & 1) ? 4 * r + 3 - w : 4 * r + w; };
+  auto own = [&](int r) { return (r & 1) ? NWV * r + NWV - 1 - w : NWV * r + w; };
   typename X::LaRegs lar;
   x.issue_la(lar);
   Raw8<TIn> kt[KS], qt[KS], kj[KS];
@@ -1041,11 +1057,17 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   x.solve_store(gmat, x.smem, bets, false);
 }
 
-// Grid (N_c, H_k, B), one chunk per work group.
+// Grid (N_c, H_k, B), one chunk per work group.  d_k <= 128: eight waves
+// (C = 128: a 16-token row block per wave; two waves per SIMD hide each
+// other's load, exponential and MFMA latencies); d_k = 256 keeps four, whose
+// operand rows need the larger register file of a four-wave workgroup.
+template <int DK>
+constexpr int prep_block_threads() { return DK <= 128 ? 512 : 256; }
 template <typename TIn, class P, int C, int DK>
-__global__ __launch_bounds__(256) void prep_block_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(prep_block_threads<DK>()) void prep_block_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  prep_block_item<TIn, P, C, DK>(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw));
+  prep_block_item<TIn, P, C, DK, prep_block_threads<DK>()>(a, blockIdx.x, blockIdx.y, blockIdx.z,
+                                                            reinterpret_cast<float *>(smem_raw));
 }
 
 // 1-D grid: work group g checks the items g + j * gridDim.x (j < 256) for the
@@ -1083,7 +1105,7 @@ __global__ __launch_bounds__(256) void prep_block_listed_kernel(ChunkArgs a) {
       v &= v - 1;
       const int u = blockIdx.x + j * gridDim.x;
       const int c = u % a.N_c, hk = (u / a.N_c) % a.H_k, b = u / (a.N_c * a.H_k);
-      prep_block_item<TIn, P, C, DK>(a, c, hk, b, smem);
+      prep_block_item<TIn, P, C, DK, 256>(a, c, hk, b, smem);
       __syncthreads();
     }
   }
@@ -1092,7 +1114,9 @@ __global__ __launch_bounds__(256) void prep_block_listed_kernel(ChunkArgs a) {
 bool prep_supported(int C, int d_k, int G) {
   if (!(C == 32 || C == 64 || C == 128)) return false;
   if (!(d_k == 64 || d_k == 128 || d_k == 256)) return false;
-  return prep_lds_bytes(C, d_k, G) <= 160 * 1024;
+  // C = 64: the chunk-pivot kernel, and the 256-thread block-pivot kernel for
+  // wide chunks; otherwise the block-pivot kernel, eight waves up to d_k = 128
+  return (C == 64 || d_k > 128 ? prep_lds_bytes(C, d_k, G) : prep_block8_lds_bytes(C, d_k, G)) <= 160 * 1024;
 }
 
 template <class K>
@@ -1107,8 +1131,10 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   hipError_t e;
   if constexpr (C != 64) {
     auto block = prep_block_kernel<TIn, P, C, DK>;
-    if ((e = set_lds(block, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(block, grid, dim3(256), lds, stream, a);
+    constexpr int nth = prep_block_threads<DK>();
+    const size_t lds_b = nth == 512 ? prep_block8_lds_bytes(C, DK, a.G) : lds;
+    if ((e = set_lds(block, lds_b)) != hipSuccess) return e;
+    hipLaunchKernelGGL(block, grid, dim3(nth), lds_b, stream, a);
     return hipGetLastError();
   } else {
   auto chunk = a.G == DK  ? prep_chunk_kernel<TIn, P, DK, kGatePerChannel>
