@@ -369,6 +369,14 @@ template <> struct TileIO<PrecF16> {
     for (int e = 0; e < 8; ++e) h[e] = static_cast<f16>(x[e]);
     __builtin_nontemporal_store(h, reinterpret_cast<f16x8 *>(at(t, blk, f)));
   }
+  // half h (elements 4 h .. 4 h + 3) of a fragment
+  __device__ static void put_half4(void *t, int blk, int f, int h, const float (&x)[4]) {
+    typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+    f16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = static_cast<f16>(x[e]);
+    __builtin_nontemporal_store(v, reinterpret_cast<f16x4 *>(at(t, blk, f) + 8 * h));
+  }
   __device__ static FragH get_plain(const void *t, int blk, int f) {
     FragH v;
     v.h = *reinterpret_cast<const f16x8 *>(at(const_cast<void *>(t), blk, f));
@@ -384,6 +392,9 @@ template <> struct TileIO<PrecF32> {
     float *p = at(t, blk, f);
     __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(p));
     __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4 *>(p + 4));
+  }
+  __device__ static void put_half4(void *t, int blk, int f, int h, const float (&x)[4]) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(at(t, blk, f) + 4 * h));
   }
   __device__ static FragF get_plain(const void *t, int blk, int f) {
     const float *p = at(const_cast<void *>(t), blk, f);

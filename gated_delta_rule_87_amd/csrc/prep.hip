@@ -168,13 +168,54 @@ __device__ __forceinline__ void invert_diag_blocks(const float *gmat, const floa
   }
 }
 
-template <int C>
+template <int C, bool kTiles = false>
 __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
   const int w = wave_id(), l = lane_id();
   invert_diag_blocks<C>(gmat, bet, amat);
   __syncthreads();
+  if constexpr (kTiles) {
+    // Eight waves: one job per 16 x 16 tile, the two products of a level
+    // separated by a barrier.  In the second half of a level's tiles the
+    // column (X) or row (A) index is mirrored, so a wave's two tiles have
+    // contractions of complementary length.
+    const int nw = blockDim.x / kWave;
+    for (int bs = 16; bs < C; bs *= 2) {
+      const int tpb = bs / 16, XLD = bs + 4;
+      const int per = tpb * tpb, jobs = (C / (2 * bs)) * per;
+      for (int job = w; job < jobs; job += nw) {
+        const int p = job / per, u = job % per, ti = u / tpb;
+        const int tj = ti >= (tpb + 1) / 2 ? tpb - 1 - u % tpb : u % tpb;
+        const int top = 2 * bs * p, bot = top + bs, c0 = top + 16 * tj, r0 = bot + 16 * ti;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_f32<C / 32>(acc,
+                 [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
+                 [&](int k, int j) { return amat[k * LD + c0 + j]; },
+                 c0, top + bs);               // A[top,top] is lower: rows k >= column
+        float *X = tmp + p * bs * XLD;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[(16 * ti + 4 * (l >> 4) + r) * XLD + 16 * tj + (l & 15)] = acc[r];
+      }
+      __syncthreads();
+      for (int job = w; job < jobs; job += nw) {
+        const int p = job / per, u = job % per, tj = u / tpb;
+        const int ti = tj >= (tpb + 1) / 2 ? tpb - 1 - u % tpb : u % tpb;
+        const int top = 2 * bs * p, bot = top + bs, r0 = bot + 16 * ti;
+        const float *X = tmp + p * bs * XLD;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        tile_f32<C / 32>(acc,
+                 [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
+                 [&](int k, int j) { return X[(k - bot) * XLD + 16 * tj + j]; },
+                 bot, r0 + 16);               // A[bot,bot] is lower: columns k <= row
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          amat[(r0 + 4 * (l >> 4) + r) * LD + top + 16 * tj + (l & 15)] = -acc[r];
+      }
+      __syncthreads();
+    }
+    return;
+  }
   // One job per (pair p, column tile tj): a wave forms the column tile of
   // X_p = M[bot, top] A[top, top] and then the same column of
   // A[bot, top] = -A[bot, bot] X_p, which needs only that column of X_p, so
@@ -654,7 +695,7 @@ struct PrepItem {
         __syncthreads();
       }
       if (a.solve == 0) {
-        solve_exact<C>(gsolve, bet, asolve, tmp);
+        solve_exact<C, NTH == 512>(gsolve, bet, asolve, tmp);
       } else if (a.solve == 1) {
         solve_neumann<C>(gsolve, bet, asolve, tmp, a.order, a.residual);
       } else {
@@ -735,6 +776,58 @@ __device__ __forceinline__ float pick(const float (&f)[8], int i) {
 // channels (one value per channel, one 8-vector of groups, or at most four
 // groups read as scalars).
 enum GateMode { kGatePerChannel, kGateGroupsVec, kGateGroupsFew };
+
+// log alpha of one token for the lane's channels 32 s + 8 lq + e (s < KS,
+// e < 8), in flight between issue() and get().
+template <typename TIn, int KS, int kGate>
+struct LaLane {
+  static constexpr bool kVec = kGate != kGateGroupsFew;  // G >= 8: read as 8-element vectors
+  Raw8<TIn> v[kVec ? KS : 1];
+  TIn sc[4];
+  // row: the token's G values for the key head
+  __device__ __forceinline__ void issue(const TIn *row, int lq, int gs, int G) {
+    if constexpr (kVec) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) v[s].load(row + min((32 * s + 8 * lq) >> gs, G - 8));
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) sc[g] = row[min(g, G - 1)];
+    }
+  }
+  // lt[s][e] = scale * log alpha; rising |= any value > 0
+  __device__ __forceinline__ void get(float (&lt)[KS][8], float scale, int lq, int gs, int G, bool &rising) const {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int ch0 = 32 * s + 8 * lq;
+      if constexpr (kGate == kGatePerChannel) {
+        float f[8];
+        v[s].to_float(f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lt[s][e] = f[e] * scale;
+      } else if constexpr (kGate == kGateGroupsVec) {
+        float f[8];
+        v[s].to_float(f);
+        const int g0 = min(ch0 >> gs, G - 8);
+        if (gs >= 3) {                                   // one group for the lane's eight channels
+          const float u = pick(f, (ch0 >> gs) - g0) * scale;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lt[s][e] = u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lt[s][e] = pick(f, ((ch0 + e) >> gs) - g0) * scale;
+        }
+      } else {
+        // G < 8 < d_k / G: the lane's eight channels share one group
+        const int g = ch0 >> gs;
+        const float u = static_cast<float>(g == 0 ? sc[0] : g == 1 ? sc[1] : g == 2 ? sc[2] : sc[3]) * scale;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lt[s][e] = u;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rising |= lt[s][e] > 0.f;
+    }
+  }
+};
 template <typename TIn, class P, int DK, int kGate>
 __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
@@ -750,17 +843,8 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
 
   // ---- all loads of the item, issued together: log alpha of the lane's
   // token, its key and query rows, beta
-  const TIn *larow = x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G;
-  constexpr bool kVecLa = kGate != kGateGroupsFew;      // G >= 8: log alpha read as 8-element vectors
-  Raw8<TIn> lav[kVecLa ? KS : 1];
-  TIn las[4];
-  if constexpr (kVecLa) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) lav[s].load(larow + min((32 * s + 8 * lq) >> gs, G - 8));
-  } else {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) las[g] = larow[min(g, G - 1)];
-  }
+  LaLane<TIn, KS, kGate> lal;
+  lal.issue(x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G, lq, gs, G);
   Raw8<TIn> kt[KS], qt[KS];
   x.load_rows(kt, x.kbase, I);
   x.load_rows(qt, x.qbase, I);
@@ -776,36 +860,7 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
   const float scale = mt * kLog2e;                     // tokens past T: zero log decay
   float lt[KS][8];
   bool rising = reset_here;                            // a positive log alpha (Lambda not monotone) or a reset
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const int ch0 = 32 * s + 8 * lq;
-    if constexpr (kGate == kGatePerChannel) {
-      float f[8];
-      lav[s].to_float(f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lt[s][e] = f[e] * scale;
-    } else if constexpr (kGate == kGateGroupsVec) {
-      float f[8];
-      lav[s].to_float(f);
-      const int g0 = min(ch0 >> gs, G - 8);
-      if (gs >= 3) {                                     // one group for the lane's eight channels
-        const float v = pick(f, (ch0 >> gs) - g0) * scale;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lt[s][e] = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lt[s][e] = pick(f, ((ch0 + e) >> gs) - g0) * scale;
-      }
-    } else {
-      // G < 8 < d_k / G: the lane's eight channels share one group
-      const int g = ch0 >> gs;
-      const float v = static_cast<float>(g == 0 ? las[0] : g == 1 ? las[1] : g == 2 ? las[2] : las[3]) * scale;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lt[s][e] = v;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rising |= lt[s][e] > 0.f;
-  }
+  lal.get(lt, scale, lq, gs, G, rising);
   // Block totals of log alpha -> LDS; then one thread per channel turns them
   // into exclusive block offsets and the per-channel factors
   // e0 = exp(Lambda_0), e0i = exp(-Lambda_0), gc = exp(Lambda_{C-1}).
@@ -1057,6 +1112,321 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   x.solve_store(gmat, x.smem, bets, false);
 }
 
+// Block-pivot route at C = 128, d_k <= 128: eight waves, wave w owns row
+// block w.  Lambda stays in registers as in the chunk-pivot route (log2
+// units; in-block prefix P_t over a DPP row, block offsets through LDS).
+// Off-diagonal pairs are factored at block boundaries,
+//   exp(Lambda_t - Lambda_j) = exp(Lambda_t - Lambda_{16 I - 1})
+//                              * prod_{J < K < I} exp(tot_K)
+//                              * exp(Lambda_{16 J + 15} - Lambda_j),
+// every factor <= 1 (tot_K: the block's summed log alpha).  The owner of
+// block J builds the last factor's column operand once and shares it through
+// LDS; a row operand walks down its row's pairs, multiplied by the block
+// decay exp(tot_K) between pairs, so a pair costs no exponential and no
+// global load.  The diagonal pair takes the same column operand with the row
+// operand K_t exp(Lambda_t - Lambda_{16 I + 15}) (>= 1, at most
+// exp(kPivotRange) unless the block is flagged and evaluated entry by
+// entry).  Pairs are balanced: the owner of row I takes J = I - 3 .. I, and
+// wave 7 - I the rest of the row (J <= I - 4).
+//
+// Products are formed transposed (column operand as the MFMA's A): a lane
+// then holds four consecutive columns of one row of G and L, which go to
+// LDS and to the workspace's fragments without a transpose.  For the same
+// reason the fp16 K-hat^T fragments come from an MFMA with an identity
+// operand (one nonzero product per output, exact) instead of an LDS
+// transpose.  The backward pass never prepares C = 128 chunks.
+template <typename TIn, class P, int DK, int kGate>
+__global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
+  constexpr int C = 128, NTH = 512;
+  using X = PrepItem<TIn, P, C, DK, NTH>;
+  using Split = typename X::Split;
+  using IO = typename X::IO;
+  constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
+  constexpr int R0 = C * (C + 4);
+  constexpr float kLog2e = 1.4426950408889634f;
+  static_assert(NB == 8 && DK <= 128, "eight row blocks, one per wave");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const X x(a, blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<float *>(smem_raw), R0);
+  const int I = x.w, lr = x.lr, lq = x.lq, gs = x.gs, G = x.G, tid = x.tid;
+  const int tr = 16 * I + lr;
+  const float mt = (x.t0 + tr < x.T) ? 1.f : 0.f;
+  // LDS.  Region 0 (later the solve's A): the column operands of blocks
+  // 0 .. 6, the block decays exp(tot_K) and the block offsets.  The G region
+  // holds the per-block factor tables until the pairs start.  The scratch
+  // after G holds the block totals and first-token values until the tables
+  // are built, then the transpose buffers.
+  unsigned char *colop = reinterpret_cast<unsigned char *>(x.smem);
+  float *dec = x.smem + (NB - 1) * KS * 512;           // [NB][DK] exp2(tot_K)
+  float *offt = dec + NB * DK;                         // [NB + 1][DK] Lambda_{16 K - 1} (log2)
+  float *f0t = x.ureg;                                 // [NB][DK] exp2(P_0)
+  float *g0t = f0t + NB * DK;                          // [NB][DK] exp2(Lambda_{16 K})
+  float *eit = g0t + NB * DK;                          // [NB][DK] exp2(P_0 - tot_K)
+  float *hct = eit + NB * DK;                          // [NB][DK] exp2(Lambda_{C-1} - Lambda_{16 K + 15})
+  float *stot = x.tmp;                                 // [NB][DK] block totals (log2)
+  float *sp0 = stot + NB * DK;                         // [NB][DK] first-token values (log2)
+  static_assert((NB - 1) * KS * 512 + NB * DK + (NB + 1) * DK <= R0, "region 0");
+  static_assert(4 * NB * DK <= R0, "factor tables");
+
+  // ---- all loads of the item, issued together
+  LaLane<TIn, KS, kGate> lal;
+  lal.issue(x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G, lq, gs, G);
+  Raw8<TIn> kt[KS], qt[KS];
+  x.load_rows(kt, x.kbase, I);
+  x.load_rows(qt, x.qbase, I);
+  TIn bets[NBET];
+  x.load_betas(bets);
+  const bool reset_here = a.reset && mt > 0.f && a.reset[x.tok(tr)] != 0;
+
+  // ---- in-block prefix, block flag, block totals and first-token values
+  float lt[KS][8];
+  bool bad = reset_here;                               // a reset or a positive log alpha in the block
+  lal.get(lt, mt * kLog2e, lq, gs, G, bad);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lt[s][e] = row_prefix16(lt[s][e]);
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p0 = dpp_row_bcast<0>(lt[s][e]);      // every lane takes part in the broadcast
+      bad = bad | ((lr == 15) & !(p0 - lt[s][e] <= kPivotRange * kLog2e));
+    }
+  }
+  const bool wide = __ballot(bad) != 0;                // uniform: the diagonal block entry by entry
+  if (lr == 0 || lr == 15) {
+    float *d0 = (lr == 0 ? sp0 : stot) + I * DK + 8 * lq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      *reinterpret_cast<float4 *>(d0 + 32 * s) = make_float4(lt[s][0], lt[s][1], lt[s][2], lt[s][3]);
+      *reinterpret_cast<float4 *>(d0 + 32 * s + 4) = make_float4(lt[s][4], lt[s][5], lt[s][6], lt[s][7]);
+    }
+  }
+  if (lq == 0) x.seg[tr] = reset_here ? 1 : 0;
+  if (tid == 0) x.flags[kHasReset] = 0;
+  x.put_betas(bets, 0);                                // the solve's first beta head, read after later barriers
+  __syncthreads();
+  // ---- per-block factor tables: thread (part, channel) takes blocks 2 part, 2 part + 1
+  if (tid < 4 * DK) {
+    const int ch = tid % DK, part = tid / DK;
+    float tot[NB], all = 0.f, o = 0.f;
+#pragma unroll
+    for (int K = 0; K < NB; ++K) {
+      tot[K] = stot[K * DK + ch];
+      all += tot[K];
+    }
+#pragma unroll
+    for (int K = 0; K < NB; ++K) {
+      if (K / 2 == part) {
+        const float p0 = sp0[K * DK + ch];
+        f0t[K * DK + ch] = __builtin_amdgcn_exp2f(p0);
+        g0t[K * DK + ch] = __builtin_amdgcn_exp2f(o + p0);
+        eit[K * DK + ch] = __builtin_amdgcn_exp2f(p0 - tot[K]);
+        hct[K * DK + ch] = __builtin_amdgcn_exp2f(all - o - tot[K]);
+        dec[K * DK + ch] = __builtin_amdgcn_exp2f(tot[K]);
+        offt[K * DK + ch] = o;
+      }
+      o += tot[K];
+    }
+    if (part == 3) offt[NB * DK + ch] = all;
+  }
+  if (a.reset && tid == NTH - 1) {                     // reset marks -> document numbers
+    int n = 0;
+    for (int t = 0; t < C; ++t) {
+      n += x.seg[t];
+      x.seg[t] = n;
+    }
+    x.flags[kHasReset] = n > 0;
+  }
+  __syncthreads();
+  // exp(Lambda_{C-1}) per channel; -0 when a document starts in the chunk
+  if (tid < DK) x.gm_row()[tid] = x.flags[kHasReset] ? -0.f : __builtin_amdgcn_exp2f(offt[NB * DK + tid]);
+
+  // Document segments (all 0 without resets): only segment 0 sees the
+  // chunk-entry state, only the last one carries to the chunk's end, pairs
+  // of different segments are zero (selects: no factor crosses a reset).
+  const bool resets = a.reset != nullptr;
+  const int seg_last = resets ? x.seg[C - 1] : 0;
+  auto same_doc = [&](int r_, int c_) { return !resets || x.seg[r_] == x.seg[c_]; };
+  const bool sees_entry = !resets || x.seg[tr] == 0, carries = !resets || x.seg[tr] == seg_last;
+  auto load8 = [&](const float *p, float (&y)[8]) __attribute__((always_inline)) {
+    const float4 u = *reinterpret_cast<const float4 *>(p);
+    const float4 v = *reinterpret_cast<const float4 *>(p + 4);
+    y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w; y[4] = v.x; y[5] = v.y; y[6] = v.z; y[7] = v.w;
+  };
+  // identity operands for the K-hat^T transpose: element (k, j) = [k == j + 16 h]
+  FragH ident[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ident[h].h[e] = (8 * lq + e == lr + 16 * h) ? f16(1.f) : f16(0.f);
+  }
+
+  // ---- operands of block I: scan operands, the shared column operand, the
+  // row operands of the pair chain (fp32), the diagonal pair
+  float yk[KS][8], yq[KS][8];
+  f32x4 dG = {0.f, 0.f, 0.f, 0.f}, dL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int ch0 = 32 * s + 8 * lq;
+    float xk[8], xq[8], f0[8], g0[8], ei[8], hc[8];
+    kt[s].to_float(xk);
+    qt[s].to_float(xq);
+    load8(f0t + I * DK + ch0, f0);
+    load8(g0t + I * DK + ch0, g0);
+    load8(eit + I * DK + ch0, ei);
+    load8(hct + I * DK + ch0, hc);
+    float ku[8], qu[8], kc[8], kbar[8], qbar[8], kh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = lt[s][e], p0 = dpp_row_bcast<0>(p), p15 = dpp_row_bcast<15>(p);
+      const float u = __builtin_amdgcn_exp2f(p - p0);  // exp(Lambda_t - Lambda_{16 I}) <= 1
+      const float v = __builtin_amdgcn_exp2f(p15 - p); // exp(Lambda_{16 I + 15} - Lambda_t) <= 1
+      const float k = xk[e] * mt, q = xq[e] * mt;       // tokens past T: zero rows
+      ku[e] = k * u;
+      qu[e] = q * u;
+      yk[s][e] = ku[e] * f0[e];                        // exp(Lambda_t - Lambda_{16 I - 1})
+      yq[s][e] = qu[e] * f0[e];
+      kbar[e] = sees_entry ? ku[e] * g0[e] : 0.f;      // exp(Lambda_t)
+      qbar[e] = sees_entry ? qu[e] * g0[e] : 0.f;
+      kc[e] = k * v;                                   // column operand
+      kh[e] = carries ? kc[e] * hc[e] : 0.f;           // exp(Lambda_{C-1} - Lambda_t)
+    }
+    const Split bc = make_frag<Split>(kc);
+    if (I < NB - 1) lds_put_frag(colop, I * KS + s, bc);
+    if (!wide) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ku[e] *= ei[e];                                // exp(Lambda_t - Lambda_{16 I + 15})
+        qu[e] *= ei[e];
+      }
+      mma(dG, bc, make_frag<Split>(ku));
+      mma(dL, bc, make_frag<Split>(qu));
+    }
+    IO::put_plain8(x.tKB, I * KS + s, x.l, kbar);
+    IO::put_plain8(x.tQB, I * KS + s, x.l, qbar);
+    if constexpr (P::kF32) {
+      x.put_channel_rows(x.tKH, I, s, kh, false);
+    } else {
+      const FragH fh = make_frag<FragH>(kh);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        mma(t, fh, ident[h]);                          // lane: channel 32 s + 16 h + lr, tokens 4 lq ..
+        const float y[4] = {t[0], t[1], t[2], t[3]};
+        IO::put_half4(x.tKH, (2 * s + h) * (C / 32) + I / 2, 16 * (2 * (I & 1) + (lq >> 1)) + lr, lq & 1, y);
+      }
+    }
+    if (wide) {
+      // Diagonal block entry by entry over this channel step: P of the
+      // block's tokens through the wave's transpose buffer, the causal and
+      // document masks before the exponential.  Lane: row lr, columns 4 lq ..
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x.xb[(8 * lq + e) * kXbLd + lr] = lt[s][e];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int cj = 4 * lq + q4, row = 16 * I + lr, col = 16 * I + cj;
+        float sg = 0.f, sl = 0.f;
+        if (lr >= cj && x.t0 + row < x.T && same_doc(row, col)) {
+          const size_t rrow = x.tok(row) * x.row_stride + 32 * s, rcol = x.tok(col) * x.row_stride + 32 * s;
+          for (int cl = 0; cl < 32; ++cl) {
+            const float d = __builtin_amdgcn_exp2f(x.xb[cl * kXbLd + lr] - x.xb[cl * kXbLd + cj]);
+            const float kcv = static_cast<float>(x.kbase[rcol + cl]);
+            sg += static_cast<float>(x.kbase[rrow + cl]) * kcv * d;
+            sl += static_cast<float>(x.qbase[rrow + cl]) * kcv * d;
+          }
+        }
+        dG[q4] += sg;
+        dL[q4] += sl;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
+  // The helper's rows (wave I < 4 finishes row 7 - I), requested before the barrier
+  const int Ih = NB - 1 - I;
+  const bool helper = I < NB / 2;                      // uniform
+  LaLane<TIn, KS, kGate> lah;
+  if (helper) {
+    lah.issue(x.la + x.tok(16 * Ih + lr) * x.la_row + (size_t)x.hk * G, lq, gs, G);
+    x.load_rows(kt, x.kbase, Ih);
+    x.load_rows(qt, x.qbase, Ih);
+  }
+  __syncthreads();                                     // column operands complete; factor tables dead
+
+  // ---- pairs.  Lane: row 16 Ir + lr of G and L, columns 16 J + 4 lq ..
+  float *gmat = x.ureg;
+  auto put_pair = [&](int Ir, int J, const f32x4 &accG, const f32x4 &accL) __attribute__((always_inline)) {
+    const int row = 16 * Ir + lr, c0 = 16 * J + 4 * lq;
+    float g[4], lv[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const bool keep = same_doc(row, c0 + q4);
+      g[q4] = (keep && (Ir > J || lr > 4 * lq + q4)) ? accG[q4] : 0.f;
+      lv[q4] = (keep && (Ir > J || lr >= 4 * lq + q4)) ? accL[q4] : 0.f;
+    }
+    *reinterpret_cast<float4 *>(gmat + row * (C + 4) + c0) = make_float4(g[0], g[1], g[2], g[3]);
+    IO::put_half4(x.tL, Ir * (C / 32) + J / 2, 16 * (2 * (J & 1) + (lq >> 1)) + lr, lq & 1, lv);
+  };
+  put_pair(I, I, dG, dL);
+  auto pair = [&](int Ir, int J) __attribute__((always_inline)) {
+    f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const Split bj = lds_get_frag<Split>(colop, J * KS + s);
+      mma(accG, bj, make_frag<Split>(yk[s]));
+      mma(accL, bj, make_frag<Split>(yq[s]));
+    }
+    put_pair(Ir, J, accG, accL);
+  };
+  auto decay = [&](int K) __attribute__((always_inline)) {   // pair (., K) -> (., K - 1)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float d[8];
+      load8(dec + K * DK + 32 * s + 8 * lq, d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        yk[s][e] *= d[e];
+        yq[s][e] *= d[e];
+      }
+    }
+  };
+  const int jlo = I >= 3 ? I - 3 : 0;
+  for (int J = I - 1; J >= jlo; --J) {
+    pair(I, J);
+    if (J > jlo) decay(J);
+  }
+  if (helper) {
+    // row Ih from J = Ih - 4 down: row operand K_t exp(Lambda_t - Lambda_{16 (Ih - 3) - 1})
+    const int jtop = Ih - 4, trh = 16 * Ih + lr;
+    const float mh = (x.t0 + trh < x.T) ? 1.f : 0.f;
+    bool unused = false;
+    lah.get(lt, mh * kLog2e, lq, gs, G, unused);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int ch0 = 32 * s + 8 * lq;
+      float oa[8], ob[8], xk[8], xq[8];
+      load8(offt + Ih * DK + ch0, oa);
+      load8(offt + (jtop + 1) * DK + ch0, ob);
+      kt[s].to_float(xk);
+      qt[s].to_float(xq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = __builtin_amdgcn_exp2f(row_prefix16(lt[s][e]) + (oa[e] - ob[e]));
+        yk[s][e] = xk[e] * mh * f;
+        yq[s][e] = xq[e] * mh * f;
+      }
+    }
+    for (int J = jtop; J >= 0; --J) {
+      pair(Ih, J);
+      if (J > 0) decay(J);
+    }
+  }
+  x.zero_upper_L();
+  x.solve_store(gmat, x.smem, bets, true);
+}
+
 // Grid (N_c, H_k, B), one chunk per work group.  d_k <= 128: eight waves
 // (C = 128: a 16-token row block per wave; two waves per SIMD hide each
 // other's load, exponential and MFMA latencies); d_k = 256 keeps four, whose
@@ -1129,7 +1499,16 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   const size_t lds = prep_lds_bytes(C, DK, a.G);
   const dim3 grid(a.N_c, a.H_k, a.B);
   hipError_t e;
-  if constexpr (C != 64) {
+  if constexpr (C == 128 && DK <= 128) {
+    if (a.bwd) return hipErrorInvalidValue;            // the backward pass prepares C = 64 chunks only
+    auto block = a.G == DK  ? prep_block128_kernel<TIn, P, DK, kGatePerChannel>
+                 : a.G >= 8 ? prep_block128_kernel<TIn, P, DK, kGateGroupsVec>
+                            : prep_block128_kernel<TIn, P, DK, kGateGroupsFew>;
+    const size_t lds_b = prep_block8_lds_bytes(C, DK, a.G);
+    if ((e = set_lds(block, lds_b)) != hipSuccess) return e;
+    hipLaunchKernelGGL(block, grid, dim3(512), lds_b, stream, a);
+    return hipGetLastError();
+  } else if constexpr (C != 64) {
     auto block = prep_block_kernel<TIn, P, C, DK>;
     constexpr int nth = prep_block_threads<DK>();
     const size_t lds_b = nth == 512 ? prep_block8_lds_bytes(C, DK, a.G) : lds;
