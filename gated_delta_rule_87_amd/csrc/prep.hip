@@ -138,7 +138,7 @@ __device__ __forceinline__ F lds_get_frag(const unsigned char *base, int idx) {
 // diagonal are zero by construction and left to the caller.
 // The 16 x 16 diagonal blocks of (I + M)^{-1}, M = gmat diag(bet), by
 // forward substitution: one thread per (block, column).
-template <int C>
+template <int C, bool kScaled = false>
 __device__ __forceinline__ void invert_diag_blocks(const float *gmat, const float *bet, float *amat) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
@@ -163,7 +163,7 @@ __device__ __forceinline__ void invert_diag_blocks(const float *gmat, const floa
 #pragma unroll
       for (int m = 0; m < i; ++m) s -= row[m] * bl[m] * x[m];
       x[i] = s;
-      amat[(base + i) * LD + base + cc] = s;
+      amat[(base + i) * LD + base + cc] = kScaled ? bl[i] * s : s;
     }
   }
 }
@@ -173,13 +173,16 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
   const int w = wave_id(), l = lane_id();
-  invert_diag_blocks<C>(gmat, bet, amat);
+  invert_diag_blocks<C, kTiles>(gmat, bet, amat);
   __syncthreads();
   if constexpr (kTiles) {
-    // Eight waves: one job per 16 x 16 tile, the two products of a level
-    // separated by a barrier.  In the second half of a level's tiles the
-    // column (X) or row (A) index is mirrored, so a wave's two tiles have
-    // contractions of complementary length.
+    // Eight waves, and amat holds diag(beta) A throughout: with
+    // Ahat = diag(beta) A the merge is Ahat[B,T] = -Ahat[B,B] (G[B,T] Ahat[T,T])
+    // (diag(beta_B) A[B,B] M[B,T] A[T,T] with M = G diag(beta)), free of beta.
+    // One job per 16 x 16 tile, the two products of a level separated by a
+    // barrier.  In the second half of a level's tiles the column (X) or row
+    // (A) index is mirrored, so a wave's two tiles have contractions of
+    // complementary length.
     const int nw = blockDim.x / kWave;
     for (int bs = 16; bs < C; bs *= 2) {
       const int tpb = bs / 16, XLD = bs + 4;
@@ -190,7 +193,7 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
         const int top = 2 * bs * p, bot = top + bs, c0 = top + 16 * tj, r0 = bot + 16 * ti;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         tile_f32<C / 32>(acc,
-                 [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
+                 [&](int i, int k) { return gmat[(r0 + i) * LD + k]; },
                  [&](int k, int j) { return amat[k * LD + c0 + j]; },
                  c0, top + bs);               // A[top,top] is lower: rows k >= column
         float *X = tmp + p * bs * XLD;
@@ -702,7 +705,10 @@ struct PrepItem {
         solve_block_neumann<C>(gsolve, bet, asolve, tmp, a.order);
       }
       __syncthreads();
-      // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y
+      // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y.
+      // The eight-wave exact solve has already scaled the rows (the
+      // backward pass, which also stores A unscaled, runs four waves).
+      const bool scaled = NTH == 512 && a.solve == 0;
       void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
       for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
         const int blk = u >> 6, f = u & 63;
@@ -720,7 +726,7 @@ struct PrepItem {
         } else {
           const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
           const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
-          const float bt = bet[row];
+          const float bt = scaled ? 1.f : bet[row];
           const float y[8] = {bt * a0.x, bt * a0.y, bt * a0.z, bt * a0.w, bt * a1.x, bt * a1.y, bt * a1.z, bt * a1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = upper ? 0.f : y[e];
@@ -1170,12 +1176,13 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
   // ---- all loads of the item, issued together
   LaLane<TIn, KS, kGate> lal;
   lal.issue(x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G, lq, gs, G);
+  const unsigned char rmark = a.reset ? a.reset[x.tok(tr)] : 0;
   Raw8<TIn> kt[KS], qt[KS];
   x.load_rows(kt, x.kbase, I);
   x.load_rows(qt, x.qbase, I);
   TIn bets[NBET];
   x.load_betas(bets);
-  const bool reset_here = a.reset && mt > 0.f && a.reset[x.tok(tr)] != 0;
+  const bool reset_here = rmark != 0 && mt > 0.f;
 
   // ---- in-block prefix, block flag, block totals and first-token values
   float lt[KS][8];
@@ -1205,7 +1212,6 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
   }
   if (lq == 0) x.seg[tr] = reset_here ? 1 : 0;
   if (tid == 0) x.flags[kHasReset] = 0;
-  x.put_betas(bets, 0);                                // the solve's first beta head, read after later barriers
   __syncthreads();
   // ---- per-block factor tables: thread (part, channel) takes blocks 2 part, 2 part + 1
   if (tid < 4 * DK) {
@@ -1344,6 +1350,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
+  x.put_betas(bets, 0);                                // the solve's first beta head, read after later barriers
   // The helper's rows (wave I < 4 finishes row 7 - I), requested before the barrier
   const int Ih = NB - 1 - I;
   const bool helper = I < NB / 2;                      // uniform
