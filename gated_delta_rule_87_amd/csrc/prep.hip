@@ -168,21 +168,22 @@ __device__ __forceinline__ void invert_diag_blocks(const float *gmat, const floa
   }
 }
 
-template <int C, bool kTiles = false>
+// kScaled: amat holds diag(beta) A throughout.  With Ahat = diag(beta) A the
+// merge is Ahat[B,T] = -Ahat[B,B] (G[B,T] Ahat[T,T]) (it is diag(beta_B)
+// A[B,B] M[B,T] A[T,T] with M = G diag(beta)), free of beta.
+template <int C, bool kTiles = false, bool kScaled = false>
 __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
   const int w = wave_id(), l = lane_id();
-  invert_diag_blocks<C, kTiles>(gmat, bet, amat);
+  auto mx = [&](int r, int k) __attribute__((always_inline)) { return kScaled ? gmat[r * LD + k] : gmat[r * LD + k] * bet[k]; };
+  invert_diag_blocks<C, kScaled>(gmat, bet, amat);
   __syncthreads();
   if constexpr (kTiles) {
-    // Eight waves, and amat holds diag(beta) A throughout: with
-    // Ahat = diag(beta) A the merge is Ahat[B,T] = -Ahat[B,B] (G[B,T] Ahat[T,T])
-    // (diag(beta_B) A[B,B] M[B,T] A[T,T] with M = G diag(beta)), free of beta.
-    // One job per 16 x 16 tile, the two products of a level separated by a
-    // barrier.  In the second half of a level's tiles the column (X) or row
-    // (A) index is mirrored, so a wave's two tiles have contractions of
-    // complementary length.
+    // Eight waves: one job per 16 x 16 tile, the two products of a level
+    // separated by a barrier.  In the second half of a level's tiles the
+    // column (X) or row (A) index is mirrored, so a wave's two tiles have
+    // contractions of complementary length.
     const int nw = blockDim.x / kWave;
     for (int bs = 16; bs < C; bs *= 2) {
       const int tpb = bs / 16, XLD = bs + 4;
@@ -193,7 +194,7 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
         const int top = 2 * bs * p, bot = top + bs, c0 = top + 16 * tj, r0 = bot + 16 * ti;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         tile_f32<C / 32>(acc,
-                 [&](int i, int k) { return gmat[(r0 + i) * LD + k]; },
+                 [&](int i, int k) { return mx(r0 + i, k); },
                  [&](int k, int j) { return amat[k * LD + c0 + j]; },
                  c0, top + bs);               // A[top,top] is lower: rows k >= column
         float *X = tmp + p * bs * XLD;
@@ -237,7 +238,7 @@ __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet,
         const int r0 = bot + 16 * ti;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         tile_f32<C / 32>(acc,
-                 [&](int i, int k) { return gmat[(r0 + i) * LD + k] * bet[k]; },
+                 [&](int i, int k) { return mx(r0 + i, k); },
                  [&](int k, int j) { return amat[k * LD + c0 + j]; },
                  c0, top + bs);               // A[top,top] is lower: rows k >= column
 #pragma unroll
@@ -698,7 +699,11 @@ struct PrepItem {
         __syncthreads();
       }
       if (a.solve == 0) {
-        solve_exact<C, NTH == 512>(gsolve, bet, asolve, tmp);
+        if (NTH == 512 || !a.bwd) {
+          solve_exact<C, NTH == 512, true>(gsolve, bet, asolve, tmp);
+        } else {
+          if constexpr (NTH != 512) solve_exact<C, false, false>(gsolve, bet, asolve, tmp);
+        }
       } else if (a.solve == 1) {
         solve_neumann<C>(gsolve, bet, asolve, tmp, a.order, a.residual);
       } else {
@@ -706,9 +711,9 @@ struct PrepItem {
       }
       __syncthreads();
       // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y.
-      // The eight-wave exact solve has already scaled the rows (the
-      // backward pass, which also stores A unscaled, runs four waves).
-      const bool scaled = NTH == 512 && a.solve == 0;
+      // The exact solve has already scaled the rows, except for the
+      // backward pass (four waves), which also stores A unscaled.
+      const bool scaled = a.solve == 0 && (NTH == 512 || !a.bwd);
       void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
       for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
         const int blk = u >> 6, f = u & 63;
@@ -835,7 +840,7 @@ struct LaLane {
   }
 };
 template <typename TIn, class P, int DK, int kGate>
-__global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   using X = PrepItem<TIn, P, C, DK>;
   using Split = typename X::Split;
@@ -931,7 +936,13 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     const float4 v = *reinterpret_cast<const float4 *>(p + 4);
     y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w; y[4] = v.x; y[5] = v.y; y[6] = v.z; y[7] = v.w;
   };
-  // ---- row and column operands, scan operands, the diagonal pair
+  // ---- row and column operands, scan operands, the diagonal pair.  The
+  // forward pass forms the products transposed (column operand as the
+  // MFMA's A), so a lane holds four consecutive columns of one row of G and
+  // L, stored without a transpose; the backward pass's reversed layouts go
+  // through the transpose buffers.
+  using IO = typename X::IO;
+  const bool fwd = !a.bwd;                             // uniform
   unsigned char *colop = reinterpret_cast<unsigned char *>(x.ureg);
   Split ak[KS], aq[KS];
   f32x4 dG = {0.f, 0.f, 0.f, 0.f}, dL = {0.f, 0.f, 0.f, 0.f};
@@ -962,30 +973,68 @@ __global__ __launch_bounds__(256) void prep_chunk_kernel(ChunkArgs a) {
     ak[s] = make_frag<Split>(yk);
     aq[s] = make_frag<Split>(yq);
     const Split bk = make_frag<Split>(yb);
-    mma(dG, ak[s], bk);
-    mma(dL, aq[s], bk);
     if (I < NB - 1) lds_put_frag(colop, I * KS + s, bk);
+    if (fwd) {
+      mma(dG, bk, ak[s]);
+      mma(dL, bk, aq[s]);
+    } else {
+      mma(dG, ak[s], bk);
+      mma(dL, aq[s], bk);
+    }
     x.scan_operands(I, s, kbar, qbar, kh);
   }
-  x.store_L_block(I, I, dL);
-  __syncthreads();                                     // column operands complete, Lambda rows dead
   float *gsolve = x.smem;
+  // forward: lane holds row 16 Ir + lr, columns 16 J + 4 lq ..
+  auto put_pair = [&](int Ir, int J, const f32x4 &accG, const f32x4 &accL) __attribute__((always_inline)) {
+    const int row = 16 * Ir + lr, c0 = 16 * J + 4 * lq;
+    float lv[4];
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int row = 16 * I + 4 * lq + q4, col = 16 * I + lr;
-    gsolve[row * (C + 4) + col] = row > col ? dG[q4] : 0.f;
+    for (int q4 = 0; q4 < 4; ++q4) lv[q4] = (Ir > J || lr >= 4 * lq + q4) ? accL[q4] : 0.f;
+    *reinterpret_cast<float4 *>(gsolve + row * (C + 4) + c0) =
+        make_float4((Ir > J || lr > 4 * lq) ? accG[0] : 0.f, (Ir > J || lr > 4 * lq + 1) ? accG[1] : 0.f,
+                    (Ir > J || lr > 4 * lq + 2) ? accG[2] : 0.f, (Ir > J || lr > 4 * lq + 3) ? accG[3] : 0.f);
+    IO::put_half4(x.tL, Ir * (C / 32) + J / 2, 16 * (2 * (J & 1) + (lq >> 1)) + lr, lq & 1, lv);
+  };
+  if (fwd) {
+    // the diagonal block's L now; its G row after the barrier (G overlays Lambda's rows)
+    float lv[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) lv[q4] = lr >= 4 * lq + q4 ? dL[q4] : 0.f;
+    IO::put_half4(x.tL, I * (C / 32) + I / 2, 16 * (2 * (I & 1) + (lq >> 1)) + lr, lq & 1, lv);
+  } else {
+    x.store_L_block(I, I, dL);
   }
-  for (int J = 0; J < I; ++J) {
-    f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();                                     // column operands complete, Lambda rows dead
+  if (fwd) {
+    put_pair(I, I, dG, dL);
+    for (int J = 0; J < I; ++J) {
+      f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const Split bj = lds_get_frag<Split>(colop, J * KS + s);
-      mma(accG, ak[s], bj);
-      mma(accL, aq[s], bj);
+      for (int s = 0; s < KS; ++s) {
+        const Split bj = lds_get_frag<Split>(colop, J * KS + s);
+        mma(accG, bj, ak[s]);
+        mma(accL, bj, aq[s]);
+      }
+      put_pair(I, J, accG, accL);
     }
+  } else {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) gsolve[(16 * I + 4 * lq + q4) * (C + 4) + 16 * J + lr] = accG[q4];
-    x.store_L_block(I, J, accL);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int row = 16 * I + 4 * lq + q4, col = 16 * I + lr;
+      gsolve[row * (C + 4) + col] = row > col ? dG[q4] : 0.f;
+    }
+    for (int J = 0; J < I; ++J) {
+      f32x4 accG = {0.f, 0.f, 0.f, 0.f}, accL = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const Split bj = lds_get_frag<Split>(colop, J * KS + s);
+        mma(accG, ak[s], bj);
+        mma(accL, aq[s], bj);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) gsolve[(16 * I + 4 * lq + q4) * (C + 4) + 16 * J + lr] = accG[q4];
+      x.store_L_block(I, J, accL);
+    }
   }
   x.zero_upper_L();
   x.solve_store(gsolve, x.ureg, bets, true);
