@@ -175,10 +175,14 @@ def test_chunk_sizes_agree():
     assert rel_err(o64.cpu().numpy(), o128.cpu().numpy()) <= TOL["bf16"]
 
 
-def test_extreme_decay_is_finite():
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_extreme_decay_is_finite(chunk):
     """log alpha = -1e4 everywhere: each token sees an empty state, so
-    o_t = beta_t (q_t . k_t) v_t; nothing may overflow (no division by decay)."""
-    w = SMALL_KDA
+    o_t = beta_t (q_t . k_t) v_t; nothing may overflow (no division by decay).
+    Every 16-token diagonal block is then too wide for a pivot and formed
+    entry by entry, on either chunk size's prep route."""
+    w = SMALL_KDA.with_(chunk=chunk)
+    print(f"[case] extreme decay C={chunk}", flush=True)
     raw, x = draw(w)
     x["log_alpha"] = np.full_like(x["log_alpha"], -1e4)
     raw["log_alpha"] = np.full_like(raw["log_alpha"], 0xC61C)   # bf16 bits of -9984
@@ -189,6 +193,25 @@ def test_extreme_decay_is_finite():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT.cpu().numpy()))
     o_ref, _ = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"])
     assert rel_err(o, o_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_some_blocks_too_wide(chunk):
+    """Every other 16-token block decays by log alpha = -6 per token (a range
+    of 90 over the block, beyond the pivot bound: that diagonal block is
+    formed entry by entry) and the rest by the workload's mild decay, against
+    the fp64 token recurrence, o and hT."""
+    w = SMALL_KDA.with_(chunk=chunk)
+    print(f"[case] wide blocks C={chunk}", flush=True)
+    raw, x = draw(w)
+    wide = (np.arange(w.T) // 16) % 2 == 1
+    raw["log_alpha"][:, wide] = 0xC0C0                           # bf16 bits of -6
+    x["log_alpha"][:, wide] = -6.0
+    dev = device_inputs(raw)
+    o, hT = run_chunk(dev, w)
+    o_ref, h_ref = recurrence_c(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"])
+    assert rel_err(o.cpu().numpy(), o_ref) <= TOL["bf16"]
+    assert rel_err(hT.cpu().numpy(), h_ref) <= TOL["bf16"]
 
 
 def test_empty_sequence_copies_state():
