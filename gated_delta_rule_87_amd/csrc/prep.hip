@@ -282,12 +282,44 @@ __device__ __forceinline__ void solve_block_neumann(const float *gmat, const flo
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int nw = blockDim.x / kWave;
   invert_diag_blocks<C>(gmat, bet, amat);
+  float *st = tmp + w * 16 * SLD;
+  if (order == 1) {
+    // One step from X = D^{-1}: X[I,J] = -D_I^{-1} (M[I,J] D_J^{-1}) for
+    // I > J, every block independent of the others, so the blocks are
+    // shared out over the waves (the step below would contract over the
+    // whole column, whose blocks other than J are still zero).
+    __syncthreads();
+    for (int job = w; job < NB * (NB - 1) / 2; job += nw) {
+      int I = 1, J = job;                              // job = I (I - 1) / 2 + J, J < I
+      while (J >= I) {
+        J -= I;
+        ++I;
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      tile_f32_n<1>(acc, [&](int i, int k) { return gmat[(16 * I + i) * LD + k] * bet[k]; },
+                    [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[(4 * (l >> 4) + r) * SLD + (l & 15)] = acc[r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+      tile_f32_n<1>(acc2, [&](int i, int k) { return amat[(16 * I + i) * LD + 16 * I + k]; },
+                    [&](int k, int j) { return st[k * SLD + j]; }, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amat[(16 * I + 4 * (l >> 4) + r) * LD + 16 * J + (l & 15)] = -acc2[r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the staging tile's reads before its next writes
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+    return;
+  }
   for (int i = tid; i < C * C; i += blockDim.x) {
     const int r = i / C, cc = i % C;
     if (r / 16 > cc / 16) amat[r * LD + cc] = 0.f;    // X = D^{-1}
   }
   __syncthreads();
-  float *st = tmp + w * 16 * SLD;
   for (int it = 0; it < order; ++it) {
     for (int J = w; J < NB - 1; J += nw) {
       for (int I = NB - 1; I > J; --I) {
