@@ -60,6 +60,17 @@ SMALL = {
                             beta_scale=2.0, seed=33),
     "kda_c32_mixed": Workload("kda_c32_mixed", 1, 400, 2, 2, 128, 64, 32, 128, "bf16", alpha_mu=0.0,
                               alpha_sigma=2.0, seed=34),
+    # chunk 128, d_k <= 128 (eight-wave block-pivot kernel): every log-alpha
+    # layout of a lane's eight channels -- at most four groups read as
+    # scalars (G = 1, 4), one group per 8-channel vector (G = 16) and two
+    # channels per group (G = 32 at d_k = 64) -- and d_k = 64
+    "gdn_bf16_c128": Workload("gdn_bf16_c128", 2, 300, 2, 2, 128, 64, 128, 1, "bf16", seed=41),
+    "g4_c128_bf16": Workload("g4_c128_bf16", 1, 450, 2, 2, 128, 64, 128, 4, "bf16", alpha_mu=1.0,
+                             alpha_sigma=2.0, seed=42),
+    "g16_c128_bkh": Workload("g16_c128_bkh", 1, 450, 2, 8, 128, 32, 128, 16, "bf16", alpha_mu=0.5,
+                             alpha_sigma=2.0, beta_per_key_head=True, beta_scale=2.0, seed=43),
+    "g32_dk64_c128": Workload("g32_dk64_c128", 2, 333, 2, 2, 64, 48, 128, 32, "bf16", seed=44),
+    "gdn_f32_c128_dk64": Workload("gdn_f32_c128_dk64", 2, 300, 2, 2, 64, 64, 128, 1, "f32", seed=45),
 }
 
 # the cases above with chunks on both sides of the chunk-pivot range limit
@@ -108,7 +119,8 @@ def test_chunk_fwd_nonzero_h0(name):
 
 @pytest.mark.parametrize("name,order,res", [("kda_c128_strong", 4, 1), ("kda_bf16", 2, 1), ("kda_f32_c128", 3, 2),
                                             ("kda_c64_mixed", 3, 1), ("gdn_f32_c64_mixed", 4, 1),
-                                            ("gva_g4_bf16", 1, 0), ("kda_bf16_c32", 2, 1), ("gdn_f32_c32", 1, 0)])
+                                            ("gva_g4_bf16", 1, 0), ("kda_bf16_c32", 2, 1), ("gdn_f32_c32", 1, 0),
+                                            ("g16_c128_bkh", 2, 1)])
 def test_neumann_small(name, order, res):
     w = SMALL[name].with_(neumann_order=order, neumann_residual=res)
     raw, x = draw(w)
@@ -127,7 +139,8 @@ def test_neumann_small(name, order, res):
 
 @pytest.mark.parametrize("name,order", [("kda_c128_strong", 1), ("kda_bf16", 1), ("kda_f32_c128", 1),
                                         ("gdn_f32_c64_mixed", 2), ("gva_g4_bf16", 1), ("dk64_bkh_gva", 1),
-                                        ("kda_f32_c128", 7), ("gdn_f32", 3), ("kda_bf16_c32", 1)])
+                                        ("kda_f32_c128", 7), ("gdn_f32", 3), ("kda_bf16_c32", 1),
+                                        ("gdn_bf16_c128", 1), ("gdn_f32_c128_dk64", 1)])
 def test_block_neumann_small(name, order):
     """SLA section 2.4.3's block-Jacobi Neumann solve (order 1 = 1-Step
     Neumann) against the fp64 chunk form with the same series; at order
@@ -214,7 +227,7 @@ def expected_operands(x, w):
 
 @pytest.mark.parametrize("name", ["gdn_f32", "kda_f32_c128", "kda_bf16", "gva_g4_bf16", "kda_c128_strong",
                                   "dk64_bkh_gva", "dk256_kda_bf16", "kda_c64_mixed", "gdn_f32_c64_mixed",
-                                  "gva_bkh_mixed", "g32_mixed", "t63_f32_g8"])
+                                  "gva_bkh_mixed", "g32_mixed", "t63_f32_g8", "g16_c128_bkh", "gdn_f32_c128_dk64"])
 @pytest.mark.parametrize("solve", ["exact", "neumann"])
 def test_prepared_workspace(name, solve):
     """Every prepared chunk quantity against the fp64 chunk pieces: diag(beta)
