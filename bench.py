@@ -343,6 +343,70 @@ def train_bench(w, args, q, k, v, beta, la):
     }), flush=True)
 
 
+def layer_bench(w, args, q, k, v, beta, la):
+    """The SLA layer's forward (Systolic Linear Attention, Table 2 and
+    section 2.1): packed documents (resets, geometric lengths of mean
+    --doc-len tokens), chunk-boundary momentum mu = 0.25, then the gated
+    RMSNorm epilogue sigma(z) * RMSNorm(o) with a seeded bf16 gate input;
+    tokens/s of the whole layer forward."""
+    import torch
+    from gated_delta_rule_87_amd import binding as gb
+    from gated_delta_rule_87_amd.inputs import make_resets
+
+    reset = torch.from_numpy(make_resets(w.B, w.T, args.doc_len, seed=w.seed + 11)).cuda()
+    p = gb.make_problem(q, v, la, beta, chunk=w.chunk)
+    ws = torch.empty(max(gb.gdr_chunk_fwd_workspace_size(p), 256), dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, w.T, w.H_v, w.d_v), **f32)
+    y = torch.empty_like(o)
+    hT = torch.empty((w.B, w.H_v, w.d_k, w.d_v), **f32)
+    zT = torch.empty_like(hT)
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 13)
+    z = torch.randn(o.shape, generator=gen, device="cuda").to(torch.bfloat16)
+    weight = torch.ones(w.d_v, **f32)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        gb.gdr_chunk_fwd_ex(q, k, v, beta, la, None, reset=reset, momentum=0.25, zT=zT, chunk=w.chunk, o=o, hT=hT,
+                            workspace=ws)
+        if evs:
+            evs[1].record()
+        gb.gdr_gated_rmsnorm(o, z, weight=weight, y=y)
+        if evs:
+            evs[2].record()
+
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(5):
+            step()
+        n_warm += 5
+        torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    epi_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    # the epilogue reads o (fp32) and z (bf16) and writes y (fp32) once
+    epi_bytes = w.B * w.T * w.H_v * w.d_v * (4 + 2 + 4)
+    print(json.dumps({
+        "metric": "SLA layer forward (resets + chunk-boundary momentum + gated RMSNorm epilogue), 1 GPU",
+        "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": w.dtype,
+        "data": "synthetic", "kernel_ms": {"forward_ex": fwd_ms, "epilogue": epi_ms},
+        "epilogue_roofline": {"bound": "hbm", "achieved": epi_bytes / (epi_ms * 1e-3) / 1e9, "peak": 8000.0,
+                              "unit": "GB/s", "frac": epi_bytes / (epi_ms * 1e-3) / 1e9 / 8000.0},
+        "config": {"workload": w.name + "_layer", "B": w.B, "T": w.T, "H_k": w.H_k, "H_v": w.H_v, "d_k": w.d_k,
+                   "d_v": w.d_v, "chunk": w.chunk, "gate_groups": w.G, "momentum": 0.25,
+                   "mean_doc_len": args.doc_len, "documents": int(reset.sum().item()) + w.B},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -360,6 +424,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time gdr_recurrent_step on one token per sequence (its own metric)")
     ap.add_argument("--state-format", default="f32", choices=["f32", "e4m3"], help="decode state format")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the SLA layer forward: resets, momentum 0.25, gated RMSNorm epilogue (its own metric)")
+    ap.add_argument("--doc-len", type=int, default=2048, help="--layer: mean document length (geometric)")
     ap.add_argument("--batch", type=int, default=0, help="decode / verify: sequences in the batch (default: workload's)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step: forward keeping chunk states + backward (its own metric)")
@@ -408,6 +475,9 @@ def main():
         return
     if args.train:
         train_bench(w, args, q, k, v, beta, la)
+        return
+    if args.layer:
+        layer_bench(w, args, q, k, v, beta, la)
         return
     p = gb.make_problem(q, v, la, beta, chunk=w.chunk, solve=solve, neumann_order=w.neumann_order,
                         neumann_residual_steps=w.neumann_residual)

@@ -133,28 +133,6 @@ __device__ __forceinline__ void prefix_column(float *col, int ld) {
   }
 }
 
-// The same, restarting the sum at every row r with restart[r] != 0 (a
-// document reset: the decay cumulates from the start of the row's document).
-template <int C>
-__device__ __forceinline__ void prefix_column_restart(float *col, int ld, const unsigned char *restart) {
-  float acc = 0.f;
-#pragma unroll
-  for (int t0 = 0; t0 < C; t0 += 16) {
-    float x[16];
-    int r[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      x[t] = col[(t0 + t) * ld];
-      r[t] = restart[t0 + t];
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      acc = (r[t] ? 0.f : acc) + x[t];
-      col[(t0 + t) * ld] = acc;
-    }
-  }
-}
-
 // ----------------------------------------------------------------- fragments
 struct FragS {            // split bf16 hi + lo
   bf16x8 h, l;

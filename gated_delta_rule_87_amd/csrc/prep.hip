@@ -107,7 +107,7 @@ size_t prep_lds_bytes(int C, int DK, int G) {
 __host__ __device__ inline int prep_chunk_region0_floats(int C) { return C * prep_ld(C); }
 size_t prep_chunk_lds_bytes(int C, int DK) {
   return sizeof(float) * (size_t)(prep_chunk_region0_floats(C) + prep_union_floats(C, DK) + C) +
-         sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd;
+         sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd + C;
 }
 
 // One lane's 32-byte fragment in LDS as two planes of 16 bytes per lane, so
@@ -517,10 +517,13 @@ struct PrepItem {
   // Lambda = in-chunk prefix sum of log alpha per decay group (Systolic
   // Linear Attention, Table 2), and the decay range flags: per 16-token block
   // and over the chunk.  With document resets (the same paper, Table 2,
-  // kappa_c) the sum restarts at each token that starts a document, seg[t]
-  // becomes the number of documents started at or before t in the chunk, a
-  // block holding a reset is flagged (its diagonal pairs are then formed
-  // entry by entry) and flags[kHasReset] is set.  Ends with a barrier.
+  // kappa_c) seg[t] becomes the number of documents started at or before t in
+  // the chunk and flags[kHasReset] is set.  Lambda does not restart at a
+  // reset: every use of it is a difference within one document (pairs of
+  // the same segment, the first segment's decay from the chunk start, the
+  // last one's to the chunk end), which a restart leaves unchanged, and
+  // without it Lambda stays monotone, so the pivoted factors stay bounded and
+  // a block holding a reset needs no entry-by-entry pass.  Ends with a barrier.
   __device__ __forceinline__ void lambda(const LaRegs &r) {
     if (G >= 8) {
 #pragma unroll
@@ -547,17 +550,12 @@ struct PrepItem {
     if (tid < 16) flags[tid] = 0;
     if (tid < C) seg[tid] = (a.reset && t0 + tid < T) ? (a.reset[(size_t)b * T + t0 + tid] != 0) : 0;
     __syncthreads();
-    if (a.reset) {
-      for (int g = tid; g < G; g += blockDim.x) prefix_column_restart<C>(lam + g, G, seg);
-    } else {
-      for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
-    }
+    for (int g = tid; g < G; g += blockDim.x) prefix_column<C>(lam + g, G);
     __syncthreads();
     if (a.reset && tid == blockDim.x - 1) {            // reset marks -> segment numbers
       int n = 0;
       for (int t = 0; t < C; ++t) {
         if (seg[t]) {
-          flags[t >> 4] = 1;
           flags[kHasReset] = 1;
           ++n;
         }
@@ -893,8 +891,12 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
   x.load_rows(qt, x.qbase, I);
   TIn bets[NBET];
   x.load_betas(bets);
-  // a document starting in the chunk sends it to the block-pivot kernel
-  const bool reset_here = a.reset && mt > 0.f && a.reset[x.tok(tr)] != 0;
+  // a document starting at this token (Systolic Linear Attention, Table 2,
+  // kappa_c): Lambda runs on across it, the pairs of different documents are
+  // zero, only the first document sees the chunk-entry state and only the
+  // last one carries to the chunk's end
+  const bool resets = a.reset != nullptr;              // uniform
+  const bool reset_here = resets && mt > 0.f && a.reset[x.tok(tr)] != 0;
 
 
   // ---- Lambda of the lane's token in log2 units (log2(e) Lambda): in-block
@@ -902,7 +904,7 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
   constexpr float kLog2e = 1.4426950408889634f;
   const float scale = mt * kLog2e;                     // tokens past T: zero log decay
   float lt[KS][8];
-  bool rising = reset_here;                            // a positive log alpha (Lambda not monotone) or a reset
+  bool rising = false;                                 // a positive log alpha (Lambda not monotone)
   lal.get(lt, scale, lq, gs, G, rising);
   // Block totals of log alpha -> LDS; then one thread per channel turns them
   // into exclusive block offsets and the per-channel factors
@@ -937,6 +939,10 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
   // lies in [-kPivotRange, 0] and all the factors below lie in
   // [exp(-kPivotRange), exp(kPivotRange)].
   if (x.tid == 0) x.flags[kChunkWide] = 0;
+  if (resets) {
+    if (lq == 0) x.seg[tr] = reset_here ? 1 : 0;
+    if (x.tid == 0) x.flags[kHasReset] = 0;
+  }
   const bool any_rising = __ballot(rising) != 0;
   __syncthreads();
   x.put_betas(bets, 0);                               // the solve's first beta head, read after later barriers
@@ -956,13 +962,26 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
     e0i[ch] = __builtin_amdgcn_exp2f(-l0);
     gc[ch] = __builtin_amdgcn_exp2f(run);
   }
+  if (resets && x.tid == 255) {                        // reset marks -> document numbers within the chunk
+    int n = 0;
+    for (int t = 0; t < C; ++t) {
+      n += x.seg[t];
+      x.seg[t] = n;
+    }
+    x.flags[kHasReset] = n > 0;
+  }
   __syncthreads();
   const bool wide = __builtin_amdgcn_readfirstlane(x.flags[kChunkWide]) != 0;
   if (wide) {
     if (x.tid == 0) x.gm_row()[0] = kWideMark;         // left to the block-pivot kernel
     return;
   }
-  if (x.tid < DK) x.gm_row()[x.tid] = gc[x.tid];
+  // exp(Lambda_C) per channel; -0 when a document starts in the chunk
+  const bool has_reset = resets && x.flags[kHasReset] != 0;
+  if (x.tid < DK) x.gm_row()[x.tid] = has_reset ? -0.f : gc[x.tid];
+  const int seg_last = resets ? x.seg[C - 1] : 0;
+  const bool sees_entry = !resets || x.seg[tr] == 0, carries = !resets || x.seg[tr] == seg_last;
+  auto same_doc = [&](int r_, int c_) { return !resets || x.seg[r_] == x.seg[c_]; };
   auto load8 = [&](const float *p, float (&y)[8]) __attribute__((always_inline)) {
     const float4 u = *reinterpret_cast<const float4 *>(p);
     const float4 v = *reinterpret_cast<const float4 *>(p + 4);
@@ -998,9 +1017,9 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
       yk[e] = k * (d * f0i[e]);                        // row side, exp(Lambda_t - Lambda_0)
       yq[e] = q * (d * f0i[e]);
       yb[e] = k * (ui * f0[e]);                        // column side, exp(Lambda_0 - Lambda_t)
-      kbar[e] = k * d;
-      qbar[e] = q * d;
-      kh[e] = k * (ui * fc[e]);                        // exp(Lambda_C - Lambda_t)
+      kbar[e] = sees_entry ? k * d : 0.f;
+      qbar[e] = sees_entry ? q * d : 0.f;
+      kh[e] = carries ? k * (ui * fc[e]) : 0.f;        // exp(Lambda_C - Lambda_t)
     }
     ak[s] = make_frag<Split>(yk);
     aq[s] = make_frag<Split>(yq);
@@ -1019,19 +1038,22 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
   // forward: lane holds row 16 Ir + lr, columns 16 J + 4 lq ..
   auto put_pair = [&](int Ir, int J, const f32x4 &accG, const f32x4 &accL) __attribute__((always_inline)) {
     const int row = 16 * Ir + lr, c0 = 16 * J + 4 * lq;
-    float lv[4];
+    float g[4], lv[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) lv[q4] = (Ir > J || lr >= 4 * lq + q4) ? accL[q4] : 0.f;
-    *reinterpret_cast<float4 *>(gsolve + row * (C + 4) + c0) =
-        make_float4((Ir > J || lr > 4 * lq) ? accG[0] : 0.f, (Ir > J || lr > 4 * lq + 1) ? accG[1] : 0.f,
-                    (Ir > J || lr > 4 * lq + 2) ? accG[2] : 0.f, (Ir > J || lr > 4 * lq + 3) ? accG[3] : 0.f);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const bool same = same_doc(row, c0 + q4);
+      g[q4] = (same && (Ir > J || lr > 4 * lq + q4)) ? accG[q4] : 0.f;
+      lv[q4] = (same && (Ir > J || lr >= 4 * lq + q4)) ? accL[q4] : 0.f;
+    }
+    *reinterpret_cast<float4 *>(gsolve + row * (C + 4) + c0) = make_float4(g[0], g[1], g[2], g[3]);
     IO::put_half4(x.tL, Ir * (C / 32) + J / 2, 16 * (2 * (J & 1) + (lq >> 1)) + lr, lq & 1, lv);
   };
   if (fwd) {
     // the diagonal block's L now; its G row after the barrier (G overlays Lambda's rows)
     float lv[4];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) lv[q4] = lr >= 4 * lq + q4 ? dL[q4] : 0.f;
+    for (int q4 = 0; q4 < 4; ++q4)
+      lv[q4] = (lr >= 4 * lq + q4 && same_doc(16 * I + lr, 16 * I + 4 * lq + q4)) ? dL[q4] : 0.f;
     IO::put_half4(x.tL, I * (C / 32) + I / 2, 16 * (2 * (I & 1) + (lq >> 1)) + lr, lq & 1, lv);
   } else {
     x.store_L_block(I, I, dL);
@@ -1098,9 +1120,9 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
   float *gmat = x.ureg;
   // Document segments (all 0 without resets): only segment 0 sees the
   // chunk-entry state (Kbar, Qbar rows), only the last one carries to the
-  // chunk's end (Khat rows), and pairs of different segments are zero.  Every
-  // mask is a select, so an infinite factor of a pair across a reset (whose
-  // Lambda values belong to different documents) never reaches a kept entry.
+  // chunk's end (Khat rows), and pairs of different segments are zero (a
+  // select after the product; Lambda runs on across resets, so their factors
+  // stay bounded).
   const bool resets = a.reset != nullptr;             // uniform: without resets no segment is read
   const int seg_last = resets ? x.seg[C - 1] : 0;
   auto same_doc = [&](int r_, int c_) { return !resets || x.seg[r_] == x.seg[c_]; };
@@ -1267,7 +1289,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
 
   // ---- in-block prefix, block flag, block totals and first-token values
   float lt[KS][8];
-  bool bad = reset_here;                               // a reset or a positive log alpha in the block
+  bool bad = false;                                    // a positive log alpha in the block
   lal.get(lt, mt * kLog2e, lq, gs, G, bad);
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -1614,9 +1636,13 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL(chunk, grid, dim3(256), chunk_lds, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // wide-range chunks, if any: two work groups per CU (the LDS of the block
-  // route allows two), at most 256 items each
+  // route allows two), at most 256 items each.  An odd group count: the
+  // items of one chunk's key heads lie N_c apart, and N_c is often a power of
+  // two, so a power-of-two count would hand a chunk with a document start in
+  // it (every head of it marked) to N_c-divisible few groups in turn.
   const long n = (long)a.N_c * a.H_k * a.B;
-  const long groups = std::max(std::min(n, 512L), (n + 255) / 256);
+  long groups = std::max(std::min(n, 511L), (n + 255) / 256);
+  if (groups % 2 == 0) ++groups;
   hipLaunchKernelGGL(listed, dim3((unsigned)groups), dim3(256), lds, stream, a);
   return hipGetLastError();
   }
