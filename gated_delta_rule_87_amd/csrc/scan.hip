@@ -85,6 +85,22 @@ struct ScanLayout {
   static constexpr size_t total = s_bytes + 2 * y_bytes + x_bytes + (XF ? 1 : 2) * st_bytes + al_bytes;
 };
 
+// The training forward's per-wave staging of the state it saves each chunk
+// (after the layout above): a wave's S rows in the state's element type, so
+// they leave as 16-byte pieces of whole rows instead of one element per lane
+// in the MFMA layout.  Rows padded by 16 bytes.
+template <int DK, int BV, int ES>
+struct SaveStage {
+  static constexpr int NBLK = DK / 16, NT = BV / 16;
+  static constexpr int RPW = NBLK >= kScanWaves ? NBLK / kScanWaves : 1;
+  static constexpr int WPR = NBLK >= kScanWaves ? 1 : kScanWaves / NBLK;
+  static constexpr int TPW = (NT + WPR - 1) / WPR;
+  static constexpr int COLS = 16 * TPW;                  // columns of a wave's state tiles
+  static constexpr int PITCH = COLS * ES + 16;           // bytes of one staged row
+  static constexpr int PIECES = 16 * RPW * COLS * ES / 16;   // 16-byte pieces per wave
+  static constexpr size_t bytes = (size_t)kScanWaves * 16 * RPW * PITCH;
+};
+
 // One thread's share when all 64 * kScanWaves threads move a row-major C x BV
 // tile of E-byte elements between HBM and LDS: NREP pieces of SW bytes, piece
 // k of thread t at byte (k * threads + t) * SW of the unpadded tile.  A wave
@@ -367,21 +383,38 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     constexpr bool kTail = decltype(tail_tag)::value;
     const int c1 = last(c + 1);
     if constexpr (kSave) {
+      // S entering chunk c, through the wave's staging rows: lane (lr, lq)
+      // holds rows 4 lq .. 4 lq + 3 of column lr of each of its tiles
       using ST = typename std::conditional<P::kF32, float, f16>::type;   // fp16 for bf16 inputs
-      ST *st = static_cast<ST *>(a.states) + (((size_t)b * a.H_v + hv) * a.N_c + c) * DK * a.d_v;
+      using SS = SaveStage<DK, BV, (int)sizeof(ST)>;
+      static_assert(SS::RPW == SJ::RPW && SS::TPW == SJ::TPW && SJ::kAllTiles, "save staging follows the S jobs");
+      unsigned char *sv = smem_raw + Lay::total + (size_t)w * 16 * SS::RPW * SS::PITCH;
 #pragma unroll
       for (int r = 0; r < SJ::RPW; ++r) {
-        const int i0 = 16 * SJ::blk(w, r);
 #pragma unroll
         for (int u = 0; u < SJ::TPW; ++u) {
-          const int n = SJ::tile(w, u);
-          if (!SJ::kAllTiles && n >= NT) continue;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(static_cast<ST>(S[r][u][e]),
-                                        st + (size_t)(i0 + 4 * lq + e) * a.d_v + c0 + 16 * n + lr);
+            *reinterpret_cast<ST *>(sv + (16 * r + 4 * lq + e) * SS::PITCH + (16 * u + lr) * (int)sizeof(ST)) =
+                static_cast<ST>(S[r][u][e]);
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      ST *st = static_cast<ST *>(a.states) + (((size_t)b * a.H_v + hv) * a.N_c + c) * DK * a.d_v;
+      constexpr int PPR = SS::COLS * (int)sizeof(ST) / 16;        // pieces per staged row
+#pragma unroll
+      for (int k = 0; k < (SS::PIECES + 63) / 64; ++k) {
+        const int pc = 64 * k + l;
+        if (SS::PIECES % 64 == 0 || pc < SS::PIECES) {
+          const int row = pc / PPR, cb = (pc % PPR) * 16;           // staged row, byte in it
+          const int r = row / 16, j = cb / (int)sizeof(ST);          // block of the wave, staged column
+          const int grow = 16 * SJ::blk(w, r) + row % 16;
+          const int gcol = c0 + 16 * SJ::tile(w, j / 16) + j % 16;
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(sv + row * SS::PITCH + cb);
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(st + (size_t)grow * a.d_v + gcol));
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the staging rows' reads before the next chunk's writes
     }
 
     // ---- Y = V - Kbar S, and Qbar S
@@ -767,9 +800,11 @@ static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream, int segm
   const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024>::total;
   auto kern = a.momentum != 0.f ? scan_kernel<TIn, TOut, P, C, DK, BV, true>
                                 : scan_kernel<TIn, TOut, P, C, DK, BV, false>;
+  size_t lds_k = lds;
   if (a.states) {                              // training forward: the shapes the backward pass takes
     if constexpr (C == 64 && DK <= 128 && BV == 32) {
       kern = scan_kernel<TIn, TOut, P, C, DK, BV, false, false, true>;
+      lds_k += SaveStage<DK, BV, P::kF32 ? 4 : 2>::bytes;
     } else {
       return hipErrorInvalidValue;
     }
@@ -777,7 +812,7 @@ static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream, int segm
   hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
   if (e != hipSuccess) return e;
   dim3 grid((a.d_v / BV) * a.H_v * a.B, segments);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), lds, stream, a);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), lds_k, stream, a);
   return hipGetLastError();
 }
 
