@@ -173,7 +173,6 @@ __device__ __forceinline__ void invert_diag_blocks(const float *gmat, const floa
 // A[B,B] M[B,T] A[T,T] with M = G diag(beta)), free of beta.
 template <int C, bool kTiles = false, bool kScaled = false>
 __device__ __forceinline__ void solve_exact(const float *gmat, const float *bet, float *amat, float *tmp) {
-  constexpr int NB = C / 16;
   constexpr int LD = C + 4;
   const int w = wave_id(), l = lane_id();
   auto mx = [&](int r, int k) __attribute__((always_inline)) { return kScaled ? gmat[r * LD + k] : gmat[r * LD + k] * bet[k]; };

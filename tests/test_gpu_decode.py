@@ -27,6 +27,13 @@ DRAFT = {
                         seed=503),
     "gdn_t5_dk64": Workload("gdn_t5_dk64", 2, 5, 2, 2, 64, 48, 64, 1, "bf16", seed=504),
     "t1": Workload("t1", 2, 1, 2, 2, 128, 32, 64, 128, "bf16", seed=505),
+    # strong decay: Lambda spans ~30 over the drafted tokens (first-token
+    # pivot with factors up to e^30) ...
+    "kda_t16_decay": Workload("kda_t16_decay", 2, 16, 2, 4, 128, 64, 64, 128, "f32", alpha_mu=-1.5,
+                              alpha_sigma=1.0, seed=508),
+    # ... and ~80, beyond the pivot bound (each pair's exponential on its own)
+    "kda_t16_wide": Workload("kda_t16_wide", 2, 16, 2, 4, 64, 64, 64, 64, "bf16", alpha_mu=-5.0,
+                             alpha_sigma=1.0, seed=509),
 }
 
 
