@@ -59,7 +59,7 @@ __host__ __device__ inline int prep_ld(int C) { return C + 4; }
 __host__ __device__ inline int prep_region0_floats(int C, int G) {
   return (C * G > C * prep_ld(C)) ? C * G : C * prep_ld(C);
 }
-__host__ __device__ inline int prep_tmp_floats(int C) {
+__host__ __device__ constexpr int prep_tmp_floats(int C) {
   // block merges of the exact solve; one 16-column block of the Neumann
   // solve; four waves' 16 x 16 staging tiles of the block-Jacobi solve
   const int merge = C * (C / 2 + 4) / 2, neumann = C * 20 > 4 * 16 * 20 ? C * 20 : 4 * 16 * 20;
@@ -345,83 +345,504 @@ __device__ __forceinline__ void solve_block_neumann(const float *gmat, const flo
 }
 
 // ----------------------------------------------------------- Neumann solve
-// X = sum_{s=0}^{m} (-M)^s by Horner (X <- I - M X, m times), then r residual
-// corrections X <- X + X (I - (I + M) X).  Horner steps update X in place by
-// 16-column blocks, one wave per block: tile (I, J) of M X contracts over
-// k in [16 J, 16 I + 16) (X is lower triangular), that is over the tiles of
-// column block J at and above row block I, so a wave that goes up its column
-// from the bottom overwrites only tiles nothing later in the column reads.
-// One barrier per step.  The residual products go one 16-column block of
-// the result at a time, X updated in place: (I + M) X[:, J] needs only
-// column block J of X, and X Rm[:, J] needs the columns of X at and right of
-// J, which are still the old ones.
-constexpr int kPrepWaves = 4;                 // the prep kernels run 256 threads
-template <int C>
+// X = sum_{s=0}^{m} (-M)^s by Horner (X <- I - M X, m times from X = I; the
+// first step needs no product: X = I - M), then r residual corrections
+// X <- X + X R with R = I - (I + M) X.
+//
+// Products of lower-triangular C x C matrices go by 16 x 16 tiles (I, J),
+// I >= J; tile (I, J) contracts over k in [16 J, 16 I + 16).  The tiles of
+// one product are independent, so they are dealt to all waves (longest
+// contraction first, dealt back and forth), each wave keeps its results in
+// registers, and all waves write them after a barrier: two barriers per
+// Horner step.  A residual correction needs R whole as the right operand of
+// X R; the solve's scratch holds g 16-column blocks of it (g from the scratch
+// size), so the correction goes by groups of g column blocks: R[:, group]
+// into the scratch, barrier, (X R)[:, group] into registers, barrier, then
+// added to X while the next group's R is formed (that reads only columns of
+// X right of the group).  F: the MFMA operand kind -- split bf16 for bf16
+// inputs (about 16 significant bits per operand, three bf16 MFMAs per
+// 32-deep step), fp32 for fp32 inputs.
+
+// Tile (I, J) of a lower-triangular product, contraction k in [16 J, 16 I + 16)
+// in 32-deep steps (the second half of an odd last step is masked).
+// yrow(r, k, y): y[e] = Y[r][k + e], e < 8; zcol(k, c) = Z[k][c].
+template <class F, class FY, class FZ>
+__device__ __forceinline__ f32x4 lower_tile(const FY &yrow, const FZ &zcol, int I, int J) {
+  const int l = lane_id(), lr = l & 15, lq = l >> 4;
+  const int kend = 16 * I + 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int k0 = 16 * J; k0 < kend; k0 += 32) {
+    const int kk = k0 + 8 * lq;
+    const bool ok = kk < kend;
+    const int ks = ok ? kk : kk - 16;                  // a valid row, read and zeroed
+    float y[8], z[8];
+    yrow(16 * I + lr, ks, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = zcol(ks + e, 16 * J + lr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[e] = ok ? y[e] : 0.f;
+      z[e] = ok ? z[e] : 0.f;
+    }
+    mma(acc, make_frag<F>(y), make_frag<F>(z));
+  }
+  return acc;
+}
+
+// Tile `p` of the lower-triangular tiles of an NB x NB block matrix ordered
+// by decreasing contraction (I - J descending, then J ascending).
+__device__ __forceinline__ void lower_tile_at(int NB, int p, int &I, int &J) {
+  int d = NB - 1;
+  while (p >= NB - d) {
+    p -= NB - d;
+    --d;
+  }
+  J = p;
+  I = p + d;
+}
+
+// Column blocks of R the scratch holds at a time.
+template <int C, int NTH>
+constexpr int neumann_res_cols() {
+  constexpr int scratch = NTH == 512 ? (prep_tmp_floats(C) > 8 * 32 * kXbLd ? prep_tmp_floats(C) : 8 * 32 * kXbLd)
+                                     : prep_tmp_floats(C);
+  int g = C / 16;
+  while (g > 1 && C * (16 * g + 4) > scratch) --g;
+  return g;
+}
+
+template <int C, int NTH, class F>
 __device__ __forceinline__ void solve_neumann(const float *gmat, const float *bet, float *amat, float *tmp, int order,
-                              int residual) {
+                                              int residual) {
   constexpr int NB = C / 16;
   constexpr int LD = C + 4;
-  constexpr int TLD = 20;                     // tmp rows: one 16-column block, padded
-  constexpr int kMaxTiles = (NB + 3) / 4;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int nw = blockDim.x / kWave;
-  for (int i = tid; i < C * LD; i += blockDim.x) amat[i] = ((i / LD) == (i % LD)) ? 1.f : 0.f;
+  constexpr int NW = NTH / kWave;
+  constexpr int NT = NB * (NB + 1) / 2;                // lower-triangular tiles
+  constexpr int SL = (NT + NW - 1) / NW;               // tiles per wave (at most)
+  constexpr int GR = neumann_res_cols<C, NTH>();       // column blocks per residual group
+  constexpr int TLD = 16 * GR + 4;
+  constexpr int SR = (GR * NB + NW - 1) / NW;
+  static_assert(C * TLD <= (NTH == 512 ? (prep_tmp_floats(C) > 8 * 32 * kXbLd ? prep_tmp_floats(C) : 8 * 32 * kXbLd)
+                                       : prep_tmp_floats(C)),
+                "one column block of R fits the scratch");
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), lr = l & 15, lq = l >> 4;
+  // M = G diag(beta), strictly lower (G's diagonal blocks hold zeros on and above the diagonal)
+  auto mrow = [&](int r, int k, float (&y)[8]) __attribute__((always_inline)) {
+    const float4 g0 = *reinterpret_cast<const float4 *>(gmat + r * LD + k);
+    const float4 g1 = *reinterpret_cast<const float4 *>(gmat + r * LD + k + 4);
+    const float4 b0 = *reinterpret_cast<const float4 *>(bet + k);
+    const float4 b1 = *reinterpret_cast<const float4 *>(bet + k + 4);
+    y[0] = g0.x * b0.x; y[1] = g0.y * b0.y; y[2] = g0.z * b0.z; y[3] = g0.w * b0.w;
+    y[4] = g1.x * b1.x; y[5] = g1.y * b1.y; y[6] = g1.z * b1.z; y[7] = g1.w * b1.w;
+  };
+  auto xrow = [&](int r, int k, float (&y)[8]) __attribute__((always_inline)) {
+    const float4 a0 = *reinterpret_cast<const float4 *>(amat + r * LD + k);
+    const float4 a1 = *reinterpret_cast<const float4 *>(amat + r * LD + k + 4);
+    y[0] = a0.x; y[1] = a0.y; y[2] = a0.z; y[3] = a0.w; y[4] = a1.x; y[5] = a1.y; y[6] = a1.z; y[7] = a1.w;
+  };
+  auto xcol = [&](int k, int c) __attribute__((always_inline)) { return amat[k * LD + c]; };
+  // tile s of this wave: position s NW + w (s even) or s NW + NW - 1 - w (s odd)
+  auto my_tile = [&](int s, int &I, int &J) __attribute__((always_inline)) {
+    const int p = s * NW + ((s & 1) ? NW - 1 - w : w);
+    if (p >= NT) return false;
+    lower_tile_at(NB, p, I, J);
+    return true;
+  };
+
+  // X = I (m = 0) or I - M
+  for (int i = tid; i < C * LD; i += NTH) {
+    const int r = i / LD, cc = i % LD;
+    float x = (r == cc) ? 1.f : 0.f;
+    if (order > 0 && cc < r) x -= gmat[i] * bet[cc];
+    amat[i] = x;
+  }
   __syncthreads();
-  auto Mx = [&](int i, int k, int r0) { return gmat[(r0 + i) * LD + k] * bet[k]; };
-  // column blocks J and NB - 1 - J share a wave: long and short columns paired
-  auto owner = [](int J) { return (J < NB / 2 ? J : NB - 1 - J) % kPrepWaves; };
-  for (int it = 0; it < order; ++it) {
-#pragma unroll 1
-    for (int J = 0; J < NB; ++J) {
-      if (owner(J) != w) continue;
-#pragma unroll 1
-      for (int I = NB - 1; I >= J; --I) {       // one tile's operands live at a time
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        tile_f32<C / 16>(acc, [&](int i, int k) { return Mx(i, k, 16 * I); },
-                 [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, 16 * I + 16);
+  for (int it = 1; it < order; ++it) {
+    f32x4 acc[SL];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          amat[row * LD + col] = ((row == col) ? 1.f : 0.f) - acc[r];
-        }
+    for (int s = 0; s < SL; ++s) {
+      int I, J;
+      if (my_tile(s, I, J)) acc[s] = lower_tile<F>(mrow, xcol, I, J);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      int I, J;
+      if (!my_tile(s, I, J)) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
+        amat[row * LD + col] = ((row == col) ? 1.f : 0.f) - acc[s][r];
       }
     }
     __syncthreads();
   }
-  for (int it = 0; it < residual; ++it) {
-    for (int J = 0; J < NB; ++J) {
-      // Rm[:, J] = I - X[:, J] - (M X)[:, J] -> tmp[row * TLD + col - 16J]
-      for (int I = J + w; I < NB; I += nw) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int r0 = 16 * I;
-        tile_f32<C / 16>(acc, [&](int i, int k) { return Mx(i, k, r0); },
-                 [&](int k, int j) { return amat[k * LD + 16 * J + j]; }, 16 * J, r0 + 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          tmp[row * TLD + (l & 15)] = ((row == col) ? 1.f : 0.f) - amat[row * LD + col] - acc[r];
-        }
-      }
-      __syncthreads();
-      f32x4 acc[kMaxTiles];
-      int nt = 0;
-      for (int I = J + w; I < NB; I += nw, ++nt) {
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r0 = 16 * I;
-        tile_f32<C / 16>(acc[nt], [&](int i, int k) { return amat[(r0 + i) * LD + k]; },
-                 [&](int k, int j) { return tmp[k * TLD + j]; }, 16 * J, r0 + 16);
-      }
-      __syncthreads();
-      nt = 0;
-      for (int I = J + w; I < NB; I += nw, ++nt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * I + 4 * (l >> 4) + r, col = 16 * J + (l & 15);
-          amat[row * LD + col] += acc[nt][r];
-        }
-      }
-      __syncthreads();
+  // residual: tile t of a group starting at column block J0 (rows from the
+  // bottom, the group's columns left to right)
+  auto res_tile = [&](int J0, int t, int &I, int &J) __attribute__((always_inline)) {
+    const int g = min(GR, NB - J0);
+    I = NB - 1;
+    while (true) {
+      const int n = min(g, I - J0 + 1);                // columns of the group at row block I
+      if (t < n) break;
+      t -= n;
+      if (--I < J0) return false;
     }
+    J = J0 + t;
+    return true;
+  };
+  for (int it = 0; it < residual; ++it) {
+    f32x4 acc[SR];
+    int J0p = -1;
+    for (int J0 = 0; J0 < NB; J0 += GR) {
+      // R[:, group] = I - X - M X  (the scratch holds rows 0 .. C - 1 of the group's columns)
+#pragma unroll
+      for (int s = 0; s < SR; ++s) {
+        int I, J;
+        if (!res_tile(J0, s * NW + w, I, J)) continue;
+        const f32x4 mx = lower_tile<F>(mrow, xcol, I, J);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * I + 4 * lq + r, col = 16 * J + lr;
+          tmp[row * TLD + col - 16 * J0] = ((row == col) ? 1.f : 0.f) - amat[row * LD + col] - mx[r];
+        }
+      }
+      // the previous group's X R, added now: its columns are left of this group
+      if (J0p >= 0) {
+#pragma unroll
+        for (int s = 0; s < SR; ++s) {
+          int I, J;
+          if (!res_tile(J0p, s * NW + w, I, J)) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) amat[(16 * I + 4 * lq + r) * LD + 16 * J + lr] += acc[s][r];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < SR; ++s) {
+        int I, J;
+        if (!res_tile(J0, s * NW + w, I, J)) continue;
+        acc[s] = lower_tile<F>(xrow, [&](int k, int c) { return tmp[k * TLD + c - 16 * J0]; }, I, J);
+      }
+      __syncthreads();
+      J0p = J0;
+    }
+#pragma unroll
+    for (int s = 0; s < SR; ++s) {
+      int I, J;
+      if (!res_tile(J0p, s * NW + w, I, J)) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amat[(16 * I + 4 * lq + r) * LD + 16 * J + lr] += acc[s][r];
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------- Neumann solve on split-bf16 planes
+// The same series and corrections for bf16 inputs with one beta head per
+// key head (G is then not needed after the solve), in the transposed
+// unknown Y = X^T: a Horner step is Y <- I - Y M^T, a residual correction
+// R^T = I - Y - Y M^T, Y <- Y + R^T Y.  Y, M = G diag(beta) and the
+// correction's R^T rows are kept in LDS as two bf16 planes (hi = bf16(x),
+// lo = bf16(x - hi)), so an MFMA operand is two 16-byte reads with no
+// conversion: every product is split-bf16 (three MFMAs per 32-deep step).
+// Y M^T reads rows of both Y and M; only R^T Y reads Y down its columns.
+// The MFMA takes M (or Y) as its row operand, so a lane's accumulator holds
+// four consecutive columns of one row of the result, written as 8-byte
+// pieces.  Both Y and R^T are upper triangular, M is strictly lower: their
+// zero triangles are stored, so a contraction of an odd number of 16-blocks
+// is padded with a zero block instead of masked.  M overwrites G.
+//
+// Plane layout: rows of C bf16 values, hi plane then lo plane; the 16-byte
+// pieces of row r are XOR-swizzled by bits of r, so that the 16 rows of a
+// fragment read fill the 16 16-byte bank slots of a 256-byte LDS line, and
+// rows 8 and 16 apart (a read down a column) fall into different slots.
+template <int C>
+struct Planes {
+  static constexpr int NCH = C / 8;                    // 16-byte pieces per row (4, 8 or 16)
+  static constexpr int SH = NCH == 16 ? 0 : NCH == 8 ? 1 : 2;
+  static __device__ __forceinline__ int off(int r, int k) {
+    const int sw = ((r >> SH) ^ ((r >> 4) << 1)) & (NCH - 1);
+    return r * C + ((((k >> 3) ^ sw) << 3) | (k & 7));
+  }
+};
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, to_bf16(x)); }
+
+// four values at (r, c .. c + 3), c % 4 == 0, as hi / lo planes
+template <int C>
+__device__ __forceinline__ void planes_put4(bf16 *hi, int rows, int r, int c, const float (&v)[4]) {
+  uint32_t h[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 hb = to_bf16(v[e]);
+    h[e] = __builtin_bit_cast(uint16_t, hb);
+    lo[e] = bf16_bits(v[e] - static_cast<float>(hb));
+  }
+  const int o = Planes<C>::off(r, c);
+  *reinterpret_cast<uint2 *>(hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2 *>(hi + rows * C + o) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+}
+template <int C>
+__device__ __forceinline__ void planes_get4(const bf16 *hi, int rows, int r, int c, float (&v)[4]) {
+  const int o = Planes<C>::off(r, c);
+  const uint2 h = *reinterpret_cast<const uint2 *>(hi + o);
+  const uint2 lo = *reinterpret_cast<const uint2 *>(hi + rows * C + o);
+  const uint32_t hw[2] = {h.x, h.y}, lw[2] = {lo.x, lo.y};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xffffu, lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    v[e] = __uint_as_float(hb << 16) + __uint_as_float(lb << 16);
+  }
+}
+template <int C>
+__device__ __forceinline__ float planes_get(const bf16 *hi, int rows, int r, int k) {
+  const int o = Planes<C>::off(r, k);
+  return static_cast<float>(hi[o]) + static_cast<float>(hi[rows * C + o]);
+}
+// 8 values (r, k .. k + 7), k % 8 == 0, as a split fragment
+template <int C>
+__device__ __forceinline__ FragS planes_row8(const bf16 *hi, int rows, int r, int k) {
+  const int o = Planes<C>::off(r, k);
+  FragS f;
+  f.h = *reinterpret_cast<const bf16x8 *>(hi + o);
+  f.l = *reinterpret_cast<const bf16x8 *>(hi + rows * C + o);
+  return f;
+}
+// 8 values (k .. k + 7, c): down a column
+template <int C>
+__device__ __forceinline__ FragS planes_col8(const bf16 *hi, int rows, int k, int c) {
+  FragS f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int o = Planes<C>::off(k + e, c);
+    f.h[e] = hi[o];
+    f.l[e] = hi[rows * C + o];
+  }
+  return f;
+}
+
+// Contraction range of tile (I, J), I <= J, of a product of upper-triangular
+// (or strictly upper, transposed strictly lower) block matrices: k in
+// [16 I, 16 J + 16), padded to whole 32-deep steps by a zero 16-block below
+// (I > 0) or above (I == 0: J + 1 < NB there, as NB is even).
+__device__ __forceinline__ void upper_range(int I, int J, int &k0, int &k1) {
+  k0 = 16 * I;
+  k1 = 16 * J + 16;
+  if ((J - I) % 2 == 0) {
+    if (I > 0) k0 -= 16;
+    else k1 += 16;
+  }
+}
+
+template <int C, int NTH>
+constexpr int neumann_plane_rows() {
+  constexpr int scratch = NTH == 512 ? (prep_tmp_floats(C) > 8 * 32 * kXbLd ? prep_tmp_floats(C) : 8 * 32 * kXbLd)
+                                     : prep_tmp_floats(C);
+  int g = C / 16;
+  while (g > 1 && 64 * g * C > 4 * scratch) --g;     // g row blocks of R^T: 2 planes x 16 g rows x C bf16
+  return g;
+}
+
+template <int C, int NTH>
+__device__ __forceinline__ void solve_neumann_planes(float *gmat, const float *bet, float *amat, float *tmp,
+                                                     int order, int residual) {
+  constexpr int NB = C / 16;
+  constexpr int LD = C + 4;
+  constexpr int NW = NTH / kWave;
+  constexpr int NT = NB * (NB + 1) / 2;
+  constexpr int SL = (NT + NW - 1) / NW;
+  constexpr int GR = neumann_plane_rows<C, NTH>();
+  constexpr int SR = (GR * NB + NW - 1) / NW;
+  static_assert(64 * C <= 4 * prep_tmp_floats(C), "one row block of R^T fits the scratch");
+  static_assert(4 * C * C <= 4 * C * LD, "planes fit the fp32 regions");
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), lr = l & 15, lq = l >> 4;
+  bf16 *const Mp = reinterpret_cast<bf16 *>(gmat);
+  bf16 *const Yp = reinterpret_cast<bf16 *>(amat);
+  bf16 *const Rp = reinterpret_cast<bf16 *>(tmp);
+
+  // Y = I (m = 0) or (I - M)^T, both triangles; M's planes after every read of G
+  constexpr int NOCT = (C * C / 8 + NTH - 1) / NTH;   // octets of M per thread
+  float gv[NOCT][8];
+#pragma unroll
+  for (int j = 0; j < NOCT; ++j) {
+    const int u = min(tid + NTH * j, C * C / 8 - 1), c = u / (C / 8), k = 8 * (u % (C / 8));
+    ld8(gmat + c * LD + k, gv[j]);
+    const float4 b0 = *reinterpret_cast<const float4 *>(bet + k);
+    const float4 b1 = *reinterpret_cast<const float4 *>(bet + k + 4);
+    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[j][e] = (k + e < c) ? gv[j][e] * bb[e] : 0.f;   // M[c][k + e]
+  }
+  for (int u = tid; u < C * C / 4; u += NTH) {
+    const int r = u % C, c = 4 * (u / C);              // neighbouring lanes read neighbouring G columns
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = ((r == c + e) ? 1.f : 0.f) - ((order > 0 && c + e > r) ? gmat[(c + e) * LD + r] * bet[r] : 0.f);
+    planes_put4<C>(Yp, C, r, c, v);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NOCT; ++j) {
+    const int u = tid + NTH * j, c = u / (C / 8), k = 8 * (u % (C / 8));
+    if (u >= C * C / 8) break;
+    const float lo4[4] = {gv[j][0], gv[j][1], gv[j][2], gv[j][3]}, hi4[4] = {gv[j][4], gv[j][5], gv[j][6], gv[j][7]};
+    planes_put4<C>(Mp, C, c, k, lo4);
+    planes_put4<C>(Mp, C, c, k + 4, hi4);
+  }
+  __syncthreads();
+
+  // tile s of this wave (upper tiles, longest contraction first, dealt back and forth)
+  auto my_tile = [&](int s, int &I, int &J) __attribute__((always_inline)) {
+    const int p = s * NW + ((s & 1) ? NW - 1 - w : w);
+    if (p >= NT) return false;
+    lower_tile_at(NB, p, J, I);
+    return true;
+  };
+  // (Y M^T)[16 I + lr][16 J + 4 lq + q]; the n = (k1 - k0) / 32 steps' reads
+  // are all issued before the first MFMA
+  auto ymt = [&](int I, int J) __attribute__((always_inline)) {
+    int k0, k1;
+    upper_range(I, J, k0, k1);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto steps = [&](auto n) __attribute__((always_inline)) {
+      constexpr int N = decltype(n)::value;
+      FragS m[N], y[N];
+#pragma unroll
+      for (int u = 0; u < N; ++u) {
+        m[u] = planes_row8<C>(Mp, C, 16 * J + lr, k0 + 32 * u + 8 * lq);
+        y[u] = planes_row8<C>(Yp, C, 16 * I + lr, k0 + 32 * u + 8 * lq);
+      }
+#pragma unroll
+      for (int u = 0; u < N; ++u) mma(acc, m[u], y[u]);
+    };
+    switch ((k1 - k0) >> 5) {
+      case 1: steps(std::integral_constant<int, 1>()); break;
+      case 2: if constexpr (NB >= 4) steps(std::integral_constant<int, 2>()); break;
+      case 3: if constexpr (NB >= 6) steps(std::integral_constant<int, 3>()); break;
+      case 4: if constexpr (NB >= 8) steps(std::integral_constant<int, 4>()); break;
+      default: break;
+    }
+    return acc;
+  };
+  for (int it = 1; it < order; ++it) {
+    f32x4 acc[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      int I, J;
+      if (my_tile(s, I, J)) acc[s] = ymt(I, J);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      int I, J;
+      if (!my_tile(s, I, J)) continue;
+      const int r = 16 * I + lr, c = 16 * J + 4 * lq;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = ((r == c + q) ? 1.f : 0.f) - acc[s][q];
+      planes_put4<C>(Yp, C, r, c, v);
+    }
+    __syncthreads();
+  }
+
+  // residual corrections by groups of GR row blocks of R^T (top to bottom):
+  // tile t of the group at I0, longest contraction first; the block left of
+  // each diagonal block of R^T is written as zeros (the padding of R^T Y)
+  auto res_tile = [&](int I0, int t, int &I, int &J) __attribute__((always_inline)) {
+    const int g = min(GR, NB - I0);
+    for (int d = NB - 1 - I0; d >= 0; --d) {
+      const int n = min(g, NB - d - I0);                 // group rows with I + d < NB
+      if (t < n) {
+        I = I0 + t;
+        J = I + d;
+        return true;
+      }
+      t -= n;
+    }
+    return false;
+  };
+  for (int it = 0; it < residual; ++it) {
+    f32x4 acc[SR];
+    int I0p = -1;
+    for (int I0 = 0; I0 < NB; I0 += GR) {
+      // R^T rows of the group: I - Y - Y M^T
+#pragma unroll
+      for (int s = 0; s < SR; ++s) {
+        int I, J;
+        if (!res_tile(I0, s * NW + w, I, J)) continue;
+        const f32x4 p = ymt(I, J);
+        const int r = 16 * I + lr, c = 16 * J + 4 * lq;
+        float y[4], v[4];
+        planes_get4<C>(Yp, C, r, c, y);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ((r == c + q) ? 1.f : 0.f) - y[q] - p[q];
+        planes_put4<C>(Rp, 16 * GR, r - 16 * I0, c, v);
+        if (I == J && I > 0) {
+          const float z[4] = {0.f, 0.f, 0.f, 0.f};
+          planes_put4<C>(Rp, 16 * GR, r - 16 * I0, c - 16, z);
+        }
+      }
+      // the previous group's update: rows above this group
+      if (I0p >= 0) {
+#pragma unroll
+        for (int s = 0; s < SR; ++s) {
+          int I, J;
+          if (!res_tile(I0p, s * NW + w, I, J)) continue;
+          const int r = 16 * I + lr, c = 16 * J + 4 * lq;
+          float y[4];
+          planes_get4<C>(Yp, C, r, c, y);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] += acc[s][q];
+          planes_put4<C>(Yp, C, r, c, y);
+        }
+      }
+      __syncthreads();
+      // (R^T Y)[16 I + lr][16 J + 4 lq + q]: Y down its columns, R^T along its rows
+#pragma unroll
+      for (int s = 0; s < SR; ++s) {
+        int I, J;
+        if (!res_tile(I0, s * NW + w, I, J)) continue;
+        int k0, k1;
+        upper_range(I, J, k0, k1);
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        auto steps = [&](auto n) __attribute__((always_inline)) {
+          constexpr int N = decltype(n)::value;
+          FragS yc[N], rr[N];
+#pragma unroll
+          for (int u = 0; u < N; ++u) {
+            yc[u] = planes_col8<C>(Yp, C, k0 + 32 * u + 8 * lq, 16 * J + lr);
+            rr[u] = planes_row8<C>(Rp, 16 * GR, 16 * (I - I0) + lr, k0 + 32 * u + 8 * lq);
+          }
+#pragma unroll
+          for (int u = 0; u < N; ++u) mma(a, yc[u], rr[u]);
+        };
+        switch ((k1 - k0) >> 5) {
+          case 1: steps(std::integral_constant<int, 1>()); break;
+          case 2: if constexpr (NB >= 4) steps(std::integral_constant<int, 2>()); break;
+          case 3: if constexpr (NB >= 6) steps(std::integral_constant<int, 3>()); break;
+          case 4: if constexpr (NB >= 8) steps(std::integral_constant<int, 4>()); break;
+          default: break;
+        }
+        acc[s] = a;
+      }
+      __syncthreads();
+      I0p = I0;
+    }
+#pragma unroll
+    for (int s = 0; s < SR; ++s) {
+      int I, J;
+      if (!res_tile(I0p, s * NW + w, I, J)) continue;
+      const int r = 16 * I + lr, c = 16 * J + 4 * lq;
+      float y[4];
+      planes_get4<C>(Yp, C, r, c, y);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] += acc[s][q];
+      planes_put4<C>(Yp, C, r, c, y);
+    }
+    __syncthreads();
   }
 }
 
@@ -720,6 +1141,9 @@ struct PrepItem {
   // (written before a barrier that precedes the call).
   __device__ __forceinline__ void solve_store(float *gsolve, float *asolve, const TIn (&bets)[NBET],
                                               bool bet0_ready) const {
+    // bf16 Neumann with one beta head per key head: the solve on split-bf16
+    // planes, which leaves X^T in asolve's bytes and overwrites G
+    const bool planes = !P::kF32 && a.solve == 1 && Rb == 1 && !a.bwd;
     for (int rb = 0; rb < Rb; ++rb) {
       const int hb = hk * Rb + rb;
       __syncthreads();
@@ -734,7 +1158,14 @@ struct PrepItem {
           if constexpr (NTH != 512) solve_exact<C, false, false>(gsolve, bet, asolve, tmp);
         }
       } else if (a.solve == 1) {
-        solve_neumann<C>(gsolve, bet, asolve, tmp, a.order, a.residual);
+        if constexpr (!P::kF32) {
+          if (planes)
+            solve_neumann_planes<C, NTH>(gsolve, bet, asolve, tmp, a.order, a.residual);
+          else
+            solve_neumann<C, NTH, Split>(gsolve, bet, asolve, tmp, a.order, a.residual);
+        } else {
+          solve_neumann<C, NTH, Split>(gsolve, bet, asolve, tmp, a.order, a.residual);
+        }
       } else {
         solve_block_neumann<C>(gsolve, bet, asolve, tmp, a.order);
       }
@@ -757,6 +1188,10 @@ struct PrepItem {
             const int rr = C - 1 - col - e;
             x[e] = upper ? 0.f : bet[rr] * asolve[rr * (C + 4) + C - 1 - row];
           }
+        } else if (planes) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[e] = upper ? 0.f : bet[row] * planes_get<C>(reinterpret_cast<const bf16 *>(asolve), C, col + e, row);
         } else {
           const float4 a0 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col);
           const float4 a1 = *reinterpret_cast<const float4 *>(asolve + row * (C + 4) + col + 4);
