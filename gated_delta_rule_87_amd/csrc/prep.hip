@@ -675,12 +675,17 @@ __device__ __forceinline__ void solve_neumann_planes(float *gmat, const float *b
 #pragma unroll
     for (int e = 0; e < 8; ++e) gv[j][e] = (k + e < c) ? gv[j][e] * bb[e] : 0.f;   // M[c][k + e]
   }
+  const float keep = order > 0 ? 1.f : 0.f;
+#pragma unroll 4
   for (int u = tid; u < C * C / 4; u += NTH) {
     const int r = u % C, c = 4 * (u / C);              // neighbouring lanes read neighbouring G columns
+    const float br = bet[r] * keep;
     float v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = ((r == c + e) ? 1.f : 0.f) - ((order > 0 && c + e > r) ? gmat[(c + e) * LD + r] * bet[r] : 0.f);
+    for (int e = 0; e < 4; ++e) {
+      const float g = gmat[(c + e) * LD + r];          // read unconditionally: no branch, no wait per element
+      v[e] = ((r == c + e) ? 1.f : 0.f) - ((c + e > r) ? g * br : 0.f);
+    }
     planes_put4<C>(Yp, C, r, c, v);
   }
   __syncthreads();
@@ -727,18 +732,20 @@ __device__ __forceinline__ void solve_neumann_planes(float *gmat, const float *b
     }
     return acc;
   };
+  int tI[SL], tJ[SL];
+  bool tv[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) tv[s] = my_tile(s, tI[s], tJ[s]);
   for (int it = 1; it < order; ++it) {
     f32x4 acc[SL];
 #pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      int I, J;
-      if (my_tile(s, I, J)) acc[s] = ymt(I, J);
-    }
+    for (int s = 0; s < SL; ++s)
+      if (tv[s]) acc[s] = ymt(tI[s], tJ[s]);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
-      int I, J;
-      if (!my_tile(s, I, J)) continue;
+      if (!tv[s]) continue;
+      const int I = tI[s], J = tJ[s];
       const int r = 16 * I + lr, c = 16 * J + 4 * lq;
       float v[4];
 #pragma unroll
@@ -748,7 +755,85 @@ __device__ __forceinline__ void solve_neumann_planes(float *gmat, const float *b
     __syncthreads();
   }
 
-  // residual corrections by groups of GR row blocks of R^T (top to bottom):
+  // (R^T Y)[16 I + lr][16 J + 4 lq + q], R^T's rows I from planes Rt with
+  // `rows` rows starting at row block I0: Y down its columns, R^T along its rows
+  auto rty = [&](const bf16 *Rt, int rows, int I0, int I, int J) __attribute__((always_inline)) {
+    int k0, k1;
+    upper_range(I, J, k0, k1);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    auto steps = [&](auto n) __attribute__((always_inline)) {
+      constexpr int N = decltype(n)::value;
+      FragS yc[N], rr[N];
+#pragma unroll
+      for (int u = 0; u < N; ++u) {
+        yc[u] = planes_col8<C>(Yp, C, k0 + 32 * u + 8 * lq, 16 * J + lr);
+        rr[u] = planes_row8<C>(Rt, rows, 16 * (I - I0) + lr, k0 + 32 * u + 8 * lq);
+      }
+#pragma unroll
+      for (int u = 0; u < N; ++u) mma(a, yc[u], rr[u]);
+    };
+    switch ((k1 - k0) >> 5) {
+      case 1: steps(std::integral_constant<int, 1>()); break;
+      case 2: if constexpr (NB >= 4) steps(std::integral_constant<int, 2>()); break;
+      case 3: if constexpr (NB >= 6) steps(std::integral_constant<int, 3>()); break;
+      case 4: if constexpr (NB >= 8) steps(std::integral_constant<int, 4>()); break;
+      default: break;
+    }
+    return a;
+  };
+  // R^T = I - Y - Y M^T at tile (I, J) (this lane's four entries)
+  auto rt_tile = [&](int I, int J, float (&v)[4]) __attribute__((always_inline)) {
+    const f32x4 p = ymt(I, J);
+    const int r = 16 * I + lr, c = 16 * J + 4 * lq;
+    float y[4];
+    planes_get4<C>(Yp, C, r, c, y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = ((r == c + q) ? 1.f : 0.f) - y[q] - p[q];
+  };
+  auto add_to_y = [&](int I, int J, const f32x4 &d) __attribute__((always_inline)) {
+    const int r = 16 * I + lr, c = 16 * J + 4 * lq;
+    float y[4];
+    planes_get4<C>(Yp, C, r, c, y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] += d[q];
+    planes_put4<C>(Yp, C, r, c, y);
+  };
+  // The last correction (the only one at r = 1): M is not read again, so
+  // R^T goes whole into M's planes, its tiles dealt like the Horner step's;
+  // four barriers.
+  auto last_correction = [&]() __attribute__((always_inline)) {
+    f32x4 acc[SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      if (!tv[s]) continue;
+      float v[4];
+      rt_tile(tI[s], tJ[s], v);
+      acc[s] = f32x4{v[0], v[1], v[2], v[3]};
+    }
+    __syncthreads();                                   // every read of M done
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      if (!tv[s]) continue;
+      const int I = tI[s], J = tJ[s], r = 16 * I + lr, c = 16 * J + 4 * lq;
+      const float v[4] = {acc[s][0], acc[s][1], acc[s][2], acc[s][3]};
+      planes_put4<C>(Mp, C, r, c, v);
+      if (I == J && I > 0) {                           // zero block left of the diagonal: R^T Y's padding
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        planes_put4<C>(Mp, C, r, c - 16, z);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+      if (tv[s]) acc[s] = rty(Mp, C, 0, tI[s], tJ[s]);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+      if (tv[s]) add_to_y(tI[s], tJ[s], acc[s]);
+    __syncthreads();
+  };
+
+  // Earlier corrections (r > 1) by groups of GR row blocks of R^T (top to bottom):
   // tile t of the group at I0, longest contraction first; the block left of
   // each diagonal block of R^T is written as zeros (the padding of R^T Y)
   auto res_tile = [&](int I0, int t, int &I, int &J) __attribute__((always_inline)) {
@@ -765,20 +850,28 @@ __device__ __forceinline__ void solve_neumann_planes(float *gmat, const float *b
     return false;
   };
   for (int it = 0; it < residual; ++it) {
+    if (it == residual - 1) {
+      last_correction();
+      break;
+    }
     f32x4 acc[SR];
-    int I0p = -1;
+    int pI[SR], pJ[SR];                                // the previous group's tiles
+    bool pv[SR];
+#pragma unroll
+    for (int s = 0; s < SR; ++s) pv[s] = false;
     for (int I0 = 0; I0 < NB; I0 += GR) {
+      int gI[SR], gJ[SR];
+      bool gv2[SR];
+#pragma unroll
+      for (int s = 0; s < SR; ++s) gv2[s] = res_tile(I0, s * NW + w, gI[s], gJ[s]);
       // R^T rows of the group: I - Y - Y M^T
 #pragma unroll
       for (int s = 0; s < SR; ++s) {
-        int I, J;
-        if (!res_tile(I0, s * NW + w, I, J)) continue;
-        const f32x4 p = ymt(I, J);
+        if (!gv2[s]) continue;
+        const int I = gI[s], J = gJ[s];
         const int r = 16 * I + lr, c = 16 * J + 4 * lq;
-        float y[4], v[4];
-        planes_get4<C>(Yp, C, r, c, y);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = ((r == c + q) ? 1.f : 0.f) - y[q] - p[q];
+        float v[4];
+        rt_tile(I, J, v);
         planes_put4<C>(Rp, 16 * GR, r - 16 * I0, c, v);
         if (I == J && I > 0) {
           const float z[4] = {0.f, 0.f, 0.f, 0.f};
@@ -786,62 +879,27 @@ __device__ __forceinline__ void solve_neumann_planes(float *gmat, const float *b
         }
       }
       // the previous group's update: rows above this group
-      if (I0p >= 0) {
+      {
 #pragma unroll
         for (int s = 0; s < SR; ++s) {
-          int I, J;
-          if (!res_tile(I0p, s * NW + w, I, J)) continue;
-          const int r = 16 * I + lr, c = 16 * J + 4 * lq;
-          float y[4];
-          planes_get4<C>(Yp, C, r, c, y);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) y[q] += acc[s][q];
-          planes_put4<C>(Yp, C, r, c, y);
+          if (pv[s]) add_to_y(pI[s], pJ[s], acc[s]);
         }
       }
       __syncthreads();
-      // (R^T Y)[16 I + lr][16 J + 4 lq + q]: Y down its columns, R^T along its rows
+#pragma unroll
+      for (int s = 0; s < SR; ++s)
+        if (gv2[s]) acc[s] = rty(Rp, 16 * GR, I0, gI[s], gJ[s]);
+      __syncthreads();
 #pragma unroll
       for (int s = 0; s < SR; ++s) {
-        int I, J;
-        if (!res_tile(I0, s * NW + w, I, J)) continue;
-        int k0, k1;
-        upper_range(I, J, k0, k1);
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        auto steps = [&](auto n) __attribute__((always_inline)) {
-          constexpr int N = decltype(n)::value;
-          FragS yc[N], rr[N];
-#pragma unroll
-          for (int u = 0; u < N; ++u) {
-            yc[u] = planes_col8<C>(Yp, C, k0 + 32 * u + 8 * lq, 16 * J + lr);
-            rr[u] = planes_row8<C>(Rp, 16 * GR, 16 * (I - I0) + lr, k0 + 32 * u + 8 * lq);
-          }
-#pragma unroll
-          for (int u = 0; u < N; ++u) mma(a, yc[u], rr[u]);
-        };
-        switch ((k1 - k0) >> 5) {
-          case 1: steps(std::integral_constant<int, 1>()); break;
-          case 2: if constexpr (NB >= 4) steps(std::integral_constant<int, 2>()); break;
-          case 3: if constexpr (NB >= 6) steps(std::integral_constant<int, 3>()); break;
-          case 4: if constexpr (NB >= 8) steps(std::integral_constant<int, 4>()); break;
-          default: break;
-        }
-        acc[s] = a;
+        pv[s] = gv2[s];
+        pI[s] = gI[s];
+        pJ[s] = gJ[s];
       }
-      __syncthreads();
-      I0p = I0;
     }
 #pragma unroll
-    for (int s = 0; s < SR; ++s) {
-      int I, J;
-      if (!res_tile(I0p, s * NW + w, I, J)) continue;
-      const int r = 16 * I + lr, c = 16 * J + 4 * lq;
-      float y[4];
-      planes_get4<C>(Yp, C, r, c, y);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] += acc[s][q];
-      planes_put4<C>(Yp, C, r, c, y);
-    }
+    for (int s = 0; s < SR; ++s)
+      if (pv[s]) add_to_y(pI[s], pJ[s], acc[s]);
     __syncthreads();
   }
 }

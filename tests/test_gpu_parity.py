@@ -120,7 +120,8 @@ def test_chunk_fwd_nonzero_h0(name):
 @pytest.mark.parametrize("name,order,res", [("kda_c128_strong", 4, 1), ("kda_bf16", 2, 1), ("kda_f32_c128", 3, 2),
                                             ("kda_c64_mixed", 3, 1), ("gdn_f32_c64_mixed", 4, 1),
                                             ("gva_g4_bf16", 1, 0), ("kda_bf16_c32", 2, 1), ("gdn_f32_c32", 1, 0),
-                                            ("g16_c128_bkh", 2, 1)])
+                                            ("g16_c128_bkh", 2, 1), ("kda_bf16", 2, 2), ("kda_c128_strong", 1, 3),
+                                            ("kda_bf16_c32", 0, 2)])
 def test_neumann_small(name, order, res):
     w = SMALL[name].with_(neumann_order=order, neumann_residual=res)
     raw, x = draw(w)
