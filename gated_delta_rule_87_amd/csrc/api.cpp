@@ -119,7 +119,7 @@ gdr::WsLayout layout_of(const gdr_problem *p) {
   const int nc = (int)(((size_t)p->T + p->chunk - 1) / p->chunk);
   const int hb = p->beta_per_key_head ? p->H_k : p->H_v;
   gdr::WsLayout w = gdr::ws_layout(p->B, p->H_k, hb, nc, p->chunk, p->d_k, p->in_dtype == GDR_BF16);
-  w.seg_bytes = gdr::scan_seg_bytes(p->B, p->H_v, nc, p->d_k, p->d_v);
+  w.seg_bytes = gdr::scan_seg_bytes(p->B, p->H_v, nc, p->d_k, p->d_v, p->chunk, p->in_dtype != GDR_BF16);
   w.total = w.seg_off + ((w.seg_bytes + 255) & ~(size_t)255);
   return w;
 }

@@ -64,12 +64,14 @@ struct ChunkArgs {
   float momentum;
   const float *z0;
   float *zT;
-  // Segment-parallel scan: chunks per segment (0 = one segment); the scan's
-  // h0 of segment y (blockIdx.y) is h0 + y * h0_seg_stride; the transfer pass
-  // writes [J | B] per segment to xfer.
+  // Segment-parallel scan: chunks per segment (0 = one segment).  A launch
+  // covers segments seg0 + y (y = blockIdx.y); the scan's h0 of segment
+  // seg0 + y is h0 + y * h0_seg_stride, and the transfer pass writes [J | B]
+  // of segment seg0 + y to slot y of xfer.
   int seg_len;
   size_t h0_seg_stride;
   float *xfer;
+  int seg0;
   // Training forward: the scan stores the state entering every chunk,
   // S_{c-1}, to states [B][H_v][N_c][d_k][d_v] (nullable; fp16 for bf16
   // inputs, fp32 for fp32 inputs).
@@ -171,8 +173,8 @@ bool prep_supported(int C, int d_k, int G);
 int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16);
 // Segments of the segment-parallel scan (1 = one scan over the whole
 // sequence) and the bytes of its workspace region.
-int scan_segments(int B, int H_v, int N_c, int d_v);
-size_t scan_seg_bytes(int B, int H_v, int N_c, int d_k, int d_v);
+int scan_segments(int B, int H_v, int N_c, int d_v, int C, int d_k, bool f32);
+size_t scan_seg_bytes(int B, int H_v, int N_c, int d_k, int d_v, int C, bool f32);
 size_t prep_lds_bytes(int C, int d_k, int G);
 
 }  // namespace gdr

@@ -151,9 +151,12 @@ __device__ __forceinline__ T *at(T *base, unsigned off) {
 // values, initial state 0); it writes [J | B] and no output.
 // kSave (training forward): the state entering each chunk, S_{c-1}, is also
 // stored to a.states for the backward pass.
+// The body takes its workgroup index bx of gx, its segment sgi (ChunkArgs
+// seg0 + the launch's segment slot) and whether it is the sequence's last
+// segment (it writes hT).
 template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom, bool kXfer = false,
           bool kSave = false>
-__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
+__device__ __forceinline__ void scan_body(const ChunkArgs &a, int bx, int gx, int sgi, bool last_seg) {
   static_assert(!(kMom && kXfer), "momentum doubles the carried state: no transfer pass");
   static_assert(!(kSave && (kMom || kXfer)), "saved states: plain forward only");
   constexpr int FB = P::kF32 ? 2048 : 1024;
@@ -189,14 +192,13 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   // of one head, which read the same operand tiles, on one XCD and so behind
   // one L2.
   const int NX = (kXfer ? DK + a.d_v : a.d_v) / BV;
-  int unit = blockIdx.x;
-  if (gridDim.x % kXcds == 0) unit = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+  int unit = bx;
+  if (gx % kXcds == 0) unit = (bx % kXcds) * (gx / kXcds) + bx / kXcds;
   const int c0 = (unit % NX) * BV, hv = (unit / NX) % a.H_v, b = unit / (NX * a.H_v);
   const bool jcols = kXfer && c0 < DK;        // transfer pass: columns of J (no value input)
   const int vc0 = kXfer ? c0 - DK : c0;       // first value column of the tile
-  // Segment of the sequence (blockIdx.y): chunks [cb, ce).  One segment (the
-  // whole sequence) unless the segment-parallel scan split it.
-  const int sgi = blockIdx.y;
+  // Segment of the sequence: chunks [cb, ce).  One segment (the whole
+  // sequence) unless the segment-parallel scan split it.
   const int cb = a.seg_len ? min(sgi * a.seg_len, a.N_c) : 0;
   const int ce = a.seg_len ? min(cb + a.seg_len, a.N_c) : a.N_c;
   const int R = a.H_v / a.H_k;
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         if constexpr (kXfer) {
           S[r][u][e] = (jcols && i == col) ? 1.f : 0.f;   // [I | 0]
         } else {
-          S[r][u][e] = a.h0 ? a.h0[(size_t)sgi * a.h0_seg_stride + sbase + (size_t)i * a.d_v + col] : 0.f;
+          S[r][u][e] = a.h0 ? a.h0[(size_t)(sgi - a.seg0) * a.h0_seg_stride + sbase + (size_t)i * a.d_v + col] : 0.f;
         }
         if constexpr (kMom) Z[r][u][e] = a.z0 ? a.z0[sbase + (size_t)i * a.d_v + col] : 0.f;
       }
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
   if constexpr (kXfer) {
     // [J | B] of this segment: [B][H_v][d_k][d_k + d_v] per segment
     const int W = DK + a.d_v;
-    float *xo = a.xfer + (size_t)sgi * ((size_t)a.B * a.H_v * DK * W) + ((size_t)b * a.H_v + hv) * DK * W;
+    float *xo = a.xfer + (size_t)(sgi - a.seg0) * ((size_t)a.B * a.H_v * DK * W) + ((size_t)b * a.H_v + hv) * DK * W;
 #pragma unroll
     for (int r = 0; r < SJ::RPW; ++r) {
       const int i0 = 16 * SJ::blk(w, r);
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
     }
     return;
   }
-  if (a.hT && sgi == (int)gridDim.y - 1) {
+  if (a.hT && last_seg) {
 #pragma unroll
     for (int r = 0; r < SJ::RPW; ++r) {
       const int i0 = 16 * SJ::blk(w, r);
@@ -663,6 +665,29 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
         }
       }
     }
+  }
+}
+
+template <typename TIn, typename TOut, class P, int C, int DK, int BV, bool kMom, bool kXfer = false,
+          bool kSave = false>
+__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(ChunkArgs a) {
+  scan_body<TIn, TOut, P, C, DK, BV, kMom, kXfer, kSave>(a, blockIdx.x, gridDim.x, a.seg0 + blockIdx.y,
+                                                          blockIdx.y == gridDim.y - 1);
+}
+
+// First phase of the segment-parallel scan, one launch: workgroups
+// [0, n_scan) scan segment 0 from h0 (32-column tiles; its final state,
+// S_in(1), goes to as.hT), the others run the transfer pass of segments
+// 1 .. P-2 (BVX-column tiles, n_xfer workgroups per segment).
+template <typename TIn, typename TOut, class P, int C, int DK, int BVX>
+__global__ __launch_bounds__(64 * kScanWaves) void scan_split_kernel(ChunkArgs as, ChunkArgs ax, int n_scan,
+                                                                     int n_xfer) {
+  const int g = blockIdx.x;
+  if (g < n_scan) {
+    scan_body<TIn, TOut, P, C, DK, 32, false>(as, g, n_scan, 0, true);
+  } else {
+    const int x = g - n_scan;
+    scan_body<TIn, TOut, P, C, DK, BVX, false, true>(ax, x % n_xfer, n_xfer, ax.seg0 + x / n_xfer, false);
   }
 }
 
@@ -697,36 +722,56 @@ int scan_choose_bv(int B, int H_v, int C, int d_k, int d_v, bool in_bf16) {
 
 // ------------------------------------------------ segment-parallel scan
 // When the (batch, value head, 32-column tile) units cannot fill the GPU
-// (fewer than 256), the sequence is cut into P segments of L chunks that are
-// scanned at the same time (Systolic Linear Attention, section 3.3: a
-// chunk's state update is an affine map S -> J S + B, and maps compose).
-//   1. Transfer pass (scan_kernel, kXfer): segments 0 .. P-2 each scan the
-//      columns [J | B] of their own map from [I | 0], without output.
-//   2. Combine (seg_combine_kernel): S_in(0) = h0, S_in(p+1) = J_p S_in(p) + B_p.
-//   3. The ordinary scan of all P segments at once, segment p from S_in(p),
-//      writing o; the last one writes hT.
-// Momentum doubles the carried state (S and Z), so it keeps one segment.
-// The transfer columns cost about (d_k + d_v) / d_v of a scan without its
-// output phase, so splitting pays only when it adds CUs.
-int scan_segments(int B, int H_v, int N_c, int d_v) {
+// (fewer than 256), the sequence is cut into P segments of L chunks
+// (Systolic Linear Attention, section 3.3: a chunk's state update is an
+// affine map S -> J S + B, and maps compose).
+//   1. One launch (scan_split_kernel): segment 0 is scanned from h0, writing
+//      its output and its final state S_in(1); beside it, segments 1 .. P-2
+//      each scan the columns [J | B] of their own map from [I | 0], without
+//      output (the transfer pass).
+//   2. Combine (seg_combine_kernel): S_in(p+1) = J_p S_in(p) + B_p, p >= 1.
+//   3. The ordinary scan of segments 1 .. P-1 at once, segment p from
+//      S_in(p), writing o; the last one writes hT.
+// P is the largest count for which both scan launches fit one workgroup per
+// CU: (P - 1) scan units, and one scan unit plus P - 2 transfer units.
+// Momentum doubles the carried state (S and Z), and the training forward
+// keeps its per-chunk states, so both keep one segment.
+// Transfer-pass workgroups per segment: (d_k + d_v) / 64 column tiles where
+// the lean layout fits, else / 32.
+static int xfer_units(int B, int H_v, int C, int d_k, int d_v, bool f32) {
+  bool k64 = false;
+  const int fb = f32 ? 2048 : 1024;
+#define GDR_X64(c_, dk_) \
+  if (C == c_ && d_k == dk_) \
+    k64 = (fb == 1024 ? ScanLayout<c_, dk_, 64, 1024, true>::total : ScanLayout<c_, dk_, 64, 2048, true>::total) <= \
+          160 * 1024;
+  GDR_X64(32, 64) GDR_X64(32, 128) GDR_X64(32, 256) GDR_X64(64, 64) GDR_X64(64, 128) GDR_X64(64, 256)
+  GDR_X64(128, 64) GDR_X64(128, 128) GDR_X64(128, 256)
+#undef GDR_X64
+  const int w = (k64 && (d_k + d_v) % 64 == 0) ? 64 : 32;
+  return B * H_v * ((d_k + d_v) / w);
+}
+
+int scan_segments(int B, int H_v, int N_c, int d_v, int C, int d_k, bool f32) {
   if (d_v % 32 != 0) return 1;
   const long units = (long)B * H_v * (d_v / 32);
   if (units >= 256) return 1;
-  int P = (int)(256 / units);
-  P = P < 16 ? P : 16;
-  P = P < N_c / 8 ? P : N_c / 8;              // at least 8 chunks per segment
-  return P >= 2 ? P : 1;
+  const long ux = xfer_units(B, H_v, C, d_k, d_v, f32);
+  int P = 2;
+  while (P < 17 && P + 1 <= N_c / 6 && (long)P * units <= 256 && units + (long)(P - 1) * ux <= 256) ++P;
+  return P >= 3 ? P : 1;                      // two segments would run one after the other
 }
 
-size_t scan_seg_bytes(int B, int H_v, int N_c, int d_k, int d_v) {
-  const int P = scan_segments(B, H_v, N_c, d_v);
+size_t scan_seg_bytes(int B, int H_v, int N_c, int d_k, int d_v, int C, bool f32) {
+  const int P = scan_segments(B, H_v, N_c, d_v, C, d_k, f32);
   if (P < 2) return 0;
   const size_t unit = (size_t)B * H_v * d_k;
-  return 4 * ((size_t)(P - 1) * unit * (d_k + d_v) + (size_t)P * unit * d_v);   // [J | B] per segment, S_in per segment
+  // [J | B] of segments 1 .. P-2, S_in of segments 1 .. P-1
+  return 4 * ((size_t)(P - 2) * unit * (d_k + d_v) + (size_t)(P - 1) * unit * d_v);
 }
 
-// S_in of every segment for one (batch, value head, 32-column tile):
-// S_in(0) = h0 (or 0), S_in(p + 1) = J_p S_in(p) + B_p, in fp32.  The kernel
+// S_in of segments 2 .. P-1 for one (batch, value head, 32-column tile):
+// S_in(p + 1) = J_p S_in(p) + B_p, in fp32, from S_in(1).  The kernel
 // is a chain of P - 1 dependent steps, so its time is load latency, not
 // arithmetic: 256 threads each own RT = d_k / 32 rows and 4 columns (column
 // group t % 8) and read their rows of J_p with 32 loads in flight per slab.
@@ -747,17 +792,14 @@ __global__ __launch_bounds__(combine_threads<DK>()) void seg_combine_kernel(Chun
   const int W = DK + a.d_v;
   const size_t unit = (size_t)b * a.H_v + hv;
   const size_t slot = (size_t)a.B * a.H_v * DK * a.d_v;           // elements of one segment's states
-  float *xs0 = xstate + unit * DK * a.d_v + c0;
+  float *xs0 = xstate + unit * DK * a.d_v + c0;       // slot 0: S_in(1), from segment 0's scan
   for (int i = tid; i < DK * 8; i += NTH) {
     const int r = i >> 3, q = i & 7;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.h0) v = *reinterpret_cast<const float4 *>(a.h0 + unit * DK * a.d_v + (size_t)r * a.d_v + c0 + 4 * q);
-    sh[r][q] = v;
-    *reinterpret_cast<float4 *>(xs0 + (size_t)r * a.d_v + 4 * q) = v;
+    sh[r][q] = *reinterpret_cast<const float4 *>(xs0 + (size_t)r * a.d_v + 4 * q);
   }
   __syncthreads();
-  for (int p = 0; p + 1 < P; ++p) {
-    const float *xo = a.xfer + (size_t)p * a.B * a.H_v * DK * W + unit * DK * W + (size_t)(tr * RT) * W;
+  for (int p = 1; p + 1 < P; ++p) {                   // [J_p | B_p] in transfer slot p - 1
+    const float *xo = a.xfer + (size_t)(p - 1) * a.B * a.H_v * DK * W + unit * DK * W + (size_t)(tr * RT) * W;
     float4 acc[RT];
 #pragma unroll
     for (int j = 0; j < RT; ++j) acc[j] = *reinterpret_cast<const float4 *>(xo + (size_t)j * W + DK + c0 + 4 * tc);
@@ -785,7 +827,7 @@ __global__ __launch_bounds__(combine_threads<DK>()) void seg_combine_kernel(Chun
       }
     }
     __syncthreads();                          // every thread has read S_in(p)
-    float *xs = xs0 + (size_t)(p + 1) * slot;
+    float *xs = xs0 + (size_t)p * slot;                // S_in(p + 1) in slot p
 #pragma unroll
     for (int j = 0; j < RT; ++j) {
       sh[tr * RT + j][tc] = acc[j];
@@ -816,52 +858,63 @@ static hipError_t launch_scan_t(const ChunkArgs &a, hipStream_t stream, int segm
   return hipGetLastError();
 }
 
-template <typename TIn, typename TOut, class P, int C, int DK, int BV>
-static hipError_t launch_xfer_t(const ChunkArgs &a, hipStream_t stream, int segments) {
-  const size_t lds = ScanLayout<C, DK, BV, P::kF32 ? 2048 : 1024, true>::total;
-  auto kern = scan_kernel<TIn, TOut, P, C, DK, BV, false, true>;
-  hipError_t e = allow_full_lds(reinterpret_cast<const void *>(kern));
-  if (e != hipSuccess) return e;
-  dim3 grid(((DK + a.d_v) / BV) * a.H_v * a.B, segments);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * kScanWaves), lds, stream, a);
-  return hipGetLastError();
-}
-
 template <typename TIn, typename TOut, class P, int C, int DK>
 static hipError_t launch_segmented(const ChunkArgs &a, hipStream_t s, int segments) {
   constexpr int FB = P::kF32 ? 2048 : 1024;
   const int L = (a.N_c + segments - 1) / segments;
   segments = (a.N_c + L - 1) / L;
+  if (segments < 3) return launch_scan_t<TIn, TOut, P, C, DK, 32>(a, s);
   float *seg = reinterpret_cast<float *>(a.ws + a.wl.seg_off);
   const size_t unit = (size_t)a.B * a.H_v * DK;
-  float *xstate = seg + (size_t)(segments - 1) * unit * (DK + a.d_v);
-  ChunkArgs ax = a;
-  ax.seg_len = L;
-  ax.xfer = seg;
+  float *xstate = seg + (size_t)(segments - 2) * unit * (DK + a.d_v);
   hipError_t e;
-  // transfer pass over segments 0 .. P-2: 64-column tiles where the lean
-  // layout fits the CU's LDS (fewer workgroups stream the same operands)
+  // 1. segment 0 from h0 (final state to S_in(1)) beside the transfer pass of
+  //    segments 1 .. P-2 (64-column tiles where the lean layout fits: fewer
+  //    workgroups stream the same operands)
+  ChunkArgs as = a, ax = a;
+  as.seg_len = ax.seg_len = L;
+  as.seg0 = 0;
+  as.hT = xstate;
+  ax.seg0 = 1;
+  ax.xfer = seg;
+  const int n_scan = (a.d_v / 32) * a.H_v * a.B;
+  auto split = [&](auto bvx) -> hipError_t {
+    constexpr int BVX = decltype(bvx)::value;
+    auto kern = scan_split_kernel<TIn, TOut, P, C, DK, BVX>;
+    const size_t l0 = ScanLayout<C, DK, 32, FB>::total, l1 = ScanLayout<C, DK, BVX, FB, true>::total;
+    hipError_t err = allow_full_lds(reinterpret_cast<const void *>(kern));
+    if (err != hipSuccess) return err;
+    const int n_xfer = ((DK + a.d_v) / BVX) * a.H_v * a.B;
+    hipLaunchKernelGGL(kern, dim3(n_scan + (segments - 2) * n_xfer), dim3(64 * kScanWaves), l0 > l1 ? l0 : l1, s,
+                       as, ax, n_scan, n_xfer);
+    return hipGetLastError();
+  };
   constexpr bool k64 = ScanLayout<C, DK, 64, FB, true>::total <= 160 * 1024;
   if (k64 && (DK + a.d_v) % 64 == 0) {
-    e = launch_xfer_t<TIn, TOut, P, C, DK, k64 ? 64 : 32>(ax, s, segments - 1);
+    e = split(std::integral_constant<int, k64 ? 64 : 32>());
   } else {
-    e = launch_xfer_t<TIn, TOut, P, C, DK, 32>(ax, s, segments - 1);
+    e = split(std::integral_constant<int, 32>());
   }
   if (e != hipSuccess) return e;
+  // 2. S_in(2) .. S_in(P-1)
   hipLaunchKernelGGL(seg_combine_kernel<DK>, dim3(a.d_v / 32, a.H_v, a.B), dim3(combine_threads<DK>()), 0, s, ax,
                      segments, xstate);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 3. segments 1 .. P-1, segment p from S_in(p) (slot p - 1)
   ChunkArgs ac = a;
   ac.seg_len = L;
+  ac.seg0 = 1;
   ac.h0 = xstate;
   ac.h0_seg_stride = unit * a.d_v;
-  return launch_scan_t<TIn, TOut, P, C, DK, 32>(ac, s, segments);
+  return launch_scan_t<TIn, TOut, P, C, DK, 32>(ac, s, segments - 1);
 }
 
 template <typename TIn, typename TOut, class P, int C, int DK>
 static hipError_t launch_scan_bv(const ChunkArgs &a, hipStream_t s) {
-  const int segments = a.momentum != 0.f ? 1 : scan_segments(a.B, a.H_v, a.N_c, a.d_v);
-  if (segments > 1 && a.wl.seg_bytes >= scan_seg_bytes(a.B, a.H_v, a.N_c, DK, a.d_v) &&
+  const int segments = (a.momentum != 0.f || a.states)
+                           ? 1
+                           : scan_segments(a.B, a.H_v, a.N_c, a.d_v, C, DK, P::kF32);
+  if (segments > 1 && a.wl.seg_bytes >= scan_seg_bytes(a.B, a.H_v, a.N_c, DK, a.d_v, C, P::kF32) &&
       scan_lds_bytes(C, DK, 32, P::kF32 ? 2048 : 1024) <= 160 * 1024)
     return launch_segmented<TIn, TOut, P, C, DK>(a, s, segments);
   const int bv = a.states ? 32 : scan_choose_bv(a.B, a.H_v, C, DK, a.d_v, sizeof(TIn) == 2);

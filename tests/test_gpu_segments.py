@@ -2,7 +2,7 @@
 units cannot fill the GPU: the sequence is cut into segments whose affine
 maps S -> J S + B are composed, Systolic Linear Attention section 3.3)
 against the fp64 oracle.  Every case here has fewer than 256 units and at
-least 16 chunks, so the library splits it (into 3 to 5 segments); together
+least 18 chunks, so the library splits it (into 3 to 10 segments); together
 they cover both transfer-pass tile widths (64 columns at C = 64 and 128 with
 d_k <= 128 or C = 64 with d_k = 256; 32 columns otherwise and for fp32),
 ragged final chunks, a nonzero h0, per-key-head beta up to 2, document
