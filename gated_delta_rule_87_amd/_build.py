@@ -18,7 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "prep.hip", "scan.hip", "recurrent.hip", "noalloc.hip", "epilogue.hip", "verify.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "prep.hip", "scan.hip", "recurrent.hip", "noalloc.hip", "epilogue.hip", "verify.hip", "bwd.hip",
+           "pad.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -328,14 +328,18 @@ def gdr_chunk_scan(q, k, v, beta, log_alpha, h0=None, *, workspace, chunk=64, so
 
 
 def gdr_chunk_prepare(q, k, beta, log_alpha, *, chunk=64, solve="exact", neumann_order=4,
-                      neumann_residual_steps=1, H_v=None, workspace=None, stream=None):
+                      neumann_residual_steps=1, H_v=None, d_v=None, workspace=None, stream=None):
     """The parallel half of the chunk forward.  Returns (workspace, problem):
     ``workspace`` (allocated as uint8 if not given) holds the prepared chunk
-    quantities laid out as gdr_chunk_workspace_layout(problem) gives."""
+    quantities laid out as gdr_chunk_workspace_layout(problem) gives.  d_v:
+    the value width of the scan that will read it (the workspace size depends
+    on it through the segment-parallel scan's region and chunk 16's padded
+    copies); by default the smallest width the chunk size takes."""
     lib = load()
     B, T, Hk, dk = q.shape
     Hv = beta.shape[2] if H_v is None else H_v
-    fake_v = torch.empty((B, T, Hv, 16), dtype=q.dtype, device=q.device)
+    dv = d_v if d_v is not None else (32 if chunk <= 32 else 16)
+    fake_v = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=q.device)
     _check_inputs(q, k, fake_v, beta, log_alpha)
     p = make_problem(q, fake_v, log_alpha, beta, chunk=chunk, solve=solve, neumann_order=neumann_order,
                      neumann_residual_steps=neumann_residual_steps)

@@ -37,6 +37,15 @@ int log2_exact(int x) {
   return ((1 << s) == x) ? s : -1;
 }
 
+// Chunk size 16 runs the C = 32 path on a padded sequence: every 16 tokens
+// followed by 16 identity tokens (csrc/pad.hip).
+gdr_problem padded16(const gdr_problem *p) {
+  gdr_problem q = *p;
+  q.chunk = 32;
+  q.T = 32 * ((p->T + 15) / 16);
+  return q;
+}
+
 // Shape checks shared by both paths.  `chunked` adds the chunk-path fields.
 gdr_status check_problem(const gdr_problem *p, bool chunked) {
   if (!p) return fail(GDR_ERR_INVALID_ARG, "problem is NULL");
@@ -78,8 +87,16 @@ gdr_status check_problem(const gdr_problem *p, bool chunked) {
         return fail(GDR_ERR_INVALID_ARG, "neumann_order=%d residual_steps=%d too large", p->neumann_order,
                     p->neumann_residual_steps);
     }
+    if (p->chunk == 16) {
+      // runs as 32-token chunks whose second halves are identity tokens
+      const long long tp = 32LL * ((p->T + 15) / 16);
+      if (tp > 2147483647LL || (double)p->B * (double)tp > 2147483647.0)
+        return fail(GDR_ERR_UNSUPPORTED, "chunk=16: the padded sequence (2 T tokens) is too long");
+      const gdr_problem pp = padded16(p);
+      return check_problem(&pp, true);
+    }
     if (!(p->chunk == 32 || p->chunk == 64 || p->chunk == 128))
-      return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: libgdr supports chunk in {32, 64, 128}", p->chunk);
+      return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: libgdr supports chunk in {16, 32, 64, 128}", p->chunk);
     if (p->chunk == 32 && p->d_v % 32 != 0)
       return fail(GDR_ERR_UNSUPPORTED, "chunk=32 needs d_v a multiple of 32 (d_v=%d)", p->d_v);
     // prep: one 256-thread workgroup per chunk along x; scan: one 512-thread
@@ -115,7 +132,42 @@ gdr_status check_ptr(const void *ptr, const char *name, bool required, uintptr_t
   return GDR_OK;
 }
 
+// Chunk size 16: the padded copies of the inputs and of o, after the padded
+// problem's own workspace (offsets from the workspace start, 256-aligned).
+struct Pad16Layout {
+  size_t q, k, v, beta, la, reset, o, end;
+};
+gdr::WsLayout layout_of(const gdr_problem *p);
+Pad16Layout pad16_layout(const gdr_problem *p) {
+  const gdr_problem pp = padded16(p);
+  const size_t rows = (size_t)p->B * pp.T;
+  const size_t es = p->in_dtype == GDR_BF16 ? 2 : 4, os = p->out_dtype == GDR_BF16 ? 2 : 4;
+  const size_t hb = p->beta_per_key_head ? p->H_k : p->H_v;
+  Pad16Layout L;
+  size_t at = layout_of(&pp).total;
+  auto take = [&](size_t bytes) {
+    const size_t o = at;
+    at = (at + bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  L.q = take(rows * p->H_k * p->d_k * es);
+  L.k = take(rows * p->H_k * p->d_k * es);
+  L.v = take(rows * p->H_v * p->d_v * es);
+  L.beta = take(rows * hb * es);
+  L.la = take(rows * p->H_k * p->gate_groups * es);
+  L.reset = take(rows);
+  L.o = take(rows * p->H_v * p->d_v * os);
+  L.end = at;
+  return L;
+}
+
 gdr::WsLayout layout_of(const gdr_problem *p) {
+  if (p->chunk == 16) {
+    const gdr_problem pp = padded16(p);
+    gdr::WsLayout w = layout_of(&pp);
+    w.total = pad16_layout(p).end;
+    return w;
+  }
   const int nc = (int)(((size_t)p->T + p->chunk - 1) / p->chunk);
   const int hb = p->beta_per_key_head ? p->H_k : p->H_v;
   gdr::WsLayout w = gdr::ws_layout(p->B, p->H_k, hb, nc, p->chunk, p->d_k, p->in_dtype == GDR_BF16);
@@ -150,6 +202,26 @@ gdr::ChunkArgs make_chunk_args(const gdr_problem *p, void *workspace) {
 
 gdr_status launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return GDR_OK;
+}
+
+// Chunk size 16: the key-side inputs (each nullable) to their padded copies.
+gdr_status pad_inputs16(const gdr_problem *p, const gdr_problem &pp, const Pad16Layout &L, unsigned char *ws,
+                        const void *q, const void *k, const void *beta, const void *log_alpha, hipStream_t st) {
+  const size_t es = p->in_dtype == GDR_BF16 ? 2 : 4;
+  const size_t hb = p->beta_per_key_head ? p->H_k : p->H_v;
+  const struct {
+    const void *src;
+    size_t off, row;
+  } t[4] = {{q, L.q, (size_t)p->H_k * p->d_k * es},
+            {k, L.k, (size_t)p->H_k * p->d_k * es},
+            {beta, L.beta, hb * es},
+            {log_alpha, L.la, (size_t)p->H_k * p->gate_groups * es}};
+  for (const auto &x : t) {
+    if (!x.src) continue;
+    gdr_status s = launched(gdr::launch_pad_rows(ws + x.off, x.src, x.row, p->B, p->T, pp.T, false, st), "pad kernel");
+    if (s != GDR_OK) return s;
+  }
   return GDR_OK;
 }
 
@@ -199,17 +271,75 @@ gdr_status gdr_chunk_prepare(const gdr_problem *p, const void *q, const void *k,
     return s;
   if (workspace_bytes < ws_bytes(p))
     return fail(GDR_ERR_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, ws_bytes(p));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p->chunk == 16) {
+    const gdr_problem pp = padded16(p);
+    const Pad16Layout L = pad16_layout(p);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    if ((s = pad_inputs16(p, pp, L, ws, q, k, beta, log_alpha, st)) != GDR_OK) return s;
+    gdr::ChunkArgs a = make_chunk_args(&pp, workspace);
+    a.q = ws + L.q;
+    a.k = ws + L.k;
+    a.beta = ws + L.beta;
+    a.log_alpha = ws + L.la;
+    return launched(gdr::launch_prep(a, p->in_dtype == GDR_BF16, st), "prep kernel");
+  }
   gdr::ChunkArgs a = make_chunk_args(p, workspace);
   a.q = q;
   a.k = k;
   a.beta = beta;
   a.log_alpha = log_alpha;
-  return launched(gdr::launch_prep(a, p->in_dtype == GDR_BF16, static_cast<hipStream_t>(stream)), "prep kernel");
+  return launched(gdr::launch_prep(a, p->in_dtype == GDR_BF16, st), "prep kernel");
 }
 
 }  // extern "C"
 
 namespace gdr {
+
+// Chunk size 16: pad the inputs into the workspace, run the C = 32 path on
+// the padded sequence (its own workspace at the front), gather o back.  The
+// final state is unaffected by the identity tokens.
+gdr_status chunk_forward16(const gdr_problem *p, const void *q, const void *k, const void *v, const void *beta,
+                           const void *log_alpha, const float *h0, void *o, float *hT, const void *workspace,
+                           size_t workspace_bytes, void *stream, bool prepare, const gdr_layer_opts *opts,
+                           void *states) {
+  const gdr_problem pp = padded16(p);
+  if (states) return set_error(GDR_ERR_UNSUPPORTED, "chunk=16: the training forward runs at chunk 64");
+  if (p->B == 0 || p->T == 0)
+    return chunk_forward(&pp, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes, stream, prepare, opts,
+                         nullptr);
+  gdr_status s;
+  if ((s = check_ptr(q, "q", prepare)) || (s = check_ptr(k, "k", prepare)) || (s = check_ptr(v, "v", true)) ||
+      (s = check_ptr(beta, "beta", prepare)) || (s = check_ptr(log_alpha, "log_alpha", prepare)) ||
+      (s = check_ptr(o, "o", true)) || (s = check_ptr(workspace, "workspace", true, 256)))
+    return s;
+  size_t need = 0;
+  if ((s = workspace_bytes_of(p, &need)) != GDR_OK) return s;
+  if (workspace_bytes < need) return set_error(GDR_ERR_WORKSPACE, "workspace_bytes is below gdr_chunk_fwd_workspace_size");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Pad16Layout L = pad16_layout(p);
+  unsigned char *ws = static_cast<unsigned char *>(const_cast<void *>(workspace));
+  const size_t es = p->in_dtype == GDR_BF16 ? 2 : 4, os = p->out_dtype == GDR_BF16 ? 2 : 4;
+  if (prepare && (s = pad_inputs16(p, pp, L, ws, q, k, beta, log_alpha, st)) != GDR_OK) return s;
+  if ((s = launched(launch_pad_rows(ws + L.v, v, (size_t)p->H_v * p->d_v * es, p->B, p->T, pp.T, false, st),
+                    "pad kernel")) != GDR_OK)
+    return s;
+  gdr_layer_opts o2{};
+  if (opts) {
+    o2 = *opts;
+    if (opts->reset) {
+      if ((s = launched(launch_pad_rows(ws + L.reset, opts->reset, 1, p->B, p->T, pp.T, false, st), "pad kernel")) !=
+          GDR_OK)
+        return s;
+      o2.reset = ws + L.reset;
+    }
+  }
+  s = chunk_forward(&pp, ws + L.q, ws + L.k, ws + L.v, ws + L.beta, ws + L.la, h0, ws + L.o, hT, workspace,
+                    ws_bytes(&pp), stream, prepare, opts ? &o2 : nullptr, nullptr);
+  if (s != GDR_OK) return s;
+  return launched(launch_pad_rows(o, ws + L.o, (size_t)p->H_v * p->d_v * os, p->B, p->T, pp.T, true, st),
+                  "unpad kernel");
+}
 
 // Shared by gdr_chunk_fwd (prepare + scan), gdr_chunk_scan (scan only) and
 // the entry point that brings its own scratch (noalloc.hip).
@@ -219,6 +349,8 @@ gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, con
                          void *states) {
   gdr_status s = check_problem(p, true);
   if (s != GDR_OK) return s;
+  if (p->chunk == 16) return chunk_forward16(p, q, k, v, beta, log_alpha, h0, o, hT, workspace, workspace_bytes,
+                                             stream, prepare, opts, states);
   if ((s = check_ptr(h0, "h0", false)) || (s = check_ptr(hT, "hT", false)) || (s = check_ptr(states, "states", false)))
     return s;
   const bool mom = opts && opts->momentum != 0.f;

@@ -161,6 +161,10 @@ gdr_status chunk_forward(const gdr_problem *p, const void *q, const void *k, con
                          void *states = nullptr);
 // Workspace bytes of a valid problem (else the validation status).
 gdr_status workspace_bytes_of(const gdr_problem *p, size_t *bytes);
+// Rows of [B][T] tokens to the padded sequence of chunk size 16 (real token
+// t at 32 (t / 16) + t % 16 of Tp, zeros elsewhere), or back (unpad).
+hipError_t launch_pad_rows(void *dst, const void *src, size_t row_bytes, int B, int T, int Tp, bool unpad,
+                           hipStream_t s);
 // Record `text` as this thread's gdr_last_error() and return s.
 gdr_status set_error(gdr_status s, const char *text);
 

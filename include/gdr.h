@@ -115,12 +115,18 @@ typedef struct {
  * are those of its last real token.  Region
  * offsets: gdr_chunk_workspace_layout.
  * When the (batch, value head, 32 value columns) units number fewer than
- * 256, d_v is a multiple of 32 and there are at least 16 chunks, the scan is
- * split into P segments of the sequence scanned at once (the affine chunk
- * map of section 3.3 composed across segments) and the workspace ends with
- * one more region, after GM at a 256-byte boundary, of
- * 4 B H_v d_k ((P - 1)(d_k + d_v) + P d_v) bytes: each segment's transition
- * [J | B] and entry state.  The total size includes it.
+ * 256, d_v is a multiple of 32 and there are at least 18 chunks, the scan is
+ * split into P >= 3 segments of the sequence (the affine chunk map of
+ * section 3.3 composed across segments) and the workspace ends with one
+ * more region, after GM at a 256-byte boundary, of
+ * 4 B H_v d_k ((P - 2)(d_k + d_v) + (P - 1) d_v) bytes: the transitions
+ * [J | B] of segments 1 .. P-2 and the entry states of segments 1 .. P-1.
+ * The total size includes it.
+ * Chunk 16 runs as chunk 32 on a padded sequence of T' = 32 ceil(T / 16)
+ * tokens, each 16 tokens followed by 16 identity tokens (zero q, k, v, beta
+ * and log alpha), which leaves the state and the per-16-token in-chunk
+ * matrices as they are: the regions above are those of that padded problem
+ * (chunk 32, T'), followed by padded copies of the inputs and of o.
  */
 size_t gdr_chunk_fwd_workspace_size(const gdr_problem *p);
 
@@ -142,8 +148,8 @@ gdr_status gdr_chunk_workspace_layout(const gdr_problem *p, size_t *offsets);
  *   workspace : device scratch of at least gdr_chunk_fwd_workspace_size(p)
  *               bytes, 256-byte aligned; its contents on return are the
  *               per-chunk quantities documented there.
- * Supported here: in_dtype bf16 or f32, chunk 32, 64 or 128, d_k in {64,128,256},
- * d_v a multiple of 16 (of 32 with chunk 32), G a divisor of d_k, B and H_v at most 65535, fewer
+ * Supported here: in_dtype bf16 or f32, chunk 16, 32, 64 or 128, d_k in {64,128,256},
+ * d_v a multiple of 16 (of 32 with chunk 16 or 32), G a divisor of d_k, B and H_v at most 65535, fewer
  * than 2^24 chunks per sequence, B H_v d_v / 16 below 2^23 and
  * chunk H_v d_v below 2^30 (one chunk of v or o within 4 GiB); beyond that
  * GDR_ERR_UNSUPPORTED.

@@ -86,6 +86,25 @@ def test_workspace_size():
         gb.gdr_chunk_workspace_layout(problem(H_v=30))
 
 
+def test_workspace_size_chunk16():
+    """Chunk 16 runs as chunk 32 on T' = 32 ceil(T / 16) tokens: its
+    workspace is that padded problem's, followed by padded copies of q, k, v,
+    beta, log alpha, the reset flags and o (each 256-byte aligned)."""
+    lib = gb.load()
+    B, T, Hk, Hv, dk, dv, G = 2, 300, 2, 4, 128, 64, 128
+    p = problem(B=B, T=T, H_k=Hk, H_v=Hv, d_k=dk, d_v=dv, chunk=16, gate_groups=G)
+    Tp = 32 * -(-T // 16)
+    pp = problem(B=B, T=Tp, H_k=Hk, H_v=Hv, d_k=dk, d_v=dv, chunk=32, gate_groups=G)
+    base = lib.gdr_chunk_fwd_workspace_size(ctypes.byref(pp))   # with the segment-parallel scan's region
+    assert base >= expected_regions(B, Tp, Hk, Hv, dk, 32)["total"]
+    up = lambda n: -(-n // 256) * 256
+    rows = B * Tp
+    extra = sum(up(n) for n in (rows * Hk * dk * 2, rows * Hk * dk * 2, rows * Hv * dv * 2, rows * Hv * 2,
+                                rows * Hk * G * 2, rows, rows * Hv * dv * 4))
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(p)) == base + extra
+    assert gb.gdr_chunk_workspace_layout(p)["KB"] == expected_regions(B, Tp, Hk, Hv, dk, 32)["KB"]
+
+
 FAKE = 0x10000          # 64 KiB-aligned non-null address, never dereferenced
 MIS = 0x10004           # misaligned
 
@@ -117,7 +136,8 @@ def call_fwd(p, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, la=FAKE, h0=None, o=FAKE, hT=
     (dict(d_k=96, gate_groups=96), gb.GDR_ERR_UNSUPPORTED),
     (dict(d_v=72), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=48), gb.GDR_ERR_UNSUPPORTED),
-    (dict(chunk=16), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=16, d_v=48), gb.GDR_ERR_UNSUPPORTED),
+    (dict(chunk=24), gb.GDR_ERR_UNSUPPORTED),
     (dict(chunk=32, d_v=48), gb.GDR_ERR_UNSUPPORTED),
     (dict(solve=2, neumann_order=-1), gb.GDR_ERR_INVALID_ARG),
     (dict(chunk=128, d_k=256, gate_groups=256), gb.GDR_ERR_UNSUPPORTED),

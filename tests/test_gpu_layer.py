@@ -35,6 +35,7 @@ LAYER = {
                                 alpha_sigma=2.0, seed=305),
     "gdn_f32": Workload("gdn_f32", 2, 300, 2, 2, 64, 64, 64, 1, "f32", seed=306),
     "kda_c32": Workload("kda_c32", 2, 700, 2, 2, 128, 64, 32, 128, "bf16", beta_scale=2.0, seed=308),
+    "kda_c16": Workload("kda_c16", 2, 500, 2, 2, 128, 64, 16, 128, "bf16", beta_scale=2.0, seed=309),
     "kda_f32_c128": Workload("kda_f32_c128", 1, 333, 2, 4, 128, 32, 128, 128, "f32", beta_scale=2.0, seed=307),
 }
 
@@ -87,7 +88,7 @@ def test_layer_exact(name, mu):
     assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype] and ez <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name", ["kda_c64_mixed", "sla_c128", "kda_c128_strong", "kda_f32_c128"])
+@pytest.mark.parametrize("name", ["kda_c64_mixed", "sla_c128", "kda_c128_strong", "kda_f32_c128", "kda_c16"])
 def test_layer_neumann(name):
     w = LAYER[name]
     raw, x = draw(w)

@@ -60,6 +60,12 @@ SMALL = {
                             beta_scale=2.0, seed=33),
     "kda_c32_mixed": Workload("kda_c32_mixed", 1, 400, 2, 2, 128, 64, 32, 128, "bf16", alpha_mu=0.0,
                               alpha_sigma=2.0, seed=34),
+    # chunk 16: the C = 32 path on the sequence padded with 16 identity tokens
+    # after every 16 (ragged tails, fp32 and bf16, d_k = 256 with per-key-head beta)
+    "gdn_f32_c16": Workload("gdn_f32_c16", 2, 300, 2, 2, 64, 64, 16, 1, "f32", seed=35),
+    "kda_bf16_c16": Workload("kda_bf16_c16", 1, 517, 2, 2, 128, 64, 16, 128, "bf16", seed=36),
+    "sla_c16_bkh": Workload("sla_c16_bkh", 1, 250, 2, 8, 256, 64, 16, 4, "bf16", beta_per_key_head=True,
+                            beta_scale=2.0, seed=37),
     # chunk 128, d_k <= 128 (eight-wave block-pivot kernel): every log-alpha
     # layout of a lane's eight channels -- at most four groups read as
     # scalars (G = 1, 4), one group per 8-channel vector (G = 16) and two
@@ -102,7 +108,7 @@ def test_chunk_fwd_small(name):
     assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("name", ["gdn_f32", "kda_bf16", "dk64_bkh_gva", "kda_bf16_c32"])
+@pytest.mark.parametrize("name", ["gdn_f32", "kda_bf16", "dk64_bkh_gva", "kda_bf16_c32", "gdn_f32_c16"])
 def test_chunk_fwd_nonzero_h0(name):
     w = SMALL[name]
     raw, x = draw(w)
@@ -121,7 +127,7 @@ def test_chunk_fwd_nonzero_h0(name):
                                             ("kda_c64_mixed", 3, 1), ("gdn_f32_c64_mixed", 4, 1),
                                             ("gva_g4_bf16", 1, 0), ("kda_bf16_c32", 2, 1), ("gdn_f32_c32", 1, 0),
                                             ("g16_c128_bkh", 2, 1), ("kda_bf16", 2, 2), ("kda_c128_strong", 1, 3),
-                                            ("kda_bf16_c32", 0, 2)])
+                                            ("kda_bf16_c32", 0, 2), ("kda_bf16_c16", 2, 1), ("gdn_f32_c16", 3, 1)])
 def test_neumann_small(name, order, res):
     w = SMALL[name].with_(neumann_order=order, neumann_residual=res)
     raw, x = draw(w)
@@ -140,7 +146,7 @@ def test_neumann_small(name, order, res):
 
 @pytest.mark.parametrize("name,order", [("kda_c128_strong", 1), ("kda_bf16", 1), ("kda_f32_c128", 1),
                                         ("gdn_f32_c64_mixed", 2), ("gva_g4_bf16", 1), ("dk64_bkh_gva", 1),
-                                        ("kda_f32_c128", 7), ("gdn_f32", 3), ("kda_bf16_c32", 1),
+                                        ("kda_f32_c128", 7), ("gdn_f32", 3), ("kda_bf16_c32", 1), ("sla_c16_bkh", 1),
                                         ("gdn_bf16_c128", 1), ("gdn_f32_c128_dk64", 1)])
 def test_block_neumann_small(name, order):
     """SLA section 2.4.3's block-Jacobi Neumann solve (order 1 = 1-Step
@@ -164,7 +170,7 @@ def test_block_neumann_small(name, order):
 
 
 @pytest.mark.parametrize("name", ["kda_bf16", "gdn_bf16", "f32_bv32", "c128_bv32_bf16", "kda_bf16_c32",
-                                  "seg_kda_c64"])
+                                  "seg_kda_c64", "kda_bf16_c16"])
 def test_chunk_fwd_bf16_output(name):
     """out_dtype bf16 (its own o staging and row pieces, 16- and 32-column scan
     tiles, the segment-parallel scan): o is the fp32-output result rounded once
@@ -185,7 +191,7 @@ def test_chunk_fwd_bf16_output(name):
 SEG_CASE = Workload("seg_kda_c64", 1, 3000, 2, 2, 128, 64, 64, 128, "bf16", seed=17)
 
 
-@pytest.mark.parametrize("name", ["kda_bf16", "f32_bv32", "seg_kda_c64"])
+@pytest.mark.parametrize("name", ["kda_bf16", "f32_bv32", "seg_kda_c64", "kda_bf16_c16"])
 def test_hT_may_alias_h0(name):
     """gdr.h: hT may alias h0 (each workgroup reads its h0 tile before writing
     its hT tile; the segment-parallel path reads h0 in the combine, before the
@@ -283,3 +289,21 @@ def test_recurrent_step(name):
     eo, eh = rel_err(o.cpu().numpy(), o_ref), rel_err(state.cpu().numpy(), h_ref)
     print(f"  err o={eo:.3e} state={eh:.3e}", flush=True)
     assert eo <= 1e-5 and eh <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["kda_bf16_c16", "gdn_f32_c16"])
+def test_chunk16_prepare_then_scan(name):
+    """Chunk 16 through the split entry points: gdr_chunk_prepare pads the
+    key side into the workspace, gdr_chunk_scan pads v and gathers o; the
+    result equals gdr_chunk_fwd bit for bit."""
+    w = SMALL[name]
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    print(f"[case] chunk 16 prepare + scan {name}", flush=True)
+    o1, h1 = run_chunk(dev, w)
+    ws, _ = gb.gdr_chunk_prepare(dev["q"], dev["k"], dev["beta"], dev["log_alpha"], chunk=16, H_v=w.H_v,
+                                 d_v=w.d_v)
+    o2, h2 = gb.gdr_chunk_scan(dev["q"], dev["k"], dev["v"], dev["beta"], dev["log_alpha"], None, workspace=ws,
+                               chunk=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
