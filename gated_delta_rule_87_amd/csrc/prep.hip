@@ -1197,11 +1197,14 @@ struct PrepItem {
   // a 16 x 32 block that straddles the diagonal as zeros, blocks wholly above
   // it not at all.  bet0_ready: the first head's beta is already in LDS
   // (written before a barrier that precedes the call).
+  // kApprox: the Neumann solves are compiled in (the exact solve's kernels
+  // leave them out, which keeps their register allocation and schedule).
+  template <bool kApprox = true>
   __device__ __forceinline__ void solve_store(float *gsolve, float *asolve, const TIn (&bets)[NBET],
                                               bool bet0_ready) const {
     // bf16 Neumann with one beta head per key head: the solve on split-bf16
     // planes, which leaves X^T in asolve's bytes and overwrites G
-    const bool planes = !P::kF32 && a.solve == 1 && Rb == 1 && !a.bwd;
+    const bool planes = kApprox && !P::kF32 && a.solve == 1 && Rb == 1 && !a.bwd;
     for (int rb = 0; rb < Rb; ++rb) {
       const int hb = hk * Rb + rb;
       __syncthreads();
@@ -1215,17 +1218,19 @@ struct PrepItem {
         } else {
           if constexpr (NTH != 512) solve_exact<C, false, false>(gsolve, bet, asolve, tmp);
         }
-      } else if (a.solve == 1) {
-        if constexpr (!P::kF32) {
-          if (planes)
-            solve_neumann_planes<C, NTH>(gsolve, bet, asolve, tmp, a.order, a.residual);
-          else
+      } else if constexpr (kApprox) {
+        if (a.solve == 1) {
+          if constexpr (!P::kF32) {
+            if (planes)
+              solve_neumann_planes<C, NTH>(gsolve, bet, asolve, tmp, a.order, a.residual);
+            else
+              solve_neumann<C, NTH, Split>(gsolve, bet, asolve, tmp, a.order, a.residual);
+          } else {
             solve_neumann<C, NTH, Split>(gsolve, bet, asolve, tmp, a.order, a.residual);
+          }
         } else {
-          solve_neumann<C, NTH, Split>(gsolve, bet, asolve, tmp, a.order, a.residual);
+          solve_block_neumann<C>(gsolve, bet, asolve, tmp, a.order);
         }
-      } else {
-        solve_block_neumann<C>(gsolve, bet, asolve, tmp, a.order);
       }
       __syncthreads();
       // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y.
@@ -1361,7 +1366,7 @@ struct LaLane {
     }
   }
 };
-template <typename TIn, class P, int DK, int kGate>
+template <typename TIn, class P, int DK, int kGate, bool kApprox>
 __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   using X = PrepItem<TIn, P, C, DK>;
@@ -1583,7 +1588,7 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
     }
   }
   x.zero_upper_L();
-  x.solve_store(gsolve, x.ureg, bets, true);
+  x.template solve_store<kApprox>(gsolve, x.ureg, bets, true);
 }
 
 // Block-pivot route for one chunk: p = first token of the row block; every
@@ -1736,7 +1741,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
 // reason the fp16 K-hat^T fragments come from an MFMA with an identity
 // operand (one nonzero product per output, exact) instead of an LDS
 // transpose.  The backward pass never prepares C = 128 chunks.
-template <typename TIn, class P, int DK, int kGate>
+template <typename TIn, class P, int DK, int kGate, bool kApprox>
 __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
   constexpr int C = 128, NTH = 512;
   using X = PrepItem<TIn, P, C, DK, NTH>;
@@ -2026,7 +2031,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
     }
   }
   x.zero_upper_L();
-  x.solve_store(gmat, x.smem, bets, true);
+  x.template solve_store<kApprox>(gmat, x.smem, bets, true);
 }
 
 // Grid (N_c, H_k, B), one chunk per work group.  d_k <= 128: eight waves
@@ -2103,9 +2108,13 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   hipError_t e;
   if constexpr (C == 128 && DK <= 128) {
     if (a.bwd) return hipErrorInvalidValue;            // the backward pass prepares C = 64 chunks only
-    auto block = a.G == DK  ? prep_block128_kernel<TIn, P, DK, kGatePerChannel>
-                 : a.G >= 8 ? prep_block128_kernel<TIn, P, DK, kGateGroupsVec>
-                            : prep_block128_kernel<TIn, P, DK, kGateGroupsFew>;
+    const bool ap = a.solve != 0;
+    auto block = a.G == DK  ? (ap ? prep_block128_kernel<TIn, P, DK, kGatePerChannel, true>
+                                  : prep_block128_kernel<TIn, P, DK, kGatePerChannel, false>)
+                 : a.G >= 8 ? (ap ? prep_block128_kernel<TIn, P, DK, kGateGroupsVec, true>
+                                  : prep_block128_kernel<TIn, P, DK, kGateGroupsVec, false>)
+                            : (ap ? prep_block128_kernel<TIn, P, DK, kGateGroupsFew, true>
+                                  : prep_block128_kernel<TIn, P, DK, kGateGroupsFew, false>);
     const size_t lds_b = prep_block8_lds_bytes(C, DK, a.G);
     if ((e = set_lds(block, lds_b)) != hipSuccess) return e;
     hipLaunchKernelGGL(block, grid, dim3(512), lds_b, stream, a);
@@ -2118,9 +2127,13 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(block, grid, dim3(nth), lds_b, stream, a);
     return hipGetLastError();
   } else {
-  auto chunk = a.G == DK  ? prep_chunk_kernel<TIn, P, DK, kGatePerChannel>
-               : a.G >= 8 ? prep_chunk_kernel<TIn, P, DK, kGateGroupsVec>
-                          : prep_chunk_kernel<TIn, P, DK, kGateGroupsFew>;
+  const bool ap = a.solve != 0;
+  auto chunk = a.G == DK  ? (ap ? prep_chunk_kernel<TIn, P, DK, kGatePerChannel, true>
+                                : prep_chunk_kernel<TIn, P, DK, kGatePerChannel, false>)
+               : a.G >= 8 ? (ap ? prep_chunk_kernel<TIn, P, DK, kGateGroupsVec, true>
+                                : prep_chunk_kernel<TIn, P, DK, kGateGroupsVec, false>)
+                          : (ap ? prep_chunk_kernel<TIn, P, DK, kGateGroupsFew, true>
+                                : prep_chunk_kernel<TIn, P, DK, kGateGroupsFew, false>);
   auto listed = prep_block_listed_kernel<TIn, P, C, DK>;
   const size_t chunk_lds = prep_chunk_lds_bytes(C, DK);
   if ((e = set_lds(chunk, chunk_lds)) != hipSuccess) return e;
