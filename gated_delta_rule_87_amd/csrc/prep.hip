@@ -921,12 +921,15 @@ constexpr float kWideMark = -1.f;
 // One (batch, key head, chunk) work item: indices, LDS carve-up, pointers.
 // NTH threads (256 or 512); with 512 the per-wave transpose buffers sit in
 // the solve's scratch.
-template <typename TIn, class P, int C, int DK, int NTH = 256>
+// kFwdOnly: the item never prepares for the backward pass (its code is left
+// out of the forward kernels).
+template <typename TIn, class P, int C, int DK, int NTH = 256, bool kFwdOnly = false>
 struct PrepItem {
   static constexpr int NB = C / 16;
   static constexpr int NKV = (C * DK / 8 + NTH - 1) / NTH;  // bound on 8-element log-alpha vectors per thread
   static constexpr int KS = DK / 32;
   using Split = typename P::Split;
+  __device__ __forceinline__ bool bwd() const { return !kFwdOnly && a.bwd != 0; }
   // workspace tiles: fp16 for bf16 inputs, fp32 for fp32 inputs
   using IO = TileIO<typename std::conditional<P::kF32, PrecF32, PrecF16>::type>;
 
@@ -1098,7 +1101,7 @@ struct PrepItem {
   // KB = J Khat (token rows), QB = (J Qbar)^T and KH = (J Kbar)^T.
   __device__ __forceinline__ void scan_operands(int I, int s, const float (&kbar)[8], const float (&qbar)[8],
                                                 const float (&kh)[8]) const {
-    if (a.bwd) {
+    if (bwd()) {
       IO::put_plain8(tKB, (NB - 1 - I) * KS + s, 16 * lq + 15 - lr, kh);
       put_channel_rows(tQB, I, s, qbar, true);
       put_channel_rows(tKH, I, s, kbar, true);
@@ -1138,7 +1141,7 @@ struct PrepItem {
   // diagonal are zero.  Backward preparation: block (I, J) of L is block
   // (NB-1-J, NB-1-I) of J L^T J, entry (r, c) at (15 - c, 15 - r).
   __device__ __forceinline__ void store_L_block(int I, int J, const f32x4 &acc) const {
-    const bool rev = a.bwd != 0;
+    const bool rev = bwd() != 0;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int r = 4 * lq + q4;
@@ -1204,7 +1207,7 @@ struct PrepItem {
                                               bool bet0_ready) const {
     // bf16 Neumann with one beta head per key head: the solve on split-bf16
     // planes, which leaves X^T in asolve's bytes and overwrites G
-    const bool planes = kApprox && !P::kF32 && a.solve == 1 && Rb == 1 && !a.bwd;
+    const bool planes = kApprox && !P::kF32 && a.solve == 1 && Rb == 1 && !bwd();
     for (int rb = 0; rb < Rb; ++rb) {
       const int hb = hk * Rb + rb;
       __syncthreads();
@@ -1213,7 +1216,7 @@ struct PrepItem {
         __syncthreads();
       }
       if (a.solve == 0) {
-        if (NTH == 512 || !a.bwd) {
+        if (NTH == 512 || !bwd()) {
           solve_exact<C, NTH == 512, true>(gsolve, bet, asolve, tmp);
         } else {
           if constexpr (NTH != 512) solve_exact<C, false, false>(gsolve, bet, asolve, tmp);
@@ -1236,7 +1239,7 @@ struct PrepItem {
       // diag(beta) A_c: the scan's chunk writes are E_c = diag(beta) A_c Y.
       // The exact solve has already scaled the rows, except for the
       // backward pass (four waves), which also stores A unscaled.
-      const bool scaled = a.solve == 0 && (NTH == 512 || !a.bwd);
+      const bool scaled = a.solve == 0 && (NTH == 512 || !bwd());
       void *tA = ws_tile(a, kWsA, a.H_beta, hb, b, c);
       for (int u = tid; u < C * C / 8; u += blockDim.x) {   // unit = fragment (row, col .. col + 7)
         const int blk = u >> 6, f = u & 63;
@@ -1244,7 +1247,7 @@ struct PrepItem {
         const int row = 16 * (blk / (C / 32)) + (f & 15), col = 32 * (blk % (C / 32)) + 8 * (f >> 4);
         const bool upper = col / 16 > row / 16;             // the half of a straddling block above the diagonal
         float x[8];
-        if (a.bwd) {
+        if (bwd()) {
           // J (diag(beta) A)^T J: entry (row, col) = beta_r A[r][C-1-row], r = C-1-col
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -1265,7 +1268,7 @@ struct PrepItem {
         }
         IO::put_plain8(tA, blk, f, x);
       }
-      if (a.bwd) {
+      if (bwd()) {
         // the gradient kernel's copies: A_c unscaled and (once) G_c, fp32 row-major
         float *au = a.au + (((size_t)b * a.H_beta + hb) * a.N_c + c) * (C * C);
         for (int u = tid; u < C * C / 4; u += blockDim.x) {
@@ -1366,10 +1369,13 @@ struct LaLane {
     }
   }
 };
-template <typename TIn, class P, int DK, int kGate, bool kApprox>
+// kMode: 0 the exact solve, forward only; 1 the exact solve, forward or
+// backward preparation; 2 the Neumann solves (forward only).
+template <typename TIn, class P, int DK, int kGate, int kMode>
 __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
-  using X = PrepItem<TIn, P, C, DK>;
+  constexpr bool kApprox = kMode == 2;
+  using X = PrepItem<TIn, P, C, DK, 256, kMode != 1>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -1490,7 +1496,7 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
   // L, stored without a transpose; the backward pass's reversed layouts go
   // through the transpose buffers.
   using IO = typename X::IO;
-  const bool fwd = !a.bwd;                             // uniform
+  const bool fwd = !x.bwd();                           // uniform
   unsigned char *colop = reinterpret_cast<unsigned char *>(x.ureg);
   Split ak[KS], aq[KS];
   f32x4 dG = {0.f, 0.f, 0.f, 0.f}, dL = {0.f, 0.f, 0.f, 0.f};
@@ -2127,13 +2133,15 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(block, grid, dim3(nth), lds_b, stream, a);
     return hipGetLastError();
   } else {
-  const bool ap = a.solve != 0;
-  auto chunk = a.G == DK  ? (ap ? prep_chunk_kernel<TIn, P, DK, kGatePerChannel, true>
-                                : prep_chunk_kernel<TIn, P, DK, kGatePerChannel, false>)
-               : a.G >= 8 ? (ap ? prep_chunk_kernel<TIn, P, DK, kGateGroupsVec, true>
-                                : prep_chunk_kernel<TIn, P, DK, kGateGroupsVec, false>)
-                          : (ap ? prep_chunk_kernel<TIn, P, DK, kGateGroupsFew, true>
-                                : prep_chunk_kernel<TIn, P, DK, kGateGroupsFew, false>);
+  const int md = a.solve != 0 ? 2 : a.bwd ? 1 : 0;
+  auto pick = [&](auto g) {
+    constexpr int kG = decltype(g)::value;
+    return md == 2 ? prep_chunk_kernel<TIn, P, DK, kG, 2>
+                   : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1> : prep_chunk_kernel<TIn, P, DK, kG, 0>;
+  };
+  auto chunk = a.G == DK  ? pick(std::integral_constant<int, kGatePerChannel>())
+               : a.G >= 8 ? pick(std::integral_constant<int, kGateGroupsVec>())
+                          : pick(std::integral_constant<int, kGateGroupsFew>());
   auto listed = prep_block_listed_kernel<TIn, P, C, DK>;
   const size_t chunk_lds = prep_chunk_lds_bytes(C, DK);
   if ((e = set_lds(chunk, chunk_lds)) != hipSuccess) return e;
