@@ -1602,9 +1602,9 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
 // is at most the block's decay range (<= kPivotRange unless the block is
 // flagged and evaluated entry by entry).  Wave w owns blocks w (and 7 - w
 // when C = 128).
-template <typename TIn, class P, int C, int DK, int NTH>
+template <typename TIn, class P, int C, int DK, int NTH, bool kFwdOnly = false>
 __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int hk, int b, float *smem) {
-  using X = PrepItem<TIn, P, C, DK, NTH>;
+  using X = PrepItem<TIn, P, C, DK, NTH, kFwdOnly>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS;
   constexpr int NWV = NTH / 64;                        // waves
@@ -1750,7 +1750,7 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
 template <typename TIn, class P, int DK, int kGate, bool kApprox>
 __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
   constexpr int C = 128, NTH = 512;
-  using X = PrepItem<TIn, P, C, DK, NTH>;
+  using X = PrepItem<TIn, P, C, DK, NTH, true>;        // C = 128: never the backward preparation
   using Split = typename X::Split;
   using IO = typename X::IO;
   constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
@@ -2049,7 +2049,8 @@ constexpr int prep_block_threads() { return DK <= 128 ? 512 : 256; }
 template <typename TIn, class P, int C, int DK>
 __global__ __launch_bounds__(prep_block_threads<DK>()) void prep_block_kernel(ChunkArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  prep_block_item<TIn, P, C, DK, prep_block_threads<DK>()>(a, blockIdx.x, blockIdx.y, blockIdx.z,
+  // C != 64 here: never the backward preparation
+  prep_block_item<TIn, P, C, DK, prep_block_threads<DK>(), true>(a, blockIdx.x, blockIdx.y, blockIdx.z,
                                                             reinterpret_cast<float *>(smem_raw));
 }
 
@@ -2126,6 +2127,7 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(block, grid, dim3(512), lds_b, stream, a);
     return hipGetLastError();
   } else if constexpr (C != 64) {
+    if (a.bwd) return hipErrorInvalidValue;            // the backward pass prepares C = 64 chunks only
     auto block = prep_block_kernel<TIn, P, C, DK>;
     constexpr int nth = prep_block_threads<DK>();
     const size_t lds_b = nth == 512 ? prep_block8_lds_bytes(C, DK, a.G) : lds;

@@ -32,6 +32,8 @@ SEG = {
                               alpha_sigma=2.0, seed=405),
     "gdn_f32": Workload("gdn_f32", 2, 2500, 2, 2, 64, 64, 64, 1, "f32", seed=406),
     "kda_c32": Workload("kda_c32", 1, 2000, 2, 2, 128, 64, 32, 128, "bf16", seed=412),
+    # chunk 16: the padded sequence (3008 tokens at chunk 32) is split too
+    "kda_c16": Workload("kda_c16", 1, 1500, 2, 2, 128, 64, 16, 128, "bf16", seed=413),
     "kda_f32_c128": Workload("kda_f32_c128", 1, 2200, 2, 2, 128, 64, 128, 128, "f32", seed=407),
     # long memory (log alpha = logsigmoid(N(7, 1)), about -1e-3 per token):
     # each segment's transition J stays of order 1, so the composed entry
