@@ -177,7 +177,10 @@ gdr_status gdr_chunk_prepare(const gdr_problem *p, const void *q, const void *k,
  * v) reuses the prepared chunks; that is the second pass of a sequence split
  * across devices, where each piece re-reads its output from the state handed
  * over by the previous piece (Systolic Linear Attention, section 3.3, the
- * affine chunk map).  Other arguments as for gdr_chunk_fwd.
+ * affine chunk map).  The scan's own regions of the workspace (the
+ * segment-parallel scan's maps and entry states; with chunk 16 the padded
+ * copies of v and o) are rewritten; the prepared chunks are not.  Other
+ * arguments as for gdr_chunk_fwd.
  */
 gdr_status gdr_chunk_scan(const gdr_problem *p, const void *v, const float *h0, void *o, float *hT,
                           const void *workspace, size_t workspace_bytes, void *stream);
