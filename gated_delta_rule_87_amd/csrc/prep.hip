@@ -1369,12 +1369,15 @@ struct LaLane {
     }
   }
 };
-// kMode: 0 the exact solve, forward only; 1 the exact solve, forward or
-// backward preparation; 2 the Neumann solves (forward only).
+// kMode: 0 the exact solve, forward only, no document resets; 1 the exact
+// solve, forward or backward preparation (no resets: the backward pass
+// takes the plain layer); 2 the Neumann solves (forward only, resets
+// allowed); 3 the exact solve, forward with resets allowed.
 template <typename TIn, class P, int DK, int kGate, int kMode>
 __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   constexpr bool kApprox = kMode == 2;
+  constexpr bool kResets = kMode >= 2;
   using X = PrepItem<TIn, P, C, DK, 256, kMode != 1>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
@@ -1398,7 +1401,7 @@ __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(Chun
   // kappa_c): Lambda runs on across it, the pairs of different documents are
   // zero, only the first document sees the chunk-entry state and only the
   // last one carries to the chunk's end
-  const bool resets = a.reset != nullptr;              // uniform
+  const bool resets = kResets && a.reset != nullptr;   // uniform
   const bool reset_here = resets && mt > 0.f && a.reset[x.tok(tr)] != 0;
 
 
@@ -2135,11 +2138,14 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(block, grid, dim3(nth), lds_b, stream, a);
     return hipGetLastError();
   } else {
-  const int md = a.solve != 0 ? 2 : a.bwd ? 1 : 0;
+  if (a.bwd && (a.solve != 0 || a.reset)) return hipErrorInvalidValue;   // backward: exact solve, plain layer
+  const int md = a.solve != 0 ? 2 : a.bwd ? 1 : a.reset ? 3 : 0;
   auto pick = [&](auto g) {
     constexpr int kG = decltype(g)::value;
-    return md == 2 ? prep_chunk_kernel<TIn, P, DK, kG, 2>
-                   : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1> : prep_chunk_kernel<TIn, P, DK, kG, 0>;
+    return md == 2   ? prep_chunk_kernel<TIn, P, DK, kG, 2>
+           : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1>
+           : md == 3 ? prep_chunk_kernel<TIn, P, DK, kG, 3>
+                     : prep_chunk_kernel<TIn, P, DK, kG, 0>;
   };
   auto chunk = a.G == DK  ? pick(std::integral_constant<int, kGatePerChannel>())
                : a.G >= 8 ? pick(std::integral_constant<int, kGateGroupsVec>())
