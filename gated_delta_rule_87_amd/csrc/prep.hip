@@ -922,8 +922,8 @@ constexpr float kWideMark = -1.f;
 // NTH threads (256 or 512); with 512 the per-wave transpose buffers sit in
 // the solve's scratch.
 // kFwdOnly: the item never prepares for the backward pass (its code is left
-// out of the forward kernels).
-template <typename TIn, class P, int C, int DK, int NTH = 256, bool kFwdOnly = false>
+// out of the forward kernels).  kOneBeta: one beta head per key head.
+template <typename TIn, class P, int C, int DK, int NTH = 256, bool kFwdOnly = false, bool kOneBeta = false>
 struct PrepItem {
   static constexpr int NB = C / 16;
   static constexpr int NKV = (C * DK / 8 + NTH - 1) / NTH;  // bound on 8-element log-alpha vectors per thread
@@ -952,7 +952,7 @@ struct PrepItem {
   __device__ __forceinline__ PrepItem(const ChunkArgs &a_, int c_, int hk_, int b_, float *smem_, int region0)
       : a(a_), c(c_), hk(hk_), b(b_), G(a_.G), gs(a_.gshift), T(a_.T), t0(c_ * C), tid(threadIdx.x),
         w(wave_id()), l(lane_id()), lr(lane_id() & 15), lq(lane_id() >> 4),
-        lgG(__builtin_ctz(DK) - a_.gshift), Rb(a_.H_beta / a_.H_k), smem(smem_), lam(smem_),
+        lgG(__builtin_ctz(DK) - a_.gshift), Rb(kOneBeta ? 1 : a_.H_beta / a_.H_k), smem(smem_), lam(smem_),
         ureg(smem_ + region0), tmp(ureg + C * prep_ld(C)),
         bet(ureg + (NTH == 256 ? prep_union_floats(C, DK) : prep_union8_floats(C, DK))),
         flags(reinterpret_cast<int *>(bet + C)),
@@ -1179,7 +1179,7 @@ struct PrepItem {
   // beta of the chunk for every beta head of this key head: element e of
   // thread tid's register j is e = tid + 256 j = rb * C + t (up to 4 * 256
   // values, C * Rb)
-  static constexpr int NBET = 1024 / NTH;              // beta values: C * Rb <= 1024
+  static constexpr int NBET = kOneBeta ? (C + NTH - 1) / NTH : 1024 / NTH;   // beta values: C * Rb <= 1024
   __device__ __forceinline__ void load_betas(TIn (&bets)[NBET]) const {
 #pragma unroll
     for (int j = 0; j < NBET; ++j) {
@@ -1372,13 +1372,14 @@ struct LaLane {
 // kMode: 0 the exact solve, forward only, no document resets; 1 the exact
 // solve, forward or backward preparation (no resets: the backward pass
 // takes the plain layer); 2 the Neumann solves (forward only, resets
-// allowed); 3 the exact solve, forward with resets allowed.
+// allowed); 3 the exact solve, forward with resets allowed; 4 as 0 with one
+// beta head per key head.
 template <typename TIn, class P, int DK, int kGate, int kMode>
 __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
   constexpr bool kApprox = kMode == 2;
-  constexpr bool kResets = kMode >= 2;
-  using X = PrepItem<TIn, P, C, DK, 256, kMode != 1>;
+  constexpr bool kResets = kMode == 2 || kMode == 3;
+  using X = PrepItem<TIn, P, C, DK, 256, kMode != 1, kMode == 4>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -2139,12 +2140,13 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     return hipGetLastError();
   } else {
   if (a.bwd && (a.solve != 0 || a.reset)) return hipErrorInvalidValue;   // backward: exact solve, plain layer
-  const int md = a.solve != 0 ? 2 : a.bwd ? 1 : a.reset ? 3 : 0;
+  const int md = a.solve != 0 ? 2 : a.bwd ? 1 : a.reset ? 3 : a.H_beta == a.H_k ? 4 : 0;
   auto pick = [&](auto g) {
     constexpr int kG = decltype(g)::value;
     return md == 2   ? prep_chunk_kernel<TIn, P, DK, kG, 2>
            : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1>
            : md == 3 ? prep_chunk_kernel<TIn, P, DK, kG, 3>
+           : md == 4 ? prep_chunk_kernel<TIn, P, DK, kG, 4>
                      : prep_chunk_kernel<TIn, P, DK, kG, 0>;
   };
   auto chunk = a.G == DK  ? pick(std::integral_constant<int, kGatePerChannel>())
