@@ -1751,8 +1751,11 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
 // reason the fp16 K-hat^T fragments come from an MFMA with an identity
 // operand (one nonzero product per output, exact) instead of an LDS
 // transpose.  The backward pass never prepares C = 128 chunks.
-template <typename TIn, class P, int DK, int kGate, bool kApprox>
+// kMode: 0 the exact solve without document resets; 2 the Neumann solves;
+// 3 the exact solve with resets allowed.
+template <typename TIn, class P, int DK, int kGate, int kMode>
 __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
+  constexpr bool kResets = kMode != 0;
   constexpr int C = 128, NTH = 512;
   using X = PrepItem<TIn, P, C, DK, NTH, true>;        // C = 128: never the backward preparation
   using Split = typename X::Split;
@@ -1786,7 +1789,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
   // ---- all loads of the item, issued together
   LaLane<TIn, KS, kGate> lal;
   lal.issue(x.la + x.tok(tr) * x.la_row + (size_t)x.hk * G, lq, gs, G);
-  const unsigned char rmark = a.reset ? a.reset[x.tok(tr)] : 0;
+  const unsigned char rmark = (kResets && a.reset) ? a.reset[x.tok(tr)] : 0;
   Raw8<TIn> kt[KS], qt[KS];
   x.load_rows(kt, x.kbase, I);
   x.load_rows(qt, x.qbase, I);
@@ -1847,7 +1850,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
     }
     if (part == 3) offt[NB * DK + ch] = all;
   }
-  if (a.reset && tid == NTH - 1) {                     // reset marks -> document numbers
+  if (kResets && a.reset && tid == NTH - 1) {          // reset marks -> document numbers
     int n = 0;
     for (int t = 0; t < C; ++t) {
       n += x.seg[t];
@@ -1862,7 +1865,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
   // Document segments (all 0 without resets): only segment 0 sees the
   // chunk-entry state, only the last one carries to the chunk's end, pairs
   // of different segments are zero (selects: no factor crosses a reset).
-  const bool resets = a.reset != nullptr;
+  const bool resets = kResets && a.reset != nullptr;
   const int seg_last = resets ? x.seg[C - 1] : 0;
   auto same_doc = [&](int r_, int c_) { return !resets || x.seg[r_] == x.seg[c_]; };
   const bool sees_entry = !resets || x.seg[tr] == 0, carries = !resets || x.seg[tr] == seg_last;
@@ -2041,7 +2044,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
     }
   }
   x.zero_upper_L();
-  x.template solve_store<kApprox>(gmat, x.smem, bets, true);
+  x.template solve_store<kMode == 2>(gmat, x.smem, bets, true);
 }
 
 // Grid (N_c, H_k, B), one chunk per work group.  d_k <= 128: eight waves
@@ -2119,13 +2122,16 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   hipError_t e;
   if constexpr (C == 128 && DK <= 128) {
     if (a.bwd) return hipErrorInvalidValue;            // the backward pass prepares C = 64 chunks only
-    const bool ap = a.solve != 0;
-    auto block = a.G == DK  ? (ap ? prep_block128_kernel<TIn, P, DK, kGatePerChannel, true>
-                                  : prep_block128_kernel<TIn, P, DK, kGatePerChannel, false>)
-                 : a.G >= 8 ? (ap ? prep_block128_kernel<TIn, P, DK, kGateGroupsVec, true>
-                                  : prep_block128_kernel<TIn, P, DK, kGateGroupsVec, false>)
-                            : (ap ? prep_block128_kernel<TIn, P, DK, kGateGroupsFew, true>
-                                  : prep_block128_kernel<TIn, P, DK, kGateGroupsFew, false>);
+    const int md = a.solve != 0 ? 2 : a.reset ? 3 : 0;
+    auto pick = [&](auto g) {
+      constexpr int kG = decltype(g)::value;
+      return md == 2   ? prep_block128_kernel<TIn, P, DK, kG, 2>
+             : md == 3 ? prep_block128_kernel<TIn, P, DK, kG, 3>
+                       : prep_block128_kernel<TIn, P, DK, kG, 0>;
+    };
+    auto block = a.G == DK  ? pick(std::integral_constant<int, kGatePerChannel>())
+                 : a.G >= 8 ? pick(std::integral_constant<int, kGateGroupsVec>())
+                            : pick(std::integral_constant<int, kGateGroupsFew>());
     const size_t lds_b = prep_block8_lds_bytes(C, DK, a.G);
     if ((e = set_lds(block, lds_b)) != hipSuccess) return e;
     hipLaunchKernelGGL(block, grid, dim3(512), lds_b, stream, a);
