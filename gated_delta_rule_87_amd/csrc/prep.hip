@@ -1371,14 +1371,14 @@ struct LaLane {
 };
 // kMode: 0 the exact solve, forward only, no document resets; 1 the exact
 // solve, forward or backward preparation (no resets: the backward pass
-// takes the plain layer); 2 the Neumann solves (forward only, resets
-// allowed); 3 the exact solve, forward with resets allowed; 4 as 0 with one
-// beta head per key head.
+// takes the plain layer); 2 the Neumann solves (forward only, no resets);
+// 3 the exact solve, forward with resets allowed; 4 as 0 with one beta head
+// per key head; 5 as 2 with resets allowed.
 template <typename TIn, class P, int DK, int kGate, int kMode>
 __global__ __launch_bounds__(256, DK <= 128 ? 3 : 2) void prep_chunk_kernel(ChunkArgs a) {
   constexpr int C = 64;
-  constexpr bool kApprox = kMode == 2;
-  constexpr bool kResets = kMode == 2 || kMode == 3;
+  constexpr bool kApprox = kMode == 2 || kMode == 5;
+  constexpr bool kResets = kMode == 3 || kMode == 5;
   using X = PrepItem<TIn, P, C, DK, 256, kMode != 1, kMode == 4>;
   using Split = typename X::Split;
   constexpr int NB = X::NB, KS = X::KS, NBET = X::NBET;
@@ -1751,11 +1751,12 @@ __device__ __forceinline__ void prep_block_item(const ChunkArgs &a, int c, int h
 // reason the fp16 K-hat^T fragments come from an MFMA with an identity
 // operand (one nonzero product per output, exact) instead of an LDS
 // transpose.  The backward pass never prepares C = 128 chunks.
-// kMode: 0 the exact solve without document resets; 2 the Neumann solves;
-// 3 the exact solve with resets allowed.
+// kMode: 0 the exact solve without document resets; 2 the Neumann solves
+// without resets; 3 the exact solve with resets allowed; 5 the Neumann
+// solves with resets allowed.
 template <typename TIn, class P, int DK, int kGate, int kMode>
 __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
-  constexpr bool kResets = kMode != 0;
+  constexpr bool kResets = kMode == 3 || kMode == 5;
   constexpr int C = 128, NTH = 512;
   using X = PrepItem<TIn, P, C, DK, NTH, true>;        // C = 128: never the backward preparation
   using Split = typename X::Split;
@@ -2044,7 +2045,7 @@ __global__ __launch_bounds__(512) void prep_block128_kernel(ChunkArgs a) {
     }
   }
   x.zero_upper_L();
-  x.template solve_store<kMode == 2>(gmat, x.smem, bets, true);
+  x.template solve_store<kMode == 2 || kMode == 5>(gmat, x.smem, bets, true);
 }
 
 // Grid (N_c, H_k, B), one chunk per work group.  d_k <= 128: eight waves
@@ -2122,10 +2123,11 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   hipError_t e;
   if constexpr (C == 128 && DK <= 128) {
     if (a.bwd) return hipErrorInvalidValue;            // the backward pass prepares C = 64 chunks only
-    const int md = a.solve != 0 ? 2 : a.reset ? 3 : 0;
+    const int md = a.solve != 0 ? (a.reset ? 5 : 2) : a.reset ? 3 : 0;
     auto pick = [&](auto g) {
       constexpr int kG = decltype(g)::value;
       return md == 2   ? prep_block128_kernel<TIn, P, DK, kG, 2>
+             : md == 5 ? prep_block128_kernel<TIn, P, DK, kG, 5>
              : md == 3 ? prep_block128_kernel<TIn, P, DK, kG, 3>
                        : prep_block128_kernel<TIn, P, DK, kG, 0>;
     };
@@ -2146,10 +2148,11 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     return hipGetLastError();
   } else {
   if (a.bwd && (a.solve != 0 || a.reset)) return hipErrorInvalidValue;   // backward: exact solve, plain layer
-  const int md = a.solve != 0 ? 2 : a.bwd ? 1 : a.reset ? 3 : a.H_beta == a.H_k ? 4 : 0;
+  const int md = a.solve != 0 ? (a.reset ? 5 : 2) : a.bwd ? 1 : a.reset ? 3 : a.H_beta == a.H_k ? 4 : 0;
   auto pick = [&](auto g) {
     constexpr int kG = decltype(g)::value;
     return md == 2   ? prep_chunk_kernel<TIn, P, DK, kG, 2>
+           : md == 5 ? prep_chunk_kernel<TIn, P, DK, kG, 5>
            : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1>
            : md == 3 ? prep_chunk_kernel<TIn, P, DK, kG, 3>
            : md == 4 ? prep_chunk_kernel<TIn, P, DK, kG, 4>
