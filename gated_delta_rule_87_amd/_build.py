@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "prep.hip", "scan.hip", "recurrent.hip", "noalloc.hip", "epilogue.hip", "verify.hip", "bwd.hip",
+SOURCES = ["prep.hip", "prep_f32.hip", "prep_bf16x.hip", "api.cpp", "scan.hip", "recurrent.hip", "noalloc.hip", "epilogue.hip", "verify.hip", "bwd.hip",
            "pad.hip"]
 
 COMMON = [

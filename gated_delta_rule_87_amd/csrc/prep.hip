@@ -49,6 +49,10 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#ifndef GDR_PREP_UNIT
+#define GDR_PREP_UNIT 0
+#endif
+
 namespace gdr {
 
 constexpr float kPivotRange = 64.f;  // exp(64) ~ 6e27 keeps every partial sum finite
@@ -92,20 +96,22 @@ __host__ __device__ inline int prep_union8_floats(int C, int DK) {
   const int solve = C * prep_ld(C) + scratch, colop = prep_colop_floats(C, DK);
   return solve > colop ? solve : colop;
 }
-size_t prep_block8_lds_bytes(int C, int DK, int G) {
+inline size_t prep_block8_lds_bytes(int C, int DK, int G) {
   return sizeof(float) * (size_t)(prep_region0_floats(C, G) + prep_union8_floats(C, DK) + C) + sizeof(int) * 16 + C;
 }
 
 // The block-pivot route also keeps each token's document segment (C bytes,
 // after the transpose buffers).
+#if !GDR_PREP_UNIT
 size_t prep_lds_bytes(int C, int DK, int G) {
   return sizeof(float) * (size_t)(prep_region0_floats(C, G) + prep_union_floats(C, DK) + C) +
          sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd + C;
 }
+#endif
 // The chunk-pivot kernel keeps Lambda in registers: region 0 holds the
 // block totals of Lambda during the build and G after it.
 __host__ __device__ inline int prep_chunk_region0_floats(int C) { return C * prep_ld(C); }
-size_t prep_chunk_lds_bytes(int C, int DK) {
+inline size_t prep_chunk_lds_bytes(int C, int DK) {
   return sizeof(float) * (size_t)(prep_chunk_region0_floats(C) + prep_union_floats(C, DK) + C) +
          sizeof(int) * 16 + sizeof(float) * 4 * 32 * kXbLd + C;
 }
@@ -2103,6 +2109,7 @@ __global__ __launch_bounds__(256) void prep_block_listed_kernel(ChunkArgs a) {
   }
 }
 
+#if !GDR_PREP_UNIT
 bool prep_supported(int C, int d_k, int G) {
   if (!(C == 32 || C == 64 || C == 128)) return false;
   if (!(d_k == 64 || d_k == 128 || d_k == 256)) return false;
@@ -2110,6 +2117,7 @@ bool prep_supported(int C, int d_k, int G) {
   // wide chunks; otherwise the block-pivot kernel, eight waves up to d_k = 128
   return (C == 64 || d_k > 128 ? prep_lds_bytes(C, d_k, G) : prep_block8_lds_bytes(C, d_k, G)) <= 160 * 1024;
 }
+#endif
 
 template <class K>
 static hipError_t set_lds(K kern, size_t /*lds*/) {
@@ -2126,10 +2134,14 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     const int md = a.solve != 0 ? (a.reset ? 5 : 2) : a.reset ? 3 : 0;
     auto pick = [&](auto g) {
       constexpr int kG = decltype(g)::value;
-      return md == 2   ? prep_block128_kernel<TIn, P, DK, kG, 2>
-             : md == 5 ? prep_block128_kernel<TIn, P, DK, kG, 5>
-             : md == 3 ? prep_block128_kernel<TIn, P, DK, kG, 3>
-                       : prep_block128_kernel<TIn, P, DK, kG, 0>;
+      if constexpr (P::kF32) {
+        return a.solve != 0 ? prep_block128_kernel<TIn, P, DK, kG, 5> : prep_block128_kernel<TIn, P, DK, kG, 3>;
+      } else {
+        return md == 2   ? prep_block128_kernel<TIn, P, DK, kG, 2>
+               : md == 5 ? prep_block128_kernel<TIn, P, DK, kG, 5>
+               : md == 3 ? prep_block128_kernel<TIn, P, DK, kG, 3>
+                         : prep_block128_kernel<TIn, P, DK, kG, 0>;
+      }
     };
     auto block = a.G == DK  ? pick(std::integral_constant<int, kGatePerChannel>())
                  : a.G >= 8 ? pick(std::integral_constant<int, kGateGroupsVec>())
@@ -2148,15 +2160,23 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
     return hipGetLastError();
   } else {
   if (a.bwd && (a.solve != 0 || a.reset)) return hipErrorInvalidValue;   // backward: exact solve, plain layer
+  // bf16 inputs get a variant per case; fp32 inputs (the checking mode) the
+  // three general ones, which keeps the build short
   const int md = a.solve != 0 ? (a.reset ? 5 : 2) : a.bwd ? 1 : a.reset ? 3 : a.H_beta == a.H_k ? 4 : 0;
   auto pick = [&](auto g) {
     constexpr int kG = decltype(g)::value;
-    return md == 2   ? prep_chunk_kernel<TIn, P, DK, kG, 2>
-           : md == 5 ? prep_chunk_kernel<TIn, P, DK, kG, 5>
-           : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1>
-           : md == 3 ? prep_chunk_kernel<TIn, P, DK, kG, 3>
-           : md == 4 ? prep_chunk_kernel<TIn, P, DK, kG, 4>
-                     : prep_chunk_kernel<TIn, P, DK, kG, 0>;
+    if constexpr (P::kF32) {
+      return a.solve != 0 ? prep_chunk_kernel<TIn, P, DK, kG, 5>
+             : a.bwd      ? prep_chunk_kernel<TIn, P, DK, kG, 1>
+                          : prep_chunk_kernel<TIn, P, DK, kG, 3>;
+    } else {
+      return md == 2   ? prep_chunk_kernel<TIn, P, DK, kG, 2>
+             : md == 5 ? prep_chunk_kernel<TIn, P, DK, kG, 5>
+             : md == 1 ? prep_chunk_kernel<TIn, P, DK, kG, 1>
+             : md == 3 ? prep_chunk_kernel<TIn, P, DK, kG, 3>
+             : md == 4 ? prep_chunk_kernel<TIn, P, DK, kG, 4>
+                       : prep_chunk_kernel<TIn, P, DK, kG, 0>;
+    }
   };
   auto chunk = a.G == DK  ? pick(std::integral_constant<int, kGatePerChannel>())
                : a.G >= 8 ? pick(std::integral_constant<int, kGateGroupsVec>())
@@ -2180,25 +2200,46 @@ static hipError_t launch_prep_t(const ChunkArgs &a, hipStream_t stream) {
   }
 }
 
-template <typename TIn, class P>
+// kPart: which d_k a translation unit instantiates (0 every d_k, 1 only
+// d_k = 128, 2 d_k in {64, 256}).
+template <typename TIn, class P, int kPart>
 static hipError_t launch_prep_dk(const ChunkArgs &a, hipStream_t s) {
+  constexpr bool k128 = kPart != 2, kOther = kPart != 1;
   switch (a.C * 1000 + a.d_k) {
-    case 32064: return launch_prep_t<TIn, P, 32, 64>(a, s);
-    case 32128: return launch_prep_t<TIn, P, 32, 128>(a, s);
-    case 32256: return launch_prep_t<TIn, P, 32, 256>(a, s);
-    case 64064: return launch_prep_t<TIn, P, 64, 64>(a, s);
-    case 64128: return launch_prep_t<TIn, P, 64, 128>(a, s);
-    case 64256: return launch_prep_t<TIn, P, 64, 256>(a, s);
-    case 128064: return launch_prep_t<TIn, P, 128, 64>(a, s);
-    case 128128: return launch_prep_t<TIn, P, 128, 128>(a, s);
-    case 128256: return launch_prep_t<TIn, P, 128, 256>(a, s);
-    default: return hipErrorInvalidValue;
+    case 32064: if constexpr (kOther) return launch_prep_t<TIn, P, 32, 64>(a, s); break;
+    case 32128: if constexpr (k128) return launch_prep_t<TIn, P, 32, 128>(a, s); break;
+    case 32256: if constexpr (kOther) return launch_prep_t<TIn, P, 32, 256>(a, s); break;
+    case 64064: if constexpr (kOther) return launch_prep_t<TIn, P, 64, 64>(a, s); break;
+    case 64128: if constexpr (k128) return launch_prep_t<TIn, P, 64, 128>(a, s); break;
+    case 64256: if constexpr (kOther) return launch_prep_t<TIn, P, 64, 256>(a, s); break;
+    case 128064: if constexpr (kOther) return launch_prep_t<TIn, P, 128, 64>(a, s); break;
+    case 128128: if constexpr (k128) return launch_prep_t<TIn, P, 128, 128>(a, s); break;
+    case 128256: if constexpr (kOther) return launch_prep_t<TIn, P, 128, 256>(a, s); break;
+    default: break;
   }
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_prep(const ChunkArgs &a, bool in_bf16, hipStream_t stream) {
-  if (in_bf16) return launch_prep_dk<bf16, PrecBF16>(a, stream);
-  return launch_prep_dk<float, PrecF32>(a, stream);
+// The kernels are compiled in three translation units, so the prep build
+// runs in parallel: this one (bf16 inputs with d_k = 128, and the
+// dispatch), prep_f32.hip (fp32 inputs, GDR_PREP_UNIT 1) and
+// prep_bf16x.hip (bf16 inputs with d_k 64 or 256, GDR_PREP_UNIT 2).
+hipError_t launch_prep_f32(const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_prep_bf16x(const ChunkArgs &a, hipStream_t stream);
+#if GDR_PREP_UNIT == 1
+hipError_t launch_prep_f32(const ChunkArgs &a, hipStream_t stream) {
+  return launch_prep_dk<float, PrecF32, 0>(a, stream);
 }
+#elif GDR_PREP_UNIT == 2
+hipError_t launch_prep_bf16x(const ChunkArgs &a, hipStream_t stream) {
+  return launch_prep_dk<bf16, PrecBF16, 2>(a, stream);
+}
+#else
+hipError_t launch_prep(const ChunkArgs &a, bool in_bf16, hipStream_t stream) {
+  if (!in_bf16) return launch_prep_f32(a, stream);
+  if (a.d_k == 128) return launch_prep_dk<bf16, PrecBF16, 1>(a, stream);
+  return launch_prep_bf16x(a, stream);
+}
+#endif
 
 }  // namespace gdr
