@@ -307,3 +307,27 @@ def test_chunk16_prepare_then_scan(name):
                                chunk=16)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("T", [0, 5, 16, 17])
+def test_chunk16_short_sequences(T):
+    """Chunk 16 on sequences shorter than one padded chunk, exactly one chunk
+    and one token more: o and hT against the fp64 recurrence; T = 0 copies
+    h0 to hT."""
+    w = SMALL["gdn_f32_c16"].with_(T=max(T, 1))
+    raw, x = draw(w)
+    dev = device_inputs(raw)
+    h0 = (0.2 * np.random.default_rng(5).standard_normal((w.B, w.H_v, w.d_k, w.d_v))).astype(np.float32)
+    print(f"[case] chunk 16 T={T}", flush=True)
+    if T == 0:
+        dev = {n: t[:, :0].contiguous() for n, t in dev.items()}
+        o, hT = run_chunk(dev, w, h0=to_torch(h0))
+        torch.cuda.synchronize()
+        assert o.numel() == 0 and np.array_equal(hT.cpu().numpy(), h0)
+        return
+    o, hT = run_chunk(dev, w, h0=to_torch(h0))
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle(x, w, h0.astype(np.float64))
+    eo, eh = rel_err(o.cpu().numpy(), o_ref), rel_err(hT.cpu().numpy(), h_ref)
+    print(f"  err o={eo:.3e} hT={eh:.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and eh <= TOL[w.dtype]
